@@ -1,0 +1,31 @@
+"""CPU oracle for paged K/V attention and the greedy speculative accept step.
+
+TEST INFRASTRUCTURE ONLY. Only the tests, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package. The GPU library
+never calls it, and it shares no code with the GPU library: it reads the data
+layout from the C header's documentation only and decodes every input itself.
+
+What it computes is the plain definition, in float64:
+
+* ``paged_attention.attention`` -- materialise each sequence's contiguous K/V
+  from its block table, then exact softmax attention with the verify window
+  causal inside the window (``paged_attention`` module docstring lists the
+  readings of the pages it follows).
+* ``greedy_accept.argmax_rows`` / ``.accept`` / ``.window_next`` -- the
+  vocab-wide argmax, the left-to-right draft comparison with one correction
+  token, and the +2 / -1 draft-window rule.
+* ``brute`` -- an independent pure-Python loop version of the attention, per
+  token and per element, used to pin ``paged_attention`` on tiny inputs.
+
+Pins: every function here is checked in ``tests/test_oracle_*.py`` against
+brute force, closed forms, invariants and hand-worked fixtures under
+``tests/golden/``. Absolute attention values at the full configuration sizes
+have no printed reference on the pages; they are pinned only through those
+checks.
+"""
+
+from .paged_attention import decode_bf16, gather_sequence, attention, attention_rows
+from .greedy_accept import argmax_rows, accept, window_next
+
+__all__ = ["decode_bf16", "gather_sequence", "attention", "attention_rows",
+           "argmax_rows", "accept", "window_next"]
