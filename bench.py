@@ -1,0 +1,267 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged-attention + greedy-accept hot path on one MI355X.
+
+A step is one speculative-verify pass over the verify workload: paged
+attention for 8 sequences of 8192 cached tokens (window of 6 rows = 5 drafts +
+1, causal inside the window; 32 q heads over 8 KV heads, head_dim 128, bf16,
+256-token pages filling a 256-page pool through permuted block tables), then
+the greedy accept over fp32 logits [48, 128256] with the window update. Inputs
+are seeded synthetic data resident in HBM before timing; the K/V pools and
+logits rotate over several replicas so that no step is served from the
+256 MB last-level cache left warm by the previous one.
+
+Prints one JSON line. `value` is the logical K/V bytes the step reads through
+the block tables divided by the step time (attention + accept); the line also
+carries the attention-only rate, the HBM fraction, verified tokens/s, the
+roofline of the attention kernel, per-configuration attention rates for the
+decode and dedup workloads, and the CPU oracle timed on a bounded sample.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, AMD's published figure
+METRIC = "paged-attn KV read GB/s (fraction of HBM peak); verified tokens/s"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--replicas", type=int, default=4)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true", help="skip the per-configuration sweep")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="time budget of the CPU oracle sample")
+    return ap.parse_args()
+
+
+class Attn:
+    """One attention workload on the device, with R replicas of its pools."""
+
+    def __init__(self, case, pk, torch, replicas):
+        self.case, self.pk, self.torch = case, pk, torch
+        dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+        i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+        k0, v0 = dev(case.k_pool), dev(case.v_pool)
+        self.k = [k0] + [k0.clone() for _ in range(replicas - 1)]
+        self.v = [v0] + [v0.clone() for _ in range(replicas - 1)]
+        self.q = dev(case.q)
+        self.bt, self.sl, self.ql = i32(case.block_table), i32(case.seq_lens), i32(case.q_lens)
+        self.out = torch.empty(case.q.shape, dtype=torch.float32, device="cuda")
+        self.shape = pk.attn_shape(self.q, k0, self.bt, max(1, case.max_q_len), case.scale)
+        self.ws = pk.new_attn_workspace(self.shape)
+        self.R = replicas
+
+    def __call__(self, i):
+        r = i % self.R
+        self.pk.pkv_attn_fwd(self.q, self.k[r], self.v[r], self.bt, self.sl, self.ql, self.out,
+                             self.shape, self.ws)
+
+
+class Accept:
+    def __init__(self, acc, pk, torch, replicas):
+        self.pk, self.torch = pk, torch
+        i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+        l0 = torch.from_numpy(np.ascontiguousarray(acc.logits)).cuda()
+        self.logits = [l0] + [l0.clone() for _ in range(replicas - 1)]
+        self.drafts = i32(acc.draft_ids)
+        self.nd = i32(acc.n_draft)
+        self.oa = torch.empty(acc.num_seqs, dtype=torch.int32, device="cuda")
+        self.on = torch.empty(acc.num_seqs, dtype=torch.int32, device="cuda")
+        self.win0 = i32(acc.window)
+        self.win = self.win0.clone()
+        self.shape = pk.accept_shape(l0, self.nd, acc.max_draft)
+        self.ws = pk.new_accept_workspace(self.shape)
+        self.R = replicas
+
+    def __call__(self, i):
+        self.pk.pkv_accept(self.logits[i % self.R], self.drafts, self.nd, self.oa, self.on, self.win,
+                           self.shape, self.ws)
+
+
+def time_ms(torch, fn, steps, warmup):
+    """Mean milliseconds per call of fn(i), timed with HIP events on the
+    current stream (the stream every launch goes to)."""
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        fn(warmup + i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def cpu_baseline(case, acc, seconds):
+    """The CPU oracle on a bounded sample of the verify step: whole sequences
+    (attention over their cached tokens + accept over their logits rows), in
+    order, until the time budget is spent."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    kv_per_tok = 2 * case.num_kv_heads * case.head_dim * 2
+    done_seqs, kv_bytes, accepted = 0, 0, 0
+    r0 = 0
+    t0 = time.perf_counter()
+    for b in range(case.num_seqs):
+        ql = int(case.q_lens[b])
+        sub = dict(q_bits=case.q[r0:r0 + ql], k_pool_bits=case.k_pool, v_pool_bits=case.v_pool,
+                   block_table=case.block_table[b:b + 1], seq_lens=case.seq_lens[b:b + 1],
+                   q_lens=case.q_lens[b:b + 1], scale=case.scale)
+        oracle.attention(**sub)
+        nd = acc.n_draft[b:b + 1]
+        d0 = int(acc.n_draft[:b].sum())
+        a, _, _ = oracle.accept(acc.logits[r0:r0 + ql], acc.draft_ids[d0:d0 + int(nd[0])], nd)
+        accepted += int(a[0])
+        kv_bytes += int(case.seq_lens[b]) * kv_per_tok
+        done_seqs += 1
+        r0 += ql
+        if time.perf_counter() - t0 > seconds:
+            break
+    dt = time.perf_counter() - t0
+    cpu = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": kv_bytes / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done_seqs} of {case.num_seqs} sequences of the verify batch (attention over "
+                      f"{int(case.seq_lens[0])} tokens x 6 rows x 32 heads in float64 + accept over "
+                      f"their 128256-wide logits rows), {dt:.1f} s",
+            "verified_tokens_per_s": accepted / dt, "seconds": dt,
+            "host_cores_available": len(os.sched_getaffinity(0)), "cpu_model": cpu}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this library has no "
+              "multi-GPU path: the hot path shards by sequence and KV head with no exchange", flush=True)
+        sys.exit(2)
+
+    import torch
+    import paged_kv_attention_attn_amd as pk
+    from workloads import make_config, kv_logical_bytes
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    props = torch.cuda.get_device_properties(0)
+    R = max(1, args.replicas)
+
+    log("generating the verify workload")
+    case, acc = make_config(3, seed=args.seed)
+    attn = Attn(case, pk, torch, R)
+    accept = Accept(acc, pk, torch, R)
+    kv_bytes = kv_logical_bytes(case.seq_lens, case.num_kv_heads, case.head_dim)
+
+    def step(i):
+        attn(i)
+        accept(i)
+
+    log("timing")
+    attn_ms = time_ms(torch, attn, args.steps, args.warmup)
+    accept_ms = time_ms(torch, accept, args.steps, args.warmup)
+    accept.win.copy_(accept.win0)
+    torch.cuda.synchronize()
+    step_ms = time_ms(torch, step, args.steps, args.warmup)
+    # one checked step: the window update is applied per call, so reset and run once
+    accept.win.copy_(accept.win0)
+    step(0)
+    torch.cuda.synchronize()
+    accepted = int(accept.oa.sum().item())
+    flags = pk.pkv_attn_check_errors(attn.ws)
+    assert flags == 0, f"attention error flags {flags}"
+
+    value = kv_bytes / (step_ms * 1e-3) / 1e9
+    attn_gbps = kv_bytes / (attn_ms * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "speculative verify: 8 sequences x 8192 cached tokens, window 6 (5 drafts + 1) "
+                               "causal inside the window, 32 q / 8 KV heads, head_dim 128, bf16 K/V in "
+                               "256-token pages (full 256-page pool, permuted tables), then greedy accept "
+                               "over fp32 logits [48, 128256] with the +2/-1 window rule",
+                   "global_batch": int(case.num_seqs), "seq_len": int(case.seq_lens[0]),
+                   "q_len": int(case.q_lens[0]), "parallelism": "single GPU"},
+        "hbm_fraction": round(value / HBM_PEAK_GBPS, 4),
+        "attn_kv_gbps": round(attn_gbps, 2),
+        "attn_hbm_fraction": round(attn_gbps / HBM_PEAK_GBPS, 4),
+        "attn_us": round(attn_ms * 1e3, 3),
+        "accept_us": round(accept_ms * 1e3, 3),
+        "verified_tokens_per_s": round(accepted / (step_ms * 1e-3), 1),
+        "accepted_per_step": accepted,
+        "kv_bytes_per_step": kv_bytes,
+        "roofline": {"bound": "hbm", "kernel": "attn_split_kernel (MFMA row tile, 24 rows)",
+                     "achieved": round(attn_gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(attn_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": kv_bytes,
+                     "avg_launch_us": round(attn_ms * 1e3, 3)},
+        "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
+                   "cus": props.multi_processor_count, "hbm_gib": round(props.total_memory / 2**30, 1)},
+    }
+    del attn, accept
+    torch.cuda.empty_cache()
+
+    if not args.no_configs:
+        sweep = {}
+        for cfg in (1, 2, 4):
+            log(f"configuration {cfg}")
+            c, _ = make_config(cfg, seed=args.seed)
+            a = Attn(c, pk, torch, R)
+            ms = time_ms(torch, a, args.steps, args.warmup)
+            kb = kv_logical_bytes(c.seq_lens, c.num_kv_heads, c.head_dim)
+            sweep[f"config{cfg}"] = {"attn_us": round(ms * 1e3, 3), "kv_bytes": kb,
+                                     "kv_gbps": round(kb / (ms * 1e-3) / 1e9, 2),
+                                     "hbm_fraction": round(kb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                                     "decode_tokens_per_s": round(c.num_seqs / (ms * 1e-3), 1)}
+            del a
+            torch.cuda.empty_cache()
+        sweep["config3"] = {"attn_us": result["attn_us"], "kv_bytes": kv_bytes,
+                            "kv_gbps": result["attn_kv_gbps"], "hbm_fraction": result["attn_hbm_fraction"]}
+        result["configs"] = sweep
+
+    if not args.no_cpu_baseline:
+        log("CPU oracle sample")
+        result["cpu_baseline"] = cpu_baseline(case, acc, args.cpu_seconds)
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,168 @@
+/*
+ * pkv -- paged K/V attention and greedy speculative accept for AMD MI355X
+ * (gfx950). C ABI: plain pointers and sizes; no C++ or framework types cross
+ * this boundary.
+ *
+ * Sources (cited by page title and section):
+ *  - ExLlamaV2 "Dynamic Generator" page, "Continuous Batching": the K/V cache
+ *    is reached through per-sequence block tables of fixed 256-token pages;
+ *    growing or shrinking a batch only rewrites block indices; freed pages
+ *    leave holes, so a table's indices need not be contiguous.
+ *  - Same page, "Deduplication": several sequences may index the same page,
+ *    so a shared prefix is stored once.
+ *  - Hugging Face "Assisted Generation" page, "How Assisted Generation works"
+ *    and "Assisted Generation loop": one forward pass scores every position of
+ *    a draft window; the base model's tokens are compared with the drafts from
+ *    the left; at the first mismatch its own token is kept and the rest
+ *    dropped; the window (5 at first) grows by 2 after a full match and
+ *    shrinks by 1 otherwise.
+ *
+ * Conventions for every entry point:
+ *  - Device pointers are caller-owned device memory. The library allocates
+ *    nothing and keeps no per-call state; every kernel is enqueued on `stream`
+ *    (a hipStream_t; NULL means the default stream) and nothing synchronises.
+ *  - Shapes are checked on the host before any launch. Contents of device
+ *    arrays are a caller contract (listed per call). Kernels never read or
+ *    write outside the documented extents even when the contract is broken:
+ *    an offending sequence is skipped and a bit is set in the workspace's
+ *    error word (read it with pkv_attn_check_errors).
+ *  - Return value: PKV_OK or a negative pkv_status. C++ exceptions never
+ *    cross this boundary.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_PAGE_SIZE 256 /* tokens per page; fixed by the Dynamic Generator page */
+#define PKV_MAX_Q_LEN 16  /* longest verify window (k drafts + 1) per sequence  */
+#define PKV_MAX_ROWS 64   /* q_len * (Hq / Hkv) per sequence and KV head        */
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_ERR_NULL = -1,      /* a required pointer is NULL                         */
+  PKV_ERR_SHAPE = -2,     /* a shape field is out of range (see each call)      */
+  PKV_ERR_WORKSPACE = -3, /* workspace NULL or smaller than the queried size    */
+  PKV_ERR_HIP = -4        /* a HIP launch or runtime call failed                */
+} pkv_status;
+
+/* Error-word bits a kernel sets when a device array breaks its contract. */
+#define PKV_EFLAG_PAGE 1u  /* a block-table entry the sequence needs is not in [0, num_pages) */
+#define PKV_EFLAG_QLEN 2u  /* q_len > max_q_len, q_len > seq_len, or seq_len > max_pages_per_seq*256 */
+#define PKV_EFLAG_ROWS 4u  /* sum(q_lens) exceeds total_q                                           */
+
+/* ------------------------------------------------------------------ attention */
+
+typedef struct {
+  int32_t num_seqs;          /* B >= 0                                              */
+  int32_t num_q_heads;       /* Hq >= 1                                             */
+  int32_t num_kv_heads;      /* Hkv >= 1, Hq % Hkv == 0                             */
+  int32_t head_dim;          /* D, 64 or 128                                        */
+  int32_t page_size;         /* must be PKV_PAGE_SIZE                               */
+  int32_t num_pages;         /* P >= 1: pages in each pool                          */
+  int32_t max_pages_per_seq; /* W >= 1: row stride of block_table                   */
+  int32_t total_q;           /* rows of q and out; must equal sum(q_lens)           */
+  int32_t max_q_len;         /* 1..PKV_MAX_Q_LEN, >= every q_lens[b]; and           */
+                             /* max_q_len * (Hq/Hkv) <= PKV_MAX_ROWS                */
+  float scale;               /* softmax scale applied to q.k (e.g. 1/sqrt(D))       */
+} pkv_attn_shape;
+
+/* Bytes of device workspace pkv_attn_fwd needs for this shape (0 on a bad
+ * shape). The workspace holds an error word, one merge counter per
+ * (sequence, KV head) and per-split partial results. It must be zero-filled
+ * before its first use and again before it is reused for a different shape
+ * (pkv_attn_workspace_init does it); every call leaves the counters at zero. */
+size_t pkv_attn_workspace_bytes(const pkv_attn_shape* shape);
+
+/* Enqueue a zero fill of `bytes` bytes of workspace on `stream`. */
+int pkv_attn_workspace_init(void* workspace, size_t bytes, void* stream);
+
+/*
+ * Paged attention for decode (q_len = 1) and speculative verification
+ * (q_len = k + 1, causal inside the window), in one kernel.
+ *
+ * q           bf16 [total_q, Hq, D]; rows packed by sequence, then window row.
+ * k_pool      bf16 [P, Hkv, 256, D]: K of page p, KV head g, slot s at
+ * v_pool            ((p * Hkv + g) * 256 + s) * D. Read only.
+ * block_table int32 [B, W]: token t of sequence b is slot t % 256 of page
+ *             block_table[b * W + t / 256]. Only the first ceil(seq_len/256)
+ *             entries of a row are read; they may repeat across rows (shared
+ *             pages) and appear in any order.
+ * seq_lens    int32 [B]: tokens in the cache per sequence, window included.
+ * q_lens      int32 [B]: window rows per sequence, 0..max_q_len, <= seq_len.
+ *             Window row i of sequence b attends to tokens
+ *             0 .. seq_len - q_len + i. q_len = 0 skips the sequence.
+ * out         fp32 [total_q, Hq, D]: softmax(scale * q.K^T) V per row; q head h
+ *             reads KV head h / (Hq / Hkv).
+ * workspace   pkv_attn_workspace_bytes(shape) bytes (see there); one call at a
+ *             time per workspace.
+ * Slots past seq_len and unreferenced pages may hold anything (NaN included):
+ * they never affect `out`. Results are deterministic: they depend only on the
+ * contents a sequence references, not on which physical pages hold them.
+ * Contract: block-table entries a sequence needs lie in [0, P); sum(q_lens) ==
+ * total_q; q_len <= max_q_len; q_len <= seq_len <= W * 256.
+ */
+int pkv_attn_fwd(const void* q, const void* k_pool, const void* v_pool,
+                 const int32_t* block_table, const int32_t* seq_lens, const int32_t* q_lens,
+                 float* out, const pkv_attn_shape* shape,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Synchronise `stream`, copy the error word of `workspace` into *flags
+ * (PKV_EFLAG_* bits; 0 = every contract held) and clear it. */
+int pkv_attn_check_errors(void* workspace, void* stream, uint32_t* flags);
+
+/* -------------------------------------------------------------------- accept */
+
+typedef struct {
+  int32_t num_seqs;   /* B >= 0                                   */
+  int32_t vocab;      /* V >= 1                                   */
+  int32_t total_rows; /* rows of logits; must equal sum(n_draft + 1) */
+  int32_t max_draft;  /* >= every n_draft[b]; 0..PKV_MAX_Q_LEN - 1   */
+} pkv_accept_shape;
+
+/* Bytes of device workspace pkv_accept needs (0 on a bad shape). No
+ * initialisation is required. */
+size_t pkv_accept_workspace_bytes(const pkv_accept_shape* shape);
+
+/*
+ * Greedy accept over a verified window.
+ *
+ * logits     fp32 [total_rows, V]; sequence b owns n_draft[b] + 1 consecutive
+ *            rows (same order as the attention rows). Row i < n predicts the
+ *            token after window token i; row n is the bonus row.
+ * draft_ids  int32 packed [sum(n_draft)]: the drafts of sequence b in order.
+ * n_draft    int32 [B]: drafts per sequence (0 = plain decode).
+ * out_accept int32 [B]: m + 1, where m is the first i < n with
+ *            argmax(row i) != draft i (m = n if every draft matches); the +1
+ *            is the base model's own token at position m.
+ * out_next   int32 [B]: argmax(row m) -- the correction token, or the bonus
+ *            token when every draft matched.
+ * window     int32 [B] or NULL: if given, updated in place by the window
+ *            rule (pkv_window_next).
+ * argmax: lowest index among equal maxima; a NaN counts as the maximum and the
+ * first NaN wins. Results are bit-exact.
+ * Contract: sum(n_draft + 1) == total_rows; n_draft[b] <= max_draft.
+ */
+int pkv_accept(const float* logits, const int32_t* draft_ids, const int32_t* n_draft,
+               int32_t* out_accept, int32_t* out_next, int32_t* window,
+               const pkv_accept_shape* shape, void* workspace, size_t workspace_bytes,
+               void* stream);
+
+/* The draft-window rule on the host: window + 2 when accepted == n_draft + 1
+ * (every draft matched, including n_draft == 0), else max(1, window - 1). */
+int32_t pkv_window_next(int32_t window, int32_t n_draft, int32_t accepted);
+
+/* ---------------------------------------------------------------------- misc */
+
+const char* pkv_status_string(int status);
+int pkv_version(void); /* major * 10000 + minor * 100 + patch */
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PKV_H */

@@ -1,0 +1,190 @@
+"""ctypes binding of libpkv.so: the C ABI of include/pkv.h under the same
+names. Argument marshalling only -- every step of the computation runs in the
+library's HIP kernels. torch supplies device memory and the stream.
+
+The library is loaded after torch so that it binds to the HIP runtime torch
+already loaded. There is no fallback: if the library is missing, importing
+the binding raises.
+"""
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libpkv.so")
+
+PKV_PAGE_SIZE = 256
+PKV_MAX_Q_LEN = 16
+PKV_MAX_ROWS = 64
+PKV_OK, PKV_ERR_NULL, PKV_ERR_SHAPE, PKV_ERR_WORKSPACE, PKV_ERR_HIP = 0, -1, -2, -3, -4
+PKV_EFLAG_PAGE, PKV_EFLAG_QLEN, PKV_EFLAG_ROWS = 1, 2, 4
+
+EXPORTS = ("pkv_attn_workspace_bytes", "pkv_attn_workspace_init", "pkv_attn_fwd",
+           "pkv_attn_check_errors", "pkv_accept_workspace_bytes", "pkv_accept",
+           "pkv_window_next", "pkv_status_string", "pkv_version")
+
+
+class pkv_attn_shape(ctypes.Structure):
+    _fields_ = [("num_seqs", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+                ("max_pages_per_seq", ctypes.c_int32), ("total_q", ctypes.c_int32),
+                ("max_q_len", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+class pkv_accept_shape(ctypes.Structure):
+    _fields_ = [("num_seqs", ctypes.c_int32), ("vocab", ctypes.c_int32),
+                ("total_rows", ctypes.c_int32), ("max_draft", ctypes.c_int32)]
+
+
+class PkvError(RuntimeError):
+    pass
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m paged_kv_attention_attn_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, sz, i32p = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p
+    lib.pkv_attn_workspace_bytes.argtypes = [ctypes.POINTER(pkv_attn_shape)]
+    lib.pkv_attn_workspace_bytes.restype = sz
+    lib.pkv_attn_workspace_init.argtypes = [vp, sz, vp]
+    lib.pkv_attn_workspace_init.restype = ctypes.c_int
+    lib.pkv_attn_fwd.argtypes = [vp, vp, vp, i32p, i32p, i32p, vp, ctypes.POINTER(pkv_attn_shape),
+                                 vp, sz, vp]
+    lib.pkv_attn_fwd.restype = ctypes.c_int
+    lib.pkv_attn_check_errors.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_uint32)]
+    lib.pkv_attn_check_errors.restype = ctypes.c_int
+    lib.pkv_accept_workspace_bytes.argtypes = [ctypes.POINTER(pkv_accept_shape)]
+    lib.pkv_accept_workspace_bytes.restype = sz
+    lib.pkv_accept.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.POINTER(pkv_accept_shape), vp, sz, vp]
+    lib.pkv_accept.restype = ctypes.c_int
+    lib.pkv_window_next.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
+    lib.pkv_window_next.restype = ctypes.c_int32
+    lib.pkv_status_string.argtypes = [ctypes.c_int]
+    lib.pkv_status_string.restype = ctypes.c_char_p
+    lib.pkv_version.argtypes = []
+    lib.pkv_version.restype = ctypes.c_int
+    return lib
+
+
+LIB = _load()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(rc, what):
+    if rc != PKV_OK:
+        raise PkvError(f"{what}: {LIB.pkv_status_string(rc).decode()} ({rc})")
+
+
+def _need(t, dtype, name):
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must live on the GPU")
+
+
+def attn_shape(q, k_pool, block_table, max_q_len, scale):
+    """pkv_attn_shape from tensor extents (q [total_q, Hq, D], pool [P, Hkv, 256, D],
+    block_table [B, W])."""
+    total_q, Hq, D = q.shape
+    P, Hkv, page, D2 = k_pool.shape
+    B, W = block_table.shape
+    if D2 != D:
+        raise ValueError("q and pool head_dim differ")
+    return pkv_attn_shape(B, Hq, Hkv, D, page, P, W, total_q, int(max_q_len), float(scale))
+
+
+def pkv_attn_workspace_bytes(shape):
+    return int(LIB.pkv_attn_workspace_bytes(ctypes.byref(shape)))
+
+
+def pkv_attn_workspace_init(workspace, stream=None):
+    _check(LIB.pkv_attn_workspace_init(_ptr(workspace), workspace.numel(), _stream(stream)),
+           "pkv_attn_workspace_init")
+
+
+def new_attn_workspace(shape, device="cuda"):
+    n = pkv_attn_workspace_bytes(shape)
+    if n == 0:
+        raise PkvError("pkv_attn_workspace_bytes: shape rejected")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def pkv_attn_fwd(q, k_pool, v_pool, block_table, seq_lens, q_lens, out, shape, workspace, stream=None):
+    """q, k_pool, v_pool: bf16; block_table, seq_lens, q_lens: int32; out: fp32."""
+    for t, dt, n in ((q, torch.bfloat16, "q"), (k_pool, torch.bfloat16, "k_pool"),
+                     (v_pool, torch.bfloat16, "v_pool"), (block_table, torch.int32, "block_table"),
+                     (seq_lens, torch.int32, "seq_lens"), (q_lens, torch.int32, "q_lens"),
+                     (out, torch.float32, "out"), (workspace, torch.uint8, "workspace")):
+        _need(t, dt, n)
+    rc = LIB.pkv_attn_fwd(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(seq_lens),
+                          _ptr(q_lens), _ptr(out), ctypes.byref(shape), _ptr(workspace),
+                          workspace.numel(), _stream(stream))
+    _check(rc, "pkv_attn_fwd")
+
+
+def pkv_attn_check_errors(workspace, stream=None):
+    flags = ctypes.c_uint32(0)
+    _check(LIB.pkv_attn_check_errors(_ptr(workspace), _stream(stream), ctypes.byref(flags)),
+           "pkv_attn_check_errors")
+    return int(flags.value)
+
+
+def accept_shape(logits, n_draft, max_draft):
+    rows, V = logits.shape
+    return pkv_accept_shape(int(n_draft.shape[0]), int(V), int(rows), int(max_draft))
+
+
+def pkv_accept_workspace_bytes(shape):
+    return int(LIB.pkv_accept_workspace_bytes(ctypes.byref(shape)))
+
+
+def new_accept_workspace(shape, device="cuda"):
+    n = pkv_accept_workspace_bytes(shape)
+    if n == 0:
+        raise PkvError("pkv_accept_workspace_bytes: shape rejected")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def pkv_accept(logits, draft_ids, n_draft, out_accept, out_next, window, shape, workspace, stream=None):
+    """logits fp32; draft_ids, n_draft, out_accept, out_next, window (or None): int32."""
+    for t, dt, n in ((logits, torch.float32, "logits"), (n_draft, torch.int32, "n_draft"),
+                     (out_accept, torch.int32, "out_accept"), (out_next, torch.int32, "out_next"),
+                     (workspace, torch.uint8, "workspace")):
+        _need(t, dt, n)
+    if draft_ids is not None and draft_ids.numel():
+        _need(draft_ids, torch.int32, "draft_ids")
+    if window is not None:
+        _need(window, torch.int32, "window")
+    drafts = draft_ids if (draft_ids is not None and draft_ids.numel()) else None
+    rc = LIB.pkv_accept(_ptr(logits), _ptr(drafts), _ptr(n_draft), _ptr(out_accept), _ptr(out_next),
+                        _ptr(window), ctypes.byref(shape), _ptr(workspace), workspace.numel(),
+                        _stream(stream))
+    _check(rc, "pkv_accept")
+
+
+def pkv_window_next(window, n_draft, accepted):
+    return int(LIB.pkv_window_next(int(window), int(n_draft), int(accepted)))
+
+
+def pkv_status_string(status):
+    return LIB.pkv_status_string(int(status)).decode()
+
+
+def pkv_version():
+    return int(LIB.pkv_version())

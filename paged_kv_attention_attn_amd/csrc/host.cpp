@@ -1,0 +1,168 @@
+// C ABI of the pkv library: host-side validation, workspace sizing, and
+// kernel launch on the caller's stream. Declarations and the contract of each
+// call are in include/pkv.h.
+
+#include "../../include/pkv.h"
+#include "internal.h"
+
+#include <cmath>
+#include <cstring>
+
+namespace {
+
+bool attn_shape_ok(const pkv_attn_shape* s) {
+  if (!s) return false;
+  if (s->num_seqs < 0 || s->num_q_heads < 1 || s->num_kv_heads < 1) return false;
+  if (s->num_q_heads % s->num_kv_heads) return false;
+  if (s->head_dim != 64 && s->head_dim != 128) return false;
+  if (s->page_size != PKV_PAGE_SIZE) return false;
+  if (s->num_pages < 1 || s->max_pages_per_seq < 1 || s->total_q < 0) return false;
+  if (s->max_q_len < 1 || s->max_q_len > PKV_MAX_Q_LEN) return false;
+  const long rows = (long)s->max_q_len * (s->num_q_heads / s->num_kv_heads);
+  if (rows > PKV_MAX_ROWS) return false;
+  if (!std::isfinite(s->scale)) return false;
+  // 32-bit indexing limits inside the kernels
+  if ((long)s->num_seqs * s->max_pages_per_seq > (1L << 31) - 1) return false;
+  if ((long)s->num_pages * s->num_kv_heads * PKV_PAGE_SIZE * s->head_dim > (1L << 40)) return false;
+  if ((long)s->num_seqs * s->num_kv_heads * s->max_pages_per_seq > (1L << 30)) return false;
+  return true;
+}
+
+bool accept_shape_ok(const pkv_accept_shape* s) {
+  if (!s) return false;
+  if (s->num_seqs < 0 || s->vocab < 1 || s->total_rows < 0) return false;
+  if (s->max_draft < 0 || s->max_draft > PKV_MAX_Q_LEN - 1) return false;
+  if (s->total_rows < s->num_seqs) return false;
+  if ((long)s->total_rows * s->vocab > (1L << 40)) return false;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t pkv_attn_workspace_bytes(const pkv_attn_shape* s) {
+  if (!attn_shape_ok(s)) return 0;
+  const int group = s->num_q_heads / s->num_kv_heads;
+  return pkv::attn_workspace(s->num_seqs, s->num_kv_heads, s->max_pages_per_seq, s->max_q_len, group,
+                             s->head_dim)
+      .total;
+}
+
+int pkv_attn_workspace_init(void* workspace, size_t bytes, void* stream) {
+  if (!workspace) return PKV_ERR_NULL;
+  if (hipMemsetAsync(workspace, 0, bytes, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return PKV_ERR_HIP;
+  return PKV_OK;
+}
+
+int pkv_attn_fwd(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_table,
+                 const int32_t* seq_lens, const int32_t* q_lens, float* out, const pkv_attn_shape* s,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+  if (!s) return PKV_ERR_NULL;
+  if (!attn_shape_ok(s)) return PKV_ERR_SHAPE;
+  if (s->num_seqs == 0 || s->total_q == 0) return PKV_OK;
+  if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !q_lens || !out) return PKV_ERR_NULL;
+  const int group = s->num_q_heads / s->num_kv_heads;
+  const pkv::AttnWorkspace ws = pkv::attn_workspace(s->num_seqs, s->num_kv_heads, s->max_pages_per_seq,
+                                                    s->max_q_len, group, s->head_dim);
+  if (!workspace || workspace_bytes < ws.total) return PKV_ERR_WORKSPACE;
+  const pkv::AttnPlan plan = pkv::attn_plan(s->num_seqs, s->num_kv_heads, s->max_pages_per_seq,
+                                            s->max_q_len, group);
+  char* w = static_cast<char*>(workspace);
+  pkv::AttnParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k_pool = static_cast<const uint16_t*>(k_pool);
+  p.v_pool = static_cast<const uint16_t*>(v_pool);
+  p.block_table = block_table;
+  p.seq_lens = seq_lens;
+  p.q_lens = q_lens;
+  p.out = out;
+  p.err = reinterpret_cast<uint32_t*>(w + ws.err_off);
+  p.counters = reinterpret_cast<uint32_t*>(w + ws.counters_off);
+  p.part_ml = reinterpret_cast<float*>(w + ws.ml_off);
+  p.part_acc = reinterpret_cast<float*>(w + ws.acc_off);
+  p.B = s->num_seqs;
+  p.Hq = s->num_q_heads;
+  p.Hkv = s->num_kv_heads;
+  p.group = group;
+  p.D = s->head_dim;
+  p.P = s->num_pages;
+  p.W = s->max_pages_per_seq;
+  p.total_q = s->total_q;
+  p.max_q_len = s->max_q_len;
+  p.rows_max = plan.rows;
+  p.pps = plan.pps;
+  p.max_splits = plan.max_splits;
+  p.num_items = s->num_seqs * s->num_kv_heads * plan.max_splits;
+  p.scale_log2 = static_cast<float>(static_cast<double>(s->scale) * 1.4426950408889634);
+  if (pkv::launch_attn(p, plan, static_cast<hipStream_t>(stream)) != hipSuccess) return PKV_ERR_HIP;
+  return PKV_OK;
+}
+
+int pkv_attn_check_errors(void* workspace, void* stream, uint32_t* flags) {
+  if (!workspace || !flags) return PKV_ERR_NULL;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint32_t v = 0;
+  if (hipMemcpyAsync(&v, workspace, 4, hipMemcpyDeviceToHost, st) != hipSuccess) return PKV_ERR_HIP;
+  if (hipStreamSynchronize(st) != hipSuccess) return PKV_ERR_HIP;
+  if (hipMemsetAsync(workspace, 0, 4, st) != hipSuccess) return PKV_ERR_HIP;
+  if (hipStreamSynchronize(st) != hipSuccess) return PKV_ERR_HIP;
+  *flags = v;
+  return PKV_OK;
+}
+
+size_t pkv_accept_workspace_bytes(const pkv_accept_shape* s) {
+  if (!accept_shape_ok(s)) return 0;
+  return pkv::accept_workspace(s->total_rows, s->vocab).total;
+}
+
+int pkv_accept(const float* logits, const int32_t* draft_ids, const int32_t* n_draft, int32_t* out_accept,
+               int32_t* out_next, int32_t* window, const pkv_accept_shape* s, void* workspace,
+               size_t workspace_bytes, void* stream) {
+  if (!s) return PKV_ERR_NULL;
+  if (!accept_shape_ok(s)) return PKV_ERR_SHAPE;
+  if (s->num_seqs == 0) return PKV_OK;
+  if (!logits || !n_draft || !out_accept || !out_next) return PKV_ERR_NULL;
+  if (!draft_ids && s->total_rows > s->num_seqs) return PKV_ERR_NULL;
+  const pkv::AcceptWorkspace ws = pkv::accept_workspace(s->total_rows, s->vocab);
+  if (!workspace || workspace_bytes < ws.total) return PKV_ERR_WORKSPACE;
+  char* w = static_cast<char*>(workspace);
+  pkv::AcceptParams p;
+  p.logits = logits;
+  p.draft_ids = draft_ids;
+  p.n_draft = n_draft;
+  p.out_accept = out_accept;
+  p.out_next = out_next;
+  p.window = window;
+  p.chunk_val = reinterpret_cast<float*>(w + ws.val_off);
+  p.chunk_idx = reinterpret_cast<int32_t*>(w + ws.idx_off);
+  p.B = s->num_seqs;
+  p.V = s->vocab;
+  p.total_rows = s->total_rows;
+  p.max_draft = s->max_draft;
+  p.chunks = ws.chunks;
+  p.chunk_len = ws.chunk_len;
+  if (pkv::launch_accept(p, static_cast<hipStream_t>(stream)) != hipSuccess) return PKV_ERR_HIP;
+  return PKV_OK;
+}
+
+int32_t pkv_window_next(int32_t window, int32_t n_draft, int32_t accepted) {
+  if (accepted == n_draft + 1) return window + 2;
+  return window - 1 < 1 ? 1 : window - 1;
+}
+
+const char* pkv_status_string(int status) {
+  switch (status) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_NULL: return "a required pointer is NULL";
+    case PKV_ERR_SHAPE: return "shape field out of range";
+    case PKV_ERR_WORKSPACE: return "workspace missing or too small";
+    case PKV_ERR_HIP: return "HIP launch or runtime call failed";
+    default: return "unknown status";
+  }
+}
+
+int pkv_version(void) { return 100; }
+
+}  // extern "C"

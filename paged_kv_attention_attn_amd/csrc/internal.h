@@ -1,0 +1,69 @@
+// Internal launch interface between the C ABI (host.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pkv {
+
+constexpr int kPage = 256;
+constexpr int kNumXcd = 8;  // MI355X: 8 XCDs, workgroups dispatched round-robin
+
+struct AttnParams {
+  const uint16_t* q;
+  const uint16_t* k_pool;
+  const uint16_t* v_pool;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  const int32_t* q_lens;
+  float* out;
+  float* part_acc;      // [items][rows_max][D]
+  float* part_ml;       // [items][rows_max][2] = (running max (log2 units), sum)
+  uint32_t* counters;   // [B * Hkv] splits finished per (sequence, KV head)
+  uint32_t* err;        // error word
+  int32_t B, Hq, Hkv, group, D, P, W, total_q, max_q_len, rows_max;
+  int32_t pps;          // pages per split
+  int32_t max_splits;   // ceil(W / pps)
+  int32_t num_items;    // B * Hkv * max_splits
+  float scale_log2;     // scale * log2(e)
+};
+
+// Workspace layout for a shape (byte offsets from the workspace base).
+struct AttnWorkspace {
+  size_t err_off, counters_off, ml_off, acc_off, total;
+};
+
+// Plan: pages per split and the kernel variant for a shape.
+struct AttnPlan {
+  int pps;
+  int max_splits;
+  int rows;      // rows_max = max_q_len * group
+  bool mfma;     // row tile on matrix cores (rows >= 16)
+};
+
+AttnPlan attn_plan(int B, int Hkv, int W, int max_q_len, int group);
+AttnWorkspace attn_workspace(int B, int Hkv, int W, int max_q_len, int group, int D);
+hipError_t launch_attn(const AttnParams& p, const AttnPlan& plan, hipStream_t stream);
+
+struct AcceptParams {
+  const float* logits;
+  const int32_t* draft_ids;
+  const int32_t* n_draft;
+  int32_t* out_accept;
+  int32_t* out_next;
+  int32_t* window;       // nullable
+  float* chunk_val;      // [total_rows][chunks]
+  int32_t* chunk_idx;    // [total_rows][chunks]
+  int32_t B, V, total_rows, max_draft, chunks, chunk_len;
+};
+
+struct AcceptWorkspace {
+  size_t val_off, idx_off, total;
+  int chunks, chunk_len;
+};
+
+AcceptWorkspace accept_workspace(int total_rows, int V);
+hipError_t launch_accept(const AcceptParams& p, hipStream_t stream);
+
+}  // namespace pkv

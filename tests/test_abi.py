@@ -1,0 +1,125 @@
+"""The C-ABI library: it loads, exports every function include/pkv.h declares,
+and its host-side checks reject bad shapes before any GPU work. No kernel is
+launched here, so these run on a machine without a GPU."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pkv.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(pkv_[a-z_0-9]+)\s*\(", text,
+                       flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def pk():
+    import paged_kv_attention_attn_amd as pk
+    return pk
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("pkv_attn_fwd", "pkv_accept", "pkv_attn_workspace_bytes",
+                     "pkv_accept_workspace_bytes", "pkv_window_next", "pkv_status_string"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(pk):
+    lib = ctypes.CDLL(pk.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+    assert sorted(pk.EXPORTS) == declared_functions()
+
+
+def test_struct_layouts_match_the_header(pk):
+    assert ctypes.sizeof(pk.pkv_attn_shape) == 40
+    assert ctypes.sizeof(pk.pkv_accept_shape) == 16
+
+
+def test_window_rule_on_the_host(pk):
+    assert pk.pkv_window_next(5, 5, 6) == 7
+    assert pk.pkv_window_next(5, 5, 3) == 4
+    assert pk.pkv_window_next(1, 1, 1) == 1
+    assert pk.pkv_window_next(3, 0, 1) == 5
+
+
+def good_shape(pk, **kw):
+    f = dict(num_seqs=4, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=256, num_pages=64,
+             max_pages_per_seq=8, total_q=4, max_q_len=1, scale=0.088)
+    f.update(kw)
+    return pk.pkv_attn_shape(**f)
+
+
+@pytest.mark.parametrize("bad", [
+    dict(num_q_heads=30),            # Hq % Hkv != 0
+    dict(head_dim=96),               # unsupported D
+    dict(page_size=128),             # pages are 256 tokens
+    dict(max_q_len=0), dict(max_q_len=17),
+    dict(num_q_heads=64, max_q_len=16),   # 16 * 8 rows > 64
+    dict(num_pages=0), dict(max_pages_per_seq=0), dict(num_seqs=-1),
+    dict(scale=float("nan")),
+])
+def test_bad_attention_shapes_are_rejected_before_launch(pk, bad):
+    s = good_shape(pk, **bad)
+    assert pk.pkv_attn_workspace_bytes(s) == 0
+    rc = pk.LIB.pkv_attn_fwd(None, None, None, None, None, None, None, ctypes.byref(s), None, 0, None)
+    assert rc == pk.PKV_ERR_SHAPE
+
+
+def test_null_pointers_and_small_workspace_are_rejected(pk):
+    s = good_shape(pk)
+    dummy = ctypes.c_void_p(0x1000)
+    rc = pk.LIB.pkv_attn_fwd(None, dummy, dummy, dummy, dummy, dummy, dummy, ctypes.byref(s), dummy,
+                             1 << 30, None)
+    assert rc == pk.PKV_ERR_NULL
+    need = pk.pkv_attn_workspace_bytes(s)
+    assert need > 0
+    rc = pk.LIB.pkv_attn_fwd(dummy, dummy, dummy, dummy, dummy, dummy, dummy, ctypes.byref(s), dummy,
+                             need - 1, None)
+    assert rc == pk.PKV_ERR_WORKSPACE
+    rc = pk.LIB.pkv_attn_fwd(dummy, dummy, dummy, dummy, dummy, dummy, dummy, None, dummy, need, None)
+    assert rc == pk.PKV_ERR_NULL
+
+
+def test_empty_batch_is_a_no_op(pk):
+    s = good_shape(pk, num_seqs=0, total_q=0)
+    rc = pk.LIB.pkv_attn_fwd(None, None, None, None, None, None, None, ctypes.byref(s), None, 0, None)
+    assert rc == pk.PKV_OK
+
+
+@pytest.mark.parametrize("bad", [dict(vocab=0), dict(max_draft=16), dict(total_rows=1, num_seqs=2),
+                                 dict(num_seqs=-1)])
+def test_bad_accept_shapes_are_rejected(pk, bad):
+    f = dict(num_seqs=2, vocab=100, total_rows=4, max_draft=3)
+    f.update(bad)
+    s = pk.pkv_accept_shape(**f)
+    assert pk.pkv_accept_workspace_bytes(s) == 0
+    rc = pk.LIB.pkv_accept(None, None, None, None, None, None, ctypes.byref(s), None, 0, None)
+    assert rc == pk.PKV_ERR_SHAPE
+
+
+def test_accept_workspace_and_nulls(pk):
+    s = pk.pkv_accept_shape(8, 128256, 48, 5)
+    need = pk.pkv_accept_workspace_bytes(s)
+    assert need >= 48 * 8
+    dummy = ctypes.c_void_p(0x1000)
+    rc = pk.LIB.pkv_accept(dummy, dummy, dummy, dummy, dummy, None, ctypes.byref(s), dummy, need - 1,
+                           None)
+    assert rc == pk.PKV_ERR_WORKSPACE
+    rc = pk.LIB.pkv_accept(None, dummy, dummy, dummy, dummy, None, ctypes.byref(s), dummy, need, None)
+    assert rc == pk.PKV_ERR_NULL
+
+
+def test_status_strings(pk):
+    for code in (0, -1, -2, -3, -4):
+        assert pk.pkv_status_string(code)
+    assert pk.pkv_version() >= 100

@@ -1,0 +1,175 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle on the
+same seeded inputs. Attention within atol 2e-3 + rtol 1e-2 of the float64
+oracle (rounded to fp32); argmax, accepted count, next token and window
+bit-exact."""
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+import oracle
+from workloads import make_config, make_tiny_case, make_accept_case, Config5Queue
+from tests.gpu_util import say, attn_gpu, assert_close, accept_gpu, DeviceCase
+
+
+@pytest.fixture(scope="module")
+def pk():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import paged_kv_attention_attn_amd as pk
+    return pk
+
+
+def oracle_attn(case):
+    return oracle.attention(case.q, case.k_pool, case.v_pool, case.block_table, case.seq_lens,
+                            case.q_lens, case.scale)
+
+
+# shapes chosen to exercise both row tiles (VALU rows 1..12, MFMA 13..64),
+# both head dims, page boundaries, ragged tails and several splits
+TINY = [
+    # seq_lens, q_lens, Hq, Hkv, D
+    ([1], [1], 1, 1, 64),
+    ([300], [1], 8, 2, 64),
+    ([17, 256, 257, 511], [1, 1, 1, 1], 4, 2, 128),
+    ([700, 33], [3, 2], 8, 2, 128),           # VALU 12 rows
+    ([1030], [2], 8, 4, 64),                  # VALU 4 rows with group 2
+    ([600, 256, 1], [6, 5, 1], 8, 2, 128),    # MFMA 24 rows / 20 rows
+    ([1500, 40], [7, 4], 8, 2, 64),           # MFMA 28 rows
+    ([2100], [16], 16, 4, 128),               # MFMA 64 rows (two row blocks)
+    ([513, 777], [16, 9], 4, 4, 128),         # MHA: 16 rows -> MFMA, 9 rows -> VALU path mixed
+    ([4096, 100, 2], [1, 1, 1], 32, 8, 128),
+    ([258], [6], 32, 8, 128),                 # window straddles a page boundary
+    ([3000], [5], 2, 1, 64),
+]
+
+
+@pytest.mark.parametrize("i", range(len(TINY)))
+def test_tiny_shapes(pk, i):
+    seq_lens, q_lens, Hq, Hkv, D = TINY[i]
+    say(f"tiny case {i}: seq_lens={seq_lens} q_lens={q_lens} Hq={Hq} Hkv={Hkv} D={D}")
+    case = make_tiny_case(100 + i, seq_lens, q_lens, Hq=Hq, Hkv=Hkv, D=D, table_width=None)
+    got, flags = attn_gpu(case, pk)
+    assert flags == 0
+    assert_close(got, oracle_attn(case), f"tiny {i}")
+
+
+def test_config1(pk):
+    say("config 1")
+    case, acc = make_config(1)
+    got, flags = attn_gpu(case, pk)
+    assert flags == 0
+    assert_close(got, oracle_attn(case), "config 1")
+    a, n, w = accept_gpu(acc, pk)
+    ea, en, _ = oracle.accept(acc.logits, acc.draft_ids, acc.n_draft)
+    np.testing.assert_array_equal(a, ea)
+    np.testing.assert_array_equal(n, en)
+    np.testing.assert_array_equal(w, oracle.window_next(acc.window, acc.n_draft, ea))
+
+
+@pytest.mark.timeout(600)
+def test_config2(pk):
+    say("config 2")
+    case, _ = make_config(2)
+    got, flags = attn_gpu(case, pk)
+    assert flags == 0
+    assert_close(got, oracle_attn(case), "config 2")
+
+
+@pytest.mark.timeout(600)
+def test_config3(pk):
+    say("config 3")
+    case, acc = make_config(3)
+    got, flags = attn_gpu(case, pk)
+    assert flags == 0
+    assert_close(got, oracle_attn(case), "config 3")
+    a, n, w = accept_gpu(acc, pk)
+    ea, en, _ = oracle.accept(acc.logits, acc.draft_ids, acc.n_draft)
+    np.testing.assert_array_equal(a, ea)
+    np.testing.assert_array_equal(a, acc.planted_match + 1)
+    np.testing.assert_array_equal(n, en)
+    np.testing.assert_array_equal(w, oracle.window_next(acc.window, acc.n_draft, ea))
+
+
+@pytest.mark.timeout(600)
+def test_config4_and_dedup_twin(pk):
+    from workloads import duplicate_shared_pages
+    say("config 4")
+    case, _ = make_config(4)
+    got, flags = attn_gpu(case, pk)
+    assert flags == 0
+    assert_close(got, oracle_attn(case), "config 4")
+    say("config 4 duplicated-prefix twin")
+    twin = duplicate_shared_pages(case)
+    got2, flags2 = attn_gpu(twin, pk)
+    assert flags2 == 0
+    np.testing.assert_array_equal(got, got2)
+
+
+@pytest.mark.timeout(900)
+def test_config5_queue(pk):
+    q = Config5Queue(seed=0)
+    ref = {}
+    for st in q.steps():
+        c = st.case
+        say(f"config 5 step {st.index}: {c.num_seqs} sequences, {int(c.seq_lens.sum())} tokens")
+        got, flags = attn_gpu(c, pk)
+        assert flags == 0
+        r0 = 0
+        for b, jid in enumerate(st.job_ids):
+            ql = int(c.q_lens[b])
+            if jid not in ref:
+                jc, _ = q.job_case(jid)
+                ref[jid] = oracle_attn(jc)
+            assert_close(got[r0:r0 + ql], ref[jid], f"config 5 step {st.index} job {jid}")
+            r0 += ql
+        a, n, w = accept_gpu(st.accept, pk)
+        ea, en, _ = oracle.accept(st.accept.logits, st.accept.draft_ids, st.accept.n_draft)
+        np.testing.assert_array_equal(a, ea)
+        np.testing.assert_array_equal(a, st.accept.planted_match + 1)
+        np.testing.assert_array_equal(n, en)
+
+
+def test_accept_random_rows_ties_and_nan(pk):
+    say("accept: random rows, ties, NaN")
+    acc = make_accept_case(3, [1, 2, 6, 16, 1, 9], 1001)   # vocab not a multiple of 4
+    lg = acc.logits
+    lg[0, [5, 900]] = 99.0                  # tie: lowest index wins
+    lg[1, 17] = np.nan                      # NaN wins
+    lg[2, [3, 1000]] = np.nan               # first NaN wins
+    lg[9, :] = -np.inf                      # all -inf: index 0
+    lg[10, 1000] = np.inf
+    a, n, _ = accept_gpu(acc, pk, window=False)
+    ea, en, _ = oracle.accept(lg, acc.draft_ids, acc.n_draft)
+    np.testing.assert_array_equal(a, ea)
+    np.testing.assert_array_equal(n, en)
+
+
+def test_accept_large_vocab_many_sequences(pk):
+    say("accept: 200 sequences over 128256 logits")
+    rng = np.random.default_rng(5)
+    q_lens = rng.integers(1, 17, 200)
+    acc = make_accept_case(6, q_lens, 128256)
+    a, n, w = accept_gpu(acc, pk)
+    ea, en, _ = oracle.accept(acc.logits, acc.draft_ids, acc.n_draft)
+    np.testing.assert_array_equal(a, ea)
+    np.testing.assert_array_equal(a, acc.planted_match + 1)
+    np.testing.assert_array_equal(n, en)
+    np.testing.assert_array_equal(w, oracle.window_next(acc.window, acc.n_draft, ea))
+
+
+def test_longest_sequence_in_a_full_pool(pk):
+    say("one 65536-token sequence over a 256-page pool, window 16 x group 4")
+    case = make_tiny_case(7, [65536], [16], Hq=8, Hkv=2, D=128, num_pages=256)
+    got, flags = attn_gpu(case, pk)
+    assert flags == 0
+    assert_close(got, oracle_attn(case), "longest")
+
+
+def test_sequences_with_empty_windows_are_skipped(pk):
+    say("q_len 0 sequences")
+    case = make_tiny_case(8, [300, 50, 700], [2, 0, 1], Hq=8, Hkv=2, D=64)
+    got, flags = attn_gpu(case, pk)
+    assert flags == 0
+    assert_close(got, oracle_attn(case), "empty windows")
