@@ -12,6 +12,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libpkv.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SOURCES = ["attn_kernels.hip", "accept_kernels.hip", "host.cpp"]
@@ -29,7 +30,7 @@ def build(verbose=False):
         # host.cpp carries HIP runtime calls; compile it as HIP too
         srcs += (["-x", "hip", path] if s.endswith(".cpp") else [path])
     tmp = LIB + ".tmp"
-    cmd = [HIPCC] + FLAGS + srcs + ["-o", tmp]
+    cmd = [HIPCC] + FLAGS + ["-I", INCLUDE] + srcs + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -46,7 +46,19 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
+#ifndef PKV_VALU_NBUF
+#define PKV_VALU_NBUF 2  // LDS ring depth (chunks) per wave, VALU row tile
+#endif
+#ifndef PKV_MFMA_NBUF
+#define PKV_MFMA_NBUF 2  // LDS ring depth (chunks) per wave, MFMA row tile
+#endif
+#ifndef PKV_FORCE_PPS
+#define PKV_FORCE_PPS 0  // pages per split; 0 = planned per shape
+#endif
+
 constexpr int kWaves = 4;
+constexpr int kNumCu = 256;           // MI355X compute units
+constexpr int kLdsPerCu = 160 * 1024;  // gfx950 LDS per CU
 constexpr int kThreads = kWaves * 64;
 constexpr float kNegInf = -__builtin_inff();
 
@@ -113,6 +125,16 @@ __device__ __forceinline__ float shfl_xor(float x, int m) {
 }
 
 __device__ __forceinline__ float exp2f_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Split partials cross XCDs (each XCD has its own L2). Agent-scope relaxed
+// atomic stores/loads are write-through / coherent by themselves, so the
+// partials need no L2-wide write-back or invalidate.
+__device__ __forceinline__ void st_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_coherent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 __device__ __forceinline__ float bf16lo(u32 w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi(u32 w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -207,18 +229,21 @@ struct ValuTile {
     const int lane = threadIdx.x & 63;
     const int rg = lane >> 4, t = lane & 15;
     const u32x4* kl = reinterpret_cast<const u32x4*>(kt);
+    // the whole token row first, so the LDS reads overlap each other
+    u32x4 kv[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) kv[c] = kl[t * NC + (c ^ (t & (NC - 1)))];
     float s[RPL];
 #pragma unroll
     for (int j = 0; j < RPL; ++j) s[j] = 0.f;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      const u32x4 kv = kl[t * NC + (c ^ (t & (NC - 1)))];
 #pragma unroll
       for (int j = 0; j < RPL; ++j) {
-        s[j] = dot2(q[j][4 * c + 0], kv.x, s[j]);
-        s[j] = dot2(q[j][4 * c + 1], kv.y, s[j]);
-        s[j] = dot2(q[j][4 * c + 2], kv.z, s[j]);
-        s[j] = dot2(q[j][4 * c + 3], kv.w, s[j]);
+        s[j] = dot2(q[j][4 * c + 0], kv[c].x, s[j]);
+        s[j] = dot2(q[j][4 * c + 1], kv[c].y, s[j]);
+        s[j] = dot2(q[j][4 * c + 2], kv[c].z, s[j]);
+        s[j] = dot2(q[j][4 * c + 3], kv[c].w, s[j]);
       }
     }
     const int tok = tok0 + t;
@@ -459,7 +484,7 @@ struct KernelCfg {
   static constexpr int STAGE = kWaves * (RING + Tile::PBUF);
   static constexpr int MERGE = kWaves * Tile::RP * (D + 2) * 4;
   static constexpr int SMEM = STAGE > MERGE ? STAGE : MERGE;
-  static constexpr int MAX_PPS = 8;
+  static constexpr int MAX_PPS = 64;
 };
 
 template <int D, class Tile, int NBUF>
@@ -494,8 +519,8 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnParams p) {
   }
   if (s >= n_splits) return;
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int q_start = wave_prefix(p.q_lens, b);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int q_start = __builtin_amdgcn_readfirstlane(wave_prefix(p.q_lens, b));
   if (q_start + q_len > p.total_q) {
     if (s == 0 && g == 0 && threadIdx.x == 0) atomicOr(p.err, 4u);
     return;
@@ -557,6 +582,10 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnParams p) {
   // rows of this sequence: window rows times the head group (<= Tile::RP)
   Tile tile;
   tile.init(p.q, p.Hq, p.group, g, q_len * p.group, q_start, seq_len, q_len);
+  // Retire every compiler-visible load now (q rows, table entries): the
+  // waitcnt pass then has nothing outstanding to wait for inside the loop,
+  // where its waits would also drain the direct-to-LDS prefetches.
+  __builtin_amdgcn_s_waitcnt(0);
 
 #pragma unroll
   for (int k = 0; k < NBUF - 1; ++k)
@@ -616,39 +645,41 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnParams p) {
       const int h = g * p.group + r % p.group;
       p.out[((size_t)(q_start + wpos) * p.Hq + h) * D + d] = A / L;
     } else {
-      p.part_acc[((size_t)it * p.rows_max + r) * D + d] = A;
+      st_coherent(&p.part_acc[((size_t)it * p.rows_max + r) * D + d], A);
       if (d == 0) {
-        p.part_ml[((size_t)it * p.rows_max + r) * 2 + 0] = M;
-        p.part_ml[((size_t)it * p.rows_max + r) * 2 + 1] = L;
+        st_coherent(&p.part_ml[((size_t)it * p.rows_max + r) * 2 + 0], M);
+        st_coherent(&p.part_ml[((size_t)it * p.rows_max + r) * 2 + 1], L);
       }
     }
   }
   if (n_splits == 1) return;
 
-  // ---- last workgroup of (b, g) merges every split in split order
+  // ---- last workgroup of (b, g) merges every split in split order. Every
+  // thread's partial stores are acknowledged (vmcnt 0) before the barrier,
+  // so they are visible device-wide before thread 0 bumps the counter.
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) {
-    const u32 prev = __hip_atomic_fetch_add(p.counters + (b * p.Hkv + g), 1u, __ATOMIC_ACQ_REL,
+    const u32 prev = __hip_atomic_fetch_add(p.counters + (b * p.Hkv + g), 1u, __ATOMIC_RELAXED,
                                             __HIP_MEMORY_SCOPE_AGENT);
     s_last = (prev == (u32)(n_splits - 1));
   }
   __syncthreads();
   if (!s_last) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   const int it0 = (b * p.Hkv + g) * p.max_splits;
   const int qrows = min(rows, q_len * p.group);
   for (int e = threadIdx.x; e < qrows * D; e += kThreads) {
     const int r = e / D, d = e % D;
     float M = kNegInf;
     for (int sp = 0; sp < n_splits; ++sp)
-      M = fmaxf(M, p.part_ml[((size_t)(it0 + sp) * p.rows_max + r) * 2]);
+      M = fmaxf(M, ld_coherent(&p.part_ml[((size_t)(it0 + sp) * p.rows_max + r) * 2]));
     float L = 0.f, A = 0.f;
     for (int sp = 0; sp < n_splits; ++sp) {
       const size_t base = (size_t)(it0 + sp) * p.rows_max + r;
-      const float ms = p.part_ml[base * 2];
+      const float ms = ld_coherent(&p.part_ml[base * 2]);
       const float wt = (ms == kNegInf) ? 0.f : exp2f_fast(ms - M);
-      L += wt * p.part_ml[base * 2 + 1];
-      A += wt * p.part_acc[base * D + d];
+      L += wt * ld_coherent(&p.part_ml[base * 2 + 1]);
+      A += wt * ld_coherent(&p.part_acc[base * D + d]);
     }
     const int wpos = r / p.group, h = g * p.group + r % p.group;
     p.out[((size_t)(q_start + wpos) * p.Hq + h) * D + d] = A / L;
@@ -670,13 +701,13 @@ hipError_t launch_d(const AttnParams& p, const AttnPlan& plan, hipStream_t strea
   if (!plan.mfma) {
     const int rpl = (plan.rows + 3) / 4;
     switch (rpl) {
-      case 1: return launch_one<D, ValuTile<D, 1>, 3>(p, stream);
-      case 2: return launch_one<D, ValuTile<D, 2>, 3>(p, stream);
-      default: return launch_one<D, ValuTile<D, 3>, 3>(p, stream);
+      case 1: return launch_one<D, ValuTile<D, 1>, PKV_VALU_NBUF>(p, stream);
+      case 2: return launch_one<D, ValuTile<D, 2>, PKV_VALU_NBUF>(p, stream);
+      default: return launch_one<D, ValuTile<D, 3>, PKV_VALU_NBUF>(p, stream);
     }
   }
-  if (plan.rows <= 32) return launch_one<D, MfmaTile<D, 1>, 2>(p, stream);
-  return launch_one<D, MfmaTile<D, 2>, 2>(p, stream);
+  if (plan.rows <= 32) return launch_one<D, MfmaTile<D, 1>, PKV_MFMA_NBUF>(p, stream);
+  return launch_one<D, MfmaTile<D, 2>, PKV_MFMA_NBUF>(p, stream);
 }
 
 }  // namespace
@@ -685,12 +716,26 @@ AttnPlan attn_plan(int B, int Hkv, int W, int max_q_len, int group) {
   AttnPlan pl;
   pl.rows = max_q_len * group;
   pl.mfma = pl.rows > 12;
-  // VALU tiles are light on work per byte: one page per split keeps enough
-  // workgroups in flight. The MFMA tile handles 2 pages per split to keep the
-  // partial-result traffic under 5% of the K/V bytes.
-  pl.pps = pl.mfma ? 2 : 1;
-  const long items1 = (long)B * Hkv * ((W + pl.pps - 1) / pl.pps);
-  if (pl.mfma && items1 < 1024) pl.pps = 1;
+  // Workgroups resident per CU, from the LDS each variant claims.
+  int smem;
+  if (pl.mfma)
+    smem = pl.rows <= 32 ? KernelCfg<128, MfmaTile<128, 1>, PKV_MFMA_NBUF>::SMEM
+                         : KernelCfg<128, MfmaTile<128, 2>, PKV_MFMA_NBUF>::SMEM;
+  else
+    smem = KernelCfg<128, ValuTile<128, 3>, PKV_VALU_NBUF>::SMEM;
+  int per_cu = kLdsPerCu / smem;
+  if (per_cu < 1) per_cu = 1;
+  // Pages per split: as few splits as keep one round of workgroups on every
+  // CU. Each extra split costs a partial write and read plus a merge; an
+  // idle CU costs more. The table width bounds every sequence's pages.
+  const long tiles = (long)B * Hkv * W;
+  const long slots = (long)kNumCu * per_cu;
+  long pps = (tiles + slots - 1) / slots;
+  if (PKV_FORCE_PPS > 0) pps = PKV_FORCE_PPS;
+  if (pps < 1) pps = 1;
+  if (pps > W) pps = W;
+  if (pps > 64) pps = 64;  // the kernel stages at most 64 table entries per split
+  pl.pps = (int)pps;
   pl.max_splits = (W + pl.pps - 1) / pl.pps;
   return pl;
 }

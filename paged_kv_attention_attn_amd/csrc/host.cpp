@@ -2,7 +2,7 @@
 // kernel launch on the caller's stream. Declarations and the contract of each
 // call are in include/pkv.h.
 
-#include "../../include/pkv.h"
+#include "pkv.h"
 #include "internal.h"
 
 #include <cmath>
