@@ -43,6 +43,7 @@ using u32 = uint32_t;
 typedef u32 u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -57,6 +58,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 #endif
 
 constexpr int kWaves = 4;
+constexpr u32 PKV_EFLAG_PAGE_BIT = 1u, PKV_EFLAG_QLEN_BIT = 2u, PKV_EFLAG_ROWS_BIT = 4u;
 constexpr int kNumCu = 256;           // MI355X compute units
 constexpr int kLdsPerCu = 160 * 1024;  // gfx950 LDS per CU
 constexpr int kThreads = kWaves * 64;
@@ -189,37 +191,37 @@ struct ValuTile {
   int lim[RPL];
   float acc[RP][8];
 
-  __device__ __forceinline__ void init(const uint16_t* qbase, int Hq, int group, int g, int rows,
-                                       int q_start, int seq_len, int q_len) {
-    const int lane = threadIdx.x & 63;
-    const int rg = lane >> 4;
+  __device__ __forceinline__ void init(int group, int rows, int seq_len, int q_len) {
+    const int rg = (threadIdx.x & 63) >> 4;
 #pragma unroll
     for (int j = 0; j < RPL; ++j) {
       const int r = rg + 4 * j;
       m[j] = kNegInf;
       l[j] = 0.f;
-      if (r < rows) {
-        const int w = r / group, h = g * group + r % group;
-        lim[j] = seq_len - q_len + w;
-        const u32x4* src = reinterpret_cast<const u32x4*>(qbase + ((size_t)(q_start + w) * Hq + h) * D);
-#pragma unroll
-        for (int c = 0; c < D / 8; ++c) {
-          u32x4 v = src[c];
-          q[j][4 * c + 0] = v.x;
-          q[j][4 * c + 1] = v.y;
-          q[j][4 * c + 2] = v.z;
-          q[j][4 * c + 3] = v.w;
-        }
-      } else {
-        lim[j] = -1;
-#pragma unroll
-        for (int c = 0; c < D / 2; ++c) q[j][c] = 0u;
-      }
+      lim[j] = r < rows ? seq_len - q_len + r / group : -1;
     }
 #pragma unroll
     for (int r = 0; r < RP; ++r)
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[r][e] = 0.f;
+  }
+
+  // q rows from the swizzled LDS copy (rows past the window are zero there)
+  __device__ __forceinline__ void load_q(const char* qlds) {
+    const int rg = (threadIdx.x & 63) >> 4;
+    const u32x4* ql = reinterpret_cast<const u32x4*>(qlds);
+#pragma unroll
+    for (int j = 0; j < RPL; ++j) {
+      const int r = rg + 4 * j;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const u32x4 v = ql[r * NC + (c ^ (r & (NC - 1)))];
+        q[j][4 * c + 0] = v.x;
+        q[j][4 * c + 1] = v.y;
+        q[j][4 * c + 2] = v.z;
+        q[j][4 * c + 3] = v.w;
+      }
+    }
   }
 
   // One chunk of TC tokens starting at absolute token tok0; nv of them are
@@ -337,30 +339,33 @@ struct MfmaTile {
   int lim[NRB];
   f32x16 acc[NRB][MB];
 
-  __device__ __forceinline__ void init(const uint16_t* qbase, int Hq, int group, int g, int rows,
-                                       int q_start, int seq_len, int q_len) {
-    const int lane = threadIdx.x & 63;
-    const int row = lane & 31, half = lane >> 5;
+  __device__ __forceinline__ void init(int group, int rows, int seq_len, int q_len) {
+    const int row = threadIdx.x & 31;
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
       const int r = rb * 32 + row;
       m[rb] = kNegInf;
       l[rb] = 0.f;
-      if (r < rows) {
-        const int w = r / group, h = g * group + r % group;
-        lim[rb] = seq_len - q_len + w;
-        const uint16_t* src = qbase + ((size_t)(q_start + w) * Hq + h) * D + half * 8;
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) qb[rb][kk] = *reinterpret_cast<const u32x4*>(src + kk * 16);
-      } else {
-        lim[rb] = -1;
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) qb[rb][kk] = u32x4{0u, 0u, 0u, 0u};
-      }
+      lim[rb] = r < rows ? seq_len - q_len + r / group : -1;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[rb][mb][i] = 0.f;
+    }
+  }
+
+  __device__ __forceinline__ void load_q(const char* qlds) {
+    const int lane = threadIdx.x & 63;
+    const int row = lane & 31, half = lane >> 5;
+    const u32x4* ql = reinterpret_cast<const u32x4*>(qlds);
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      const int r = rb * 32 + row;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const int c = 2 * kk + half;
+        qb[rb][kk] = ql[r * NC + (c ^ (r & (NC - 1)))];
+      }
     }
   }
 
@@ -481,11 +486,28 @@ struct KernelCfg {
   static constexpr int TC = Tile::TC;
   using G = TileGeom<D, TC>;
   static constexpr int RING = NBUF * 2 * G::TILE;        // per wave: K and V tiles
-  static constexpr int STAGE = kWaves * (RING + Tile::PBUF);
+  static constexpr int QB = (Tile::RP * D * 2 + 1023) / 1024 * 1024;  // whole 1 KiB loads
+  static constexpr int NQI = QB / 1024;                  // q load instructions per workgroup
+  static constexpr int STAGE = kWaves * (RING + Tile::PBUF) + QB;
   static constexpr int MERGE = kWaves * Tile::RP * (D + 2) * 4;
   static constexpr int SMEM = STAGE > MERGE ? STAGE : MERGE;
   static constexpr int MAX_PPS = 64;
 };
+
+constexpr int kSc1 = 16;  // cache-policy bit: coherent across XCDs (write-through / miss)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, u32 bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_ahead(int ahead) {
+  // wait until at most `ahead` chunks (N ops each) remain in flight
+  if (ahead >= 3) wait_vmcnt<3 * N>();
+  else if (ahead == 2) wait_vmcnt<2 * N>();
+  else if (ahead == 1) wait_vmcnt<N>();
+  else wait_vmcnt<0>();
+}
 
 template <int D, class Tile, int NBUF>
 __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnParams p) {
@@ -493,6 +515,9 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnParams p) {
   using G = typename C::G;
   constexpr int TC = C::TC;
   constexpr int NI = G::NI;
+  constexpr int NC = G::NC;
+  constexpr int RP = Tile::RP;
+  static_assert(NBUF >= 2 && NBUF <= 4, "ring depth");
   __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
   __shared__ int s_pages[C::MAX_PPS];
   __shared__ int s_last;
@@ -507,35 +532,38 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnParams p) {
   const int rest = item / p.B;
   const int g = rest % p.Hkv;
   const int s = rest / p.Hkv;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
 
+  // independent loads first, so their latencies overlap: the sequence's
+  // lengths, the split's table entries and the window-row prefix sum
+  const int page0 = s * p.pps;
+  int tbl = -1;
+  if ((int)threadIdx.x < p.pps && page0 + (int)threadIdx.x < p.W)
+    tbl = p.block_table[(size_t)b * p.W + page0 + threadIdx.x];
   const int seq_len = p.seq_lens[b];
   const int q_len = p.q_lens[b];
+  const int q_start = __builtin_amdgcn_readfirstlane(wave_prefix(p.q_lens, b));
   if (q_len <= 0) return;
   const int n_pages = (seq_len + kPage - 1) / kPage;
   const int n_splits = (n_pages + p.pps - 1) / p.pps;
   if (q_len > p.max_q_len || q_len > seq_len || n_pages > p.W) {
-    if (s == 0 && g == 0 && threadIdx.x == 0) atomicOr(p.err, 2u);
+    if (s == 0 && g == 0 && threadIdx.x == 0) atomicOr(p.err, PKV_EFLAG_QLEN_BIT);
     return;
   }
   if (s >= n_splits) return;
-
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int q_start = __builtin_amdgcn_readfirstlane(wave_prefix(p.q_lens, b));
   if (q_start + q_len > p.total_q) {
-    if (s == 0 && g == 0 && threadIdx.x == 0) atomicOr(p.err, 4u);
+    if (s == 0 && g == 0 && threadIdx.x == 0) atomicOr(p.err, PKV_EFLAG_ROWS_BIT);
     return;
   }
-
-  const int page0 = s * p.pps;
   const int npg = min(p.pps, n_pages - page0);
-  if (threadIdx.x < npg) {
-    int pg = p.block_table[(size_t)b * p.W + page0 + threadIdx.x];
-    if (pg < 0 || pg >= p.P) {
-      atomicOr(p.err, 1u);
-      pg = -1;
+  if ((int)threadIdx.x < npg) {
+    if (tbl < 0 || tbl >= p.P) {
+      atomicOr(p.err, PKV_EFLAG_PAGE_BIT);
+      tbl = -1;
     }
-    s_pages[threadIdx.x] = pg;
+    s_pages[threadIdx.x] = tbl;
   }
+  const int rows = q_len * p.group;  // <= RP by the plan
   __syncthreads();
 
   const int tok_begin = page0 * kPage;
@@ -545,16 +573,35 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnParams p) {
 
   char* ring = smem + wave * C::RING;
   float* pbuf = reinterpret_cast<float*>(smem + kWaves * C::RING + wave * Tile::PBUF);
+  char* qlds = smem + kWaves * (C::RING + Tile::PBUF);
   const u32 ring_lds = lds_addr_of(ring);
 
-  // per-lane byte offsets of the direct loads (the chunk base goes into the
-  // descriptor, so they are the same for every chunk)
+  // ---- q rows of (b, g) into LDS, XOR-swizzled like the K tiles; rows past
+  // the window read out of range and land as zeros. The waves share the work.
+  {
+    const u32 q_bytes = (u32)p.total_q * p.Hq * D * 2;
+    const u32x4 rq = make_rsrc(p.q, q_bytes);
+    const u32 qbase = lds_addr_of(qlds);
+    for (int i = wave; i < C::NQI; i += kWaves) {
+      const int slot = i * 64 + lane;
+      const int r = slot / NC, pos = slot % NC;
+      u32 off = q_bytes;  // out of range: zero
+      if (r < rows) {
+        const int c = pos ^ (r & (NC - 1));
+        off = (u32)(((q_start + r / p.group) * p.Hq + g * p.group + r % p.group) * D) * 2u + c * 16;
+      }
+      dma16(rq, off, uniform(qbase + i * 1024));
+    }
+  }
+
+  // per-lane byte offsets of the K/V direct loads (the chunk base goes into
+  // the descriptor, so they are the same for every chunk)
   u32 voff[NI];
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int slot = i * 64 + lane;
-    const int t = slot / G::NC, pos = slot % G::NC;
-    voff[i] = t * G::RB + ((pos ^ (t & (G::NC - 1))) * 16);
+    const int t = slot / NC, pos = slot % NC;
+    voff[i] = t * G::RB + ((pos ^ (t & (NC - 1))) * 16);
   }
 
   const size_t head_stride = (size_t)kPage * D;  // elements per (page, head) tile
@@ -579,34 +626,22 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnParams p) {
     for (int i = 0; i < NI; ++i) dma16(rv, voff[i], base + G::TILE + i * 1024);
   };
 
-  // rows of this sequence: window rows times the head group (<= Tile::RP)
   Tile tile;
-  tile.init(p.q, p.Hq, p.group, g, q_len * p.group, q_start, seq_len, q_len);
-  // Retire every compiler-visible load now (q rows, table entries): the
-  // waitcnt pass then has nothing outstanding to wait for inside the loop,
-  // where its waits would also drain the direct-to-LDS prefetches.
-  __builtin_amdgcn_s_waitcnt(0);
-
+  tile.init(p.group, rows, seq_len, q_len);
+  const int pro = min(NBUF - 1, my_chunks);
 #pragma unroll
   for (int k = 0; k < NBUF - 1; ++k)
     if (k < my_chunks) issue(k);
+  // this wave's q loads were issued before its prologue chunks: once at most
+  // `pro` chunks remain in flight they have landed; the barrier covers the
+  // other waves' share
+  wait_ahead<2 * NI>(pro);
+  asm volatile("s_barrier" ::: "memory");
+  tile.load_q(qlds);
 
   for (int k = 0; k < my_chunks; ++k) {
     if (k + NBUF - 1 < my_chunks) issue(k + NBUF - 1);
-    const int ahead = min(NBUF - 1, my_chunks - 1 - k);
-    if constexpr (NBUF >= 4) {
-      if (ahead >= 3) wait_vmcnt<3 * 2 * NI>();
-      else if (ahead == 2) wait_vmcnt<2 * 2 * NI>();
-      else if (ahead == 1) wait_vmcnt<2 * NI>();
-      else wait_vmcnt<0>();
-    } else if constexpr (NBUF == 3) {
-      if (ahead >= 2) wait_vmcnt<2 * 2 * NI>();
-      else if (ahead == 1) wait_vmcnt<2 * NI>();
-      else wait_vmcnt<0>();
-    } else {
-      if (ahead >= 1) wait_vmcnt<2 * NI>();
-      else wait_vmcnt<0>();
-    }
+    wait_ahead<2 * NI>(min(NBUF - 1, my_chunks - 1 - k));
     const int c = wave + k * kWaves;
     const int t0 = tok_begin + c * TC;
     const char* kt = ring + (k % NBUF) * 2 * G::TILE;
@@ -615,77 +650,94 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnParams p) {
 
   // ---- merge the waves in LDS
   __syncthreads();
-  constexpr int RP = Tile::RP;
   float* red_m = reinterpret_cast<float*>(smem);
   float* red_l = red_m + kWaves * RP;
   float* red_acc = red_l + kWaves * RP;
   tile.spill(red_m + wave * RP, red_l + wave * RP, red_acc + (size_t)wave * RP * D);
   __syncthreads();
 
-  const int rows = min(p.rows_max, RP);
-  const int it = (b * p.Hkv + g) * p.max_splits + s;
-  for (int e = threadIdx.x; e < rows * D; e += kThreads) {
-    const int r = e / D, d = e % D;
+  constexpr int D4 = D / 4;
+  const size_t bg = (size_t)b * p.Hkv + g;
+  const u32 acc_bytes = (u32)(p.max_splits * p.rows_max * D * 4);
+  const u32 ml_bytes = (u32)(p.max_splits * p.rows_max * 2 * 4);
+  const auto acc_rsrc = buf_rsrc(p.part_acc + bg * p.max_splits * p.rows_max * D, acc_bytes);
+  const auto ml_rsrc = buf_rsrc(p.part_ml + bg * p.max_splits * p.rows_max * 2, ml_bytes);
+  for (int e = threadIdx.x; e < rows * D4; e += kThreads) {
+    const int r = e / D4, dq = e % D4;
     float M = kNegInf;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) M = fmaxf(M, red_m[w * RP + r]);
-    float L = 0.f, A = 0.f;
+    float L = 0.f;
+    f32x4 A = {0.f, 0.f, 0.f, 0.f};
     if (M != kNegInf) {
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
         const float mw = red_m[w * RP + r];
         const float wt = (mw == kNegInf) ? 0.f : exp2f_fast(mw - M);
         L += wt * red_l[w * RP + r];
-        A += wt * red_acc[((size_t)w * RP + r) * D + d];
+        A += wt * *reinterpret_cast<const f32x4*>(red_acc + ((size_t)w * RP + r) * D + 4 * dq);
       }
     }
-    const int wpos = r / p.group;
-    if (wpos >= q_len) continue;
     if (n_splits == 1) {
       const int h = g * p.group + r % p.group;
-      p.out[((size_t)(q_start + wpos) * p.Hq + h) * D + d] = A / L;
+      *reinterpret_cast<f32x4*>(p.out + ((size_t)(q_start + r / p.group) * p.Hq + h) * D + 4 * dq) = A / L;
     } else {
-      st_coherent(&p.part_acc[((size_t)it * p.rows_max + r) * D + d], A);
-      if (d == 0) {
-        st_coherent(&p.part_ml[((size_t)it * p.rows_max + r) * 2 + 0], M);
-        st_coherent(&p.part_ml[((size_t)it * p.rows_max + r) * 2 + 1], L);
+      // write-through stores: visible to the merging workgroup on any XCD
+      __builtin_amdgcn_raw_buffer_store_b128(A, acc_rsrc, ((s * p.rows_max + r) * D + 4 * dq) * 4, 0, kSc1);
+      if (dq == 0) {
+        const f32x2 ml = {M, L};
+        __builtin_amdgcn_raw_buffer_store_b64(ml, ml_rsrc, (s * p.rows_max + r) * 8, 0, kSc1);
       }
     }
   }
   if (n_splits == 1) return;
 
-  // ---- last workgroup of (b, g) merges every split in split order. Every
-  // thread's partial stores are acknowledged (vmcnt 0) before the barrier,
-  // so they are visible device-wide before thread 0 bumps the counter.
+  // ---- the last workgroup of (b, g) merges every split in split order.
+  // Every thread's partial stores are acknowledged (vmcnt 0) before the
+  // barrier, so they are device-visible before thread 0 bumps the counter.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) {
-    const u32 prev = __hip_atomic_fetch_add(p.counters + (b * p.Hkv + g), 1u, __ATOMIC_RELAXED,
-                                            __HIP_MEMORY_SCOPE_AGENT);
+    const u32 prev = __hip_atomic_fetch_add(p.counters + bg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_last = (prev == (u32)(n_splits - 1));
   }
   __syncthreads();
   if (!s_last) return;
-  const int it0 = (b * p.Hkv + g) * p.max_splits;
-  const int qrows = min(rows, q_len * p.group);
-  for (int e = threadIdx.x; e < qrows * D; e += kThreads) {
-    const int r = e / D, d = e % D;
-    float M = kNegInf;
-    for (int sp = 0; sp < n_splits; ++sp)
-      M = fmaxf(M, ld_coherent(&p.part_ml[((size_t)(it0 + sp) * p.rows_max + r) * 2]));
-    float L = 0.f, A = 0.f;
-    for (int sp = 0; sp < n_splits; ++sp) {
-      const size_t base = (size_t)(it0 + sp) * p.rows_max + r;
-      const float ms = ld_coherent(&p.part_ml[base * 2]);
-      const float wt = (ms == kNegInf) ? 0.f : exp2f_fast(ms - M);
-      L += wt * ld_coherent(&p.part_ml[base * 2 + 1]);
-      A += wt * ld_coherent(&p.part_acc[base * D + d]);
+  for (int e = threadIdx.x; e < rows * D4; e += kThreads) {
+    const int r = e / D4, dq = e % D4;
+    float M = kNegInf, L = 0.f;
+    f32x4 A = {0.f, 0.f, 0.f, 0.f};
+    for (int sp0 = 0; sp0 < n_splits; sp0 += 8) {
+      f32x2 ml[8];
+      f32x4 pa[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        // splits past the end read out of range (zeros) and are dropped below
+        const int sp = sp0 + j < n_splits ? sp0 + j : p.max_splits;
+        ml[j] = __builtin_amdgcn_raw_buffer_load_b64(ml_rsrc, (sp * p.rows_max + r) * 8, 0, kSc1);
+        pa[j] = __builtin_amdgcn_raw_buffer_load_b128(acc_rsrc, ((sp * p.rows_max + r) * D + 4 * dq) * 4, 0,
+                                                      kSc1);
+      }
+      float Mn = M;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (sp0 + j < n_splits) Mn = fmaxf(Mn, ml[j].x);
+      if (Mn == kNegInf) continue;
+      const float f = (M == kNegInf) ? 0.f : exp2f_fast(M - Mn);
+      L *= f;
+      A *= f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float wt = (sp0 + j >= n_splits || ml[j].x == kNegInf) ? 0.f : exp2f_fast(ml[j].x - Mn);
+        L += wt * ml[j].y;
+        A += wt * pa[j];
+      }
+      M = Mn;
     }
-    const int wpos = r / p.group, h = g * p.group + r % p.group;
-    p.out[((size_t)(q_start + wpos) * p.Hq + h) * D + d] = A / L;
+    const int h = g * p.group + r % p.group;
+    *reinterpret_cast<f32x4*>(p.out + ((size_t)(q_start + r / p.group) * p.Hq + h) * D + 4 * dq) = A / L;
   }
-  if (threadIdx.x == 0)
-    __hip_atomic_store(p.counters + (b * p.Hkv + g), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0) __hip_atomic_store(p.counters + bg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int D, class Tile, int NBUF>

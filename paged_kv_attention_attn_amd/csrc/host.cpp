@@ -25,6 +25,7 @@ bool attn_shape_ok(const pkv_attn_shape* s) {
   if ((long)s->num_seqs * s->max_pages_per_seq > (1L << 31) - 1) return false;
   if ((long)s->num_pages * s->num_kv_heads * PKV_PAGE_SIZE * s->head_dim > (1L << 40)) return false;
   if ((long)s->num_seqs * s->num_kv_heads * s->max_pages_per_seq > (1L << 30)) return false;
+  if ((long)s->total_q * s->num_q_heads * s->head_dim * 2 >= (1L << 32)) return false;  // q buffer offsets
   return true;
 }
 
