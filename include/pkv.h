@@ -121,12 +121,14 @@ int pkv_attn_check_errors(void* workspace, void* stream, uint32_t* flags);
 typedef struct {
   int32_t num_seqs;   /* B >= 0                                   */
   int32_t vocab;      /* V >= 1                                   */
-  int32_t total_rows; /* rows of logits; must equal sum(n_draft + 1) */
+  int32_t total_rows; /* rows of logits, <= 65535; must equal sum(n_draft + 1) */
   int32_t max_draft;  /* >= every n_draft[b]; 0..PKV_MAX_Q_LEN - 1   */
 } pkv_accept_shape;
 
-/* Bytes of device workspace pkv_accept needs (0 on a bad shape). No
- * initialisation is required. */
+/* Bytes of device workspace pkv_accept needs (0 on a bad shape). It holds one
+ * counter per sequence and per-chunk argmax partials; it must be zero-filled
+ * before its first use and again before reuse for a different shape (every
+ * call leaves the counters at zero). */
 size_t pkv_accept_workspace_bytes(const pkv_accept_shape* shape);
 
 /*
@@ -146,6 +148,8 @@ size_t pkv_accept_workspace_bytes(const pkv_accept_shape* shape);
  *            rule (pkv_window_next).
  * argmax: lowest index among equal maxima; a NaN counts as the maximum and the
  * first NaN wins. Results are bit-exact.
+ * A sequence whose rows or drafts break the contract gets out_accept = 0 and
+ * out_next = -1. One call at a time per workspace.
  * Contract: sum(n_draft + 1) == total_rows; n_draft[b] <= max_draft.
  */
 int pkv_accept(const float* logits, const int32_t* draft_ids, const int32_t* n_draft,

@@ -158,7 +158,7 @@ def new_accept_workspace(shape, device="cuda"):
     n = pkv_accept_workspace_bytes(shape)
     if n == 0:
         raise PkvError("pkv_accept_workspace_bytes: shape rejected")
-    return torch.empty(n, dtype=torch.uint8, device=device)
+    return torch.zeros(n, dtype=torch.uint8, device=device)
 
 
 def pkv_accept(logits, draft_ids, n_draft, out_accept, out_next, window, shape, workspace, stream=None):

@@ -53,15 +53,19 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 #ifndef PKV_MFMA_NBUF
 #define PKV_MFMA_NBUF 2  // LDS ring depth (chunks) per wave, MFMA row tile
 #endif
+#ifndef PKV_VALU_WAVES
+#define PKV_VALU_WAVES 4  // waves per workgroup, VALU row tile
+#endif
+#ifndef PKV_MFMA_WAVES
+#define PKV_MFMA_WAVES 4  // waves per workgroup, MFMA row tile
+#endif
 #ifndef PKV_FORCE_PPS
 #define PKV_FORCE_PPS 0  // pages per split; 0 = planned per shape
 #endif
 
-constexpr int kWaves = 4;
 constexpr u32 PKV_EFLAG_PAGE_BIT = 1u, PKV_EFLAG_QLEN_BIT = 2u, PKV_EFLAG_ROWS_BIT = 4u;
 constexpr int kNumCu = 256;           // MI355X compute units
 constexpr int kLdsPerCu = 160 * 1024;  // gfx950 LDS per CU
-constexpr int kThreads = kWaves * 64;
 constexpr float kNegInf = -__builtin_inff();
 
 __device__ __forceinline__ u32 uniform(u32 x) { return __builtin_amdgcn_readfirstlane(x); }
@@ -190,6 +194,8 @@ struct ValuTile {
   float m[RPL], l[RPL];
   int lim[RPL];
   float acc[RP][8];
+  u32x4 kv[NC];      // this lane's token row of the current K chunk
+  u32x4 vv[STEPS];   // this lane's V pieces of the current chunk
 
   __device__ __forceinline__ void init(int group, int rows, int seq_len, int q_len) {
     const int rg = (threadIdx.x & 63) >> 4;
@@ -226,15 +232,30 @@ struct ValuTile {
 
   // One chunk of TC tokens starting at absolute token tok0; nv of them are
   // inside the sequence. kt / vt: LDS tiles; pb: this wave's P staging.
-  __device__ __forceinline__ void step(const char* kt, const char* vt, float* pb, int tok0, int nv,
-                                       float scale_log2) {
+  // Copy one chunk's operands out of its LDS slot (so the slot can be
+  // refilled while this chunk is computed): this lane's token row of K and
+  // its 8-dim pieces of V (rows past the sequence zeroed).
+  __device__ __forceinline__ void fetch(const char* kt, const char* vt, int nv) {
     const int lane = threadIdx.x & 63;
-    const int rg = lane >> 4, t = lane & 15;
+    const int t = lane & 15;
     const u32x4* kl = reinterpret_cast<const u32x4*>(kt);
-    // the whole token row first, so the LDS reads overlap each other
-    u32x4 kv[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) kv[c] = kl[t * NC + (c ^ (t & (NC - 1)))];
+    const int tg = lane / NC, dc = lane % NC;
+    const u32x4* vl = reinterpret_cast<const u32x4*>(vt);
+#pragma unroll
+    for (int st = 0; st < STEPS; ++st) {
+      const int tt = st * TG + tg;
+      vv[st] = vl[tt * NC + (dc ^ (tt & (NC - 1)))];
+      if (tt >= nv) vv[st] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  // One chunk of TC tokens starting at absolute token tok0 (nv of them
+  // inside the sequence), from the operands fetch() copied.
+  __device__ __forceinline__ void compute(float* pb, int tok0, int nv, float scale_log2) {
+    const int lane = threadIdx.x & 63;
+    const int rg = lane >> 4, t = lane & 15;
     float s[RPL];
 #pragma unroll
     for (int j = 0; j < RPL; ++j) s[j] = 0.f;
@@ -272,16 +293,14 @@ struct ValuTile {
       }
     }
     // P.V
-    const int tg = lane / NC, dc = lane % NC;
-    const u32x4* vl = reinterpret_cast<const u32x4*>(vt);
+    const int tg = lane / NC;
     const f32x4* pl = reinterpret_cast<const f32x4*>(pb);
 #pragma unroll
     for (int st = 0; st < STEPS; ++st) {
       const int tt = st * TG + tg;
-      u32x4 vv = vl[tt * NC + (dc ^ (tt & (NC - 1)))];
-      if (tt >= nv) vv = u32x4{0u, 0u, 0u, 0u};
-      float v8[8] = {bf16lo(vv.x), bf16hi(vv.x), bf16lo(vv.y), bf16hi(vv.y),
-                     bf16lo(vv.z), bf16hi(vv.z), bf16lo(vv.w), bf16hi(vv.w)};
+      const u32x4 w = vv[st];
+      float v8[8] = {bf16lo(w.x), bf16hi(w.x), bf16lo(w.y), bf16hi(w.y),
+                     bf16lo(w.z), bf16hi(w.z), bf16lo(w.w), bf16hi(w.w)};
 #pragma unroll
       for (int r4 = 0; r4 < RP / 4; ++r4) {
         const f32x4 pp = pl[tt * (RP / 4) + r4];
@@ -338,6 +357,8 @@ struct MfmaTile {
   float m[NRB], l[NRB];
   int lim[NRB];
   f32x16 acc[NRB][MB];
+  u32x4 ka[KK];      // K operand of the current chunk
+  u32x4 va[MB][2];   // V^T operands of the current chunk
 
   __device__ __forceinline__ void init(int group, int rows, int seq_len, int q_len) {
     const int row = threadIdx.x & 31;
@@ -369,11 +390,47 @@ struct MfmaTile {
     }
   }
 
-  __device__ __forceinline__ void step(const char* kt, const char* vt, float*, int tok0, int nv,
-                                       float scale_log2) {
+  // Copy one chunk's MFMA operands out of its LDS slot: the K rows as the
+  // A operand of S^T, and V^T gathered 16 bits at a time as the A operand of
+  // O^T (k index j of lane half h at k-step ks is token 16*ks + 8*(j/4) +
+  // 4*h + j%4, matching where P sits in the S^T result).
+  __device__ __forceinline__ void fetch(const char* kt, const char* vt, int nv) {
     const int lane = threadIdx.x & 63;
     const int row = lane & 31, half = lane >> 5;
     const u32x4* kl = reinterpret_cast<const u32x4*>(kt);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const int c = 2 * kk + half;
+      ka[kk] = kl[row * NC + (c ^ (row & (NC - 1)))];
+    }
+    const uint16_t* vl = reinterpret_cast<const uint16_t*>(vt);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int d = mb * 32 + row;
+      const int dch = d >> 3, dw = d & 7;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        u32 w4[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          u32 lohi[2];
+#pragma unroll
+          for (int z = 0; z < 2; ++z) {
+            const int j = 2 * jj + z;
+            const int tt = 16 * ks + 8 * (j >> 2) + 4 * half + (j & 3);
+            const u32 v = vl[(tt * NC + (dch ^ (tt & (NC - 1)))) * 8 + dw];
+            lohi[z] = (tt < nv) ? v : 0u;
+          }
+          w4[jj] = lohi[0] | (lohi[1] << 16);
+        }
+        va[mb][ks] = u32x4{w4[0], w4[1], w4[2], w4[3]};
+      }
+    }
+  }
+
+  __device__ __forceinline__ void compute(float*, int tok0, int nv, float scale_log2) {
+    const int lane = threadIdx.x & 63;
+    const int half = lane >> 5;
     f32x16 S[NRB];
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb)
@@ -382,11 +439,9 @@ struct MfmaTile {
     // S^T[token][q row] = sum_d K[token][d] * Q[q row][d]
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      const int c = 2 * kk + half;
-      const u32x4 a = kl[row * NC + (c ^ (row & (NC - 1)))];
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb)
-        S[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+        S[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ka[kk]),
                                                         __builtin_bit_cast(bf16x8, qb[rb][kk]), S[rb], 0, 0,
                                                         0);
     }
@@ -425,36 +480,16 @@ struct MfmaTile {
         pb[rb][ks].w = pack_bf16(p[8 * ks + 6], p[8 * ks + 7]);
       }
     }
-    // O^T[d][q row] += sum_token V[token][d] * P[q row][token]; k index j of
-    // lane half h at k-step ks is token 16*ks + 8*(j/4) + 4*h + j%4.
-    const uint16_t* vl = reinterpret_cast<const uint16_t*>(vt);
+    // O^T[d][q row] += sum_token V[token][d] * P[q row][token]
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const int d = mb * 32 + row;
-      const int dch = d >> 3, dw = d & 7;
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        u32 w4[4];
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          u32 lohi[2];
-#pragma unroll
-          for (int z = 0; z < 2; ++z) {
-            const int j = 2 * jj + z;
-            const int tt = 16 * ks + 8 * (j >> 2) + 4 * half + (j & 3);
-            u32 v = vl[(tt * NC + (dch ^ (tt & (NC - 1)))) * 8 + dw];
-            lohi[z] = (tt < nv) ? v : 0u;
-          }
-          w4[jj] = lohi[0] | (lohi[1] << 16);
-        }
-        const u32x4 a = {w4[0], w4[1], w4[2], w4[3]};
+      for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb)
-          acc[rb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+          acc[rb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va[mb][ks]),
                                                                 __builtin_bit_cast(bf16x8, pb[rb][ks]),
                                                                 acc[rb][mb], 0, 0, 0);
-      }
-    }
   }
 
   __device__ __forceinline__ void spill(float* rm, float* rl, float* racc) {
@@ -481,15 +516,17 @@ struct MfmaTile {
 
 // ------------------------------------------------------------------- kernel
 
-template <int D, class Tile, int NBUF>
+template <int D, class Tile, int NBUF, int WAVES>
 struct KernelCfg {
+  static constexpr int W = WAVES;
+  static constexpr int THREADS = WAVES * 64;
   static constexpr int TC = Tile::TC;
   using G = TileGeom<D, TC>;
   static constexpr int RING = NBUF * 2 * G::TILE;        // per wave: K and V tiles
   static constexpr int QB = (Tile::RP * D * 2 + 1023) / 1024 * 1024;  // whole 1 KiB loads
   static constexpr int NQI = QB / 1024;                  // q load instructions per workgroup
-  static constexpr int STAGE = kWaves * (RING + Tile::PBUF) + QB;
-  static constexpr int MERGE = kWaves * Tile::RP * (D + 2) * 4;
+  static constexpr int STAGE = WAVES * (RING + Tile::PBUF) + QB;
+  static constexpr int MERGE = WAVES * Tile::RP * (D + 2) * 4;
   static constexpr int SMEM = STAGE > MERGE ? STAGE : MERGE;
   static constexpr int MAX_PPS = 64;
 };
@@ -500,18 +537,27 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, u32
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
 }
 
-template <int N>
+// Wait until at most `ahead` (0..MAXA) chunks of N load ops each are pending.
+template <int N, int MAXA>
 __device__ __forceinline__ void wait_ahead(int ahead) {
-  // wait until at most `ahead` chunks (N ops each) remain in flight
-  if (ahead >= 3) wait_vmcnt<3 * N>();
-  else if (ahead == 2) wait_vmcnt<2 * N>();
-  else if (ahead == 1) wait_vmcnt<N>();
+  if constexpr (MAXA >= 4) {
+    if (ahead >= 4) { wait_vmcnt<4 * N>(); return; }
+  }
+  if constexpr (MAXA >= 3) {
+    if (ahead >= 3) { wait_vmcnt<3 * N>(); return; }
+  }
+  if constexpr (MAXA >= 2) {
+    if (ahead >= 2) { wait_vmcnt<2 * N>(); return; }
+  }
+  if (ahead >= 1) wait_vmcnt<N>();
   else wait_vmcnt<0>();
 }
 
-template <int D, class Tile, int NBUF>
-__global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnParams p) {
-  using C = KernelCfg<D, Tile, NBUF>;
+template <int D, class Tile, int NBUF, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void attn_split_kernel(AttnParams p) {
+  using C = KernelCfg<D, Tile, NBUF, WAVES>;
+  constexpr int kWaves = WAVES;
+  constexpr int kThreads = WAVES * 64;
   using G = typename C::G;
   constexpr int TC = C::TC;
   constexpr int NI = G::NI;
@@ -628,24 +674,30 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnParams p) {
 
   Tile tile;
   tile.init(p.group, rows, seq_len, q_len);
-  const int pro = min(NBUF - 1, my_chunks);
+  // fill the whole ring
+  const int pro = min(NBUF, my_chunks);
 #pragma unroll
-  for (int k = 0; k < NBUF - 1; ++k)
+  for (int k = 0; k < NBUF; ++k)
     if (k < my_chunks) issue(k);
   // this wave's q loads were issued before its prologue chunks: once at most
   // `pro` chunks remain in flight they have landed; the barrier covers the
   // other waves' share
-  wait_ahead<2 * NI>(pro);
+  wait_ahead<2 * NI, NBUF>(pro);
   asm volatile("s_barrier" ::: "memory");
   tile.load_q(qlds);
 
   for (int k = 0; k < my_chunks; ++k) {
-    if (k + NBUF - 1 < my_chunks) issue(k + NBUF - 1);
-    wait_ahead<2 * NI>(min(NBUF - 1, my_chunks - 1 - k));
+    // chunk k has landed once at most the chunks issued after it are pending
+    wait_ahead<2 * NI, NBUF - 1>(min(NBUF - 1, my_chunks - 1 - k));
     const int c = wave + k * kWaves;
     const int t0 = tok_begin + c * TC;
+    const int nv = min(TC, tok_end - t0);
     const char* kt = ring + (k % NBUF) * 2 * G::TILE;
-    tile.step(kt, kt + G::TILE, pbuf, t0, min(TC, tok_end - t0), p.scale_log2);
+    tile.fetch(kt, kt + G::TILE, nv);
+    // the slot is free once its operands sit in registers: refill it now so
+    // NBUF chunks stay in flight while this one is computed
+    if (k + NBUF < my_chunks) issue(k + NBUF);
+    tile.compute(pbuf, t0, nv, p.scale_log2);
   }
 
   // ---- merge the waves in LDS
@@ -740,11 +792,11 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnParams p) {
   if (threadIdx.x == 0) __hip_atomic_store(p.counters + bg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int D, class Tile, int NBUF>
+template <int D, class Tile, int NBUF, int WAVES>
 hipError_t launch_one(const AttnParams& p, hipStream_t stream) {
   const int per_xcd = (p.num_items + kNumXcd - 1) / kNumXcd;
   const int grid = per_xcd * kNumXcd;
-  hipLaunchKernelGGL((attn_split_kernel<D, Tile, NBUF>), dim3(grid), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((attn_split_kernel<D, Tile, NBUF, WAVES>), dim3(grid), dim3(WAVES * 64), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -753,13 +805,13 @@ hipError_t launch_d(const AttnParams& p, const AttnPlan& plan, hipStream_t strea
   if (!plan.mfma) {
     const int rpl = (plan.rows + 3) / 4;
     switch (rpl) {
-      case 1: return launch_one<D, ValuTile<D, 1>, PKV_VALU_NBUF>(p, stream);
-      case 2: return launch_one<D, ValuTile<D, 2>, PKV_VALU_NBUF>(p, stream);
-      default: return launch_one<D, ValuTile<D, 3>, PKV_VALU_NBUF>(p, stream);
+      case 1: return launch_one<D, ValuTile<D, 1>, PKV_VALU_NBUF, PKV_VALU_WAVES>(p, stream);
+      case 2: return launch_one<D, ValuTile<D, 2>, PKV_VALU_NBUF, PKV_VALU_WAVES>(p, stream);
+      default: return launch_one<D, ValuTile<D, 3>, PKV_VALU_NBUF, PKV_VALU_WAVES>(p, stream);
     }
   }
-  if (plan.rows <= 32) return launch_one<D, MfmaTile<D, 1>, PKV_MFMA_NBUF>(p, stream);
-  return launch_one<D, MfmaTile<D, 2>, PKV_MFMA_NBUF>(p, stream);
+  if (plan.rows <= 32) return launch_one<D, MfmaTile<D, 1>, PKV_MFMA_NBUF, PKV_MFMA_WAVES>(p, stream);
+  return launch_one<D, MfmaTile<D, 2>, PKV_MFMA_NBUF, PKV_MFMA_WAVES>(p, stream);
 }
 
 }  // namespace
@@ -771,10 +823,10 @@ AttnPlan attn_plan(int B, int Hkv, int W, int max_q_len, int group) {
   // Workgroups resident per CU, from the LDS each variant claims.
   int smem;
   if (pl.mfma)
-    smem = pl.rows <= 32 ? KernelCfg<128, MfmaTile<128, 1>, PKV_MFMA_NBUF>::SMEM
-                         : KernelCfg<128, MfmaTile<128, 2>, PKV_MFMA_NBUF>::SMEM;
+    smem = pl.rows <= 32 ? KernelCfg<128, MfmaTile<128, 1>, PKV_MFMA_NBUF, PKV_MFMA_WAVES>::SMEM
+                         : KernelCfg<128, MfmaTile<128, 2>, PKV_MFMA_NBUF, PKV_MFMA_WAVES>::SMEM;
   else
-    smem = KernelCfg<128, ValuTile<128, 3>, PKV_VALU_NBUF>::SMEM;
+    smem = KernelCfg<128, ValuTile<128, 3>, PKV_VALU_NBUF, PKV_VALU_WAVES>::SMEM;
   int per_cu = kLdsPerCu / smem;
   if (per_cu < 1) per_cu = 1;
   // Pages per split: as few splits as keep one round of workgroups on every

@@ -35,6 +35,9 @@ bool accept_shape_ok(const pkv_accept_shape* s) {
   if (s->max_draft < 0 || s->max_draft > PKV_MAX_Q_LEN - 1) return false;
   if (s->total_rows < s->num_seqs) return false;
   if ((long)s->total_rows * s->vocab > (1L << 40)) return false;
+  if (s->total_rows > 65535) return false;  // one grid row per logits row
+  const pkv::AcceptWorkspace ws = pkv::accept_workspace(s->num_seqs, s->total_rows, s->vocab);
+  if ((long)s->total_rows * ws.chunks * 4 >= (1L << 31)) return false;  // chunk-pair offsets
   return true;
 }
 
@@ -115,7 +118,7 @@ int pkv_attn_check_errors(void* workspace, void* stream, uint32_t* flags) {
 
 size_t pkv_accept_workspace_bytes(const pkv_accept_shape* s) {
   if (!accept_shape_ok(s)) return 0;
-  return pkv::accept_workspace(s->total_rows, s->vocab).total;
+  return pkv::accept_workspace(s->num_seqs, s->total_rows, s->vocab).total;
 }
 
 int pkv_accept(const float* logits, const int32_t* draft_ids, const int32_t* n_draft, int32_t* out_accept,
@@ -126,7 +129,7 @@ int pkv_accept(const float* logits, const int32_t* draft_ids, const int32_t* n_d
   if (s->num_seqs == 0) return PKV_OK;
   if (!logits || !n_draft || !out_accept || !out_next) return PKV_ERR_NULL;
   if (!draft_ids && s->total_rows > s->num_seqs) return PKV_ERR_NULL;
-  const pkv::AcceptWorkspace ws = pkv::accept_workspace(s->total_rows, s->vocab);
+  const pkv::AcceptWorkspace ws = pkv::accept_workspace(s->num_seqs, s->total_rows, s->vocab);
   if (!workspace || workspace_bytes < ws.total) return PKV_ERR_WORKSPACE;
   char* w = static_cast<char*>(workspace);
   pkv::AcceptParams p;
@@ -138,6 +141,7 @@ int pkv_accept(const float* logits, const int32_t* draft_ids, const int32_t* n_d
   p.window = window;
   p.chunk_val = reinterpret_cast<float*>(w + ws.val_off);
   p.chunk_idx = reinterpret_cast<int32_t*>(w + ws.idx_off);
+  p.counters = reinterpret_cast<uint32_t*>(w + ws.counters_off);
   p.B = s->num_seqs;
   p.V = s->vocab;
   p.total_rows = s->total_rows;

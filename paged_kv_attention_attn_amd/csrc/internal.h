@@ -55,15 +55,16 @@ struct AcceptParams {
   int32_t* window;       // nullable
   float* chunk_val;      // [total_rows][chunks]
   int32_t* chunk_idx;    // [total_rows][chunks]
+  uint32_t* counters;    // [B] chunks finished per sequence
   int32_t B, V, total_rows, max_draft, chunks, chunk_len;
 };
 
 struct AcceptWorkspace {
-  size_t val_off, idx_off, total;
+  size_t counters_off, val_off, idx_off, total;
   int chunks, chunk_len;
 };
 
-AcceptWorkspace accept_workspace(int total_rows, int V);
+AcceptWorkspace accept_workspace(int B, int total_rows, int V);
 hipError_t launch_accept(const AcceptParams& p, hipStream_t stream);
 
 }  // namespace pkv
