@@ -49,7 +49,57 @@ def parse():
     ap.add_argument("--no-configs", action="store_true", help="skip the per-configuration sweep")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="time budget of the CPU oracle sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run device-to-device copies of a known size (the reference dispatches "
+                         "that scale the rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes)")
     return ap.parse_args()
+
+
+# Sources of the attention kernel: a stored HBM-traffic measurement is used only
+# while their hash matches the one recorded with it.
+KERNEL_SOURCES = ("paged_kv_attention_attn_amd/csrc/attn_kernels.hip",
+                  "paged_kv_attention_attn_amd/csrc/internal.h")
+TRAFFIC_PROFILE = "profiles/attn_split_kernel_mfma.verify_8x8192_w6.md"
+COPY_CAL_BYTES = 256 << 20
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def stored_traffic():
+    """HBM bytes per launch of the verify-workload attention kernel from the
+    committed rocprofv3 counter summary (FETCH_SIZE and WRITE_SIZE, each
+    scaled by its reading on a plain copy of known size), or None when the
+    summary is missing or was taken on different kernel sources."""
+    path = os.path.join(ROOT, TRAFFIC_PROFILE)
+    try:
+        text = open(path).read()
+        block = text.split("```json", 1)[1].split("```", 1)[0]
+        rec = json.loads(block)
+    except (OSError, IndexError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return rec
+
+
+def copy_calibration(torch):
+    """Device-to-device copies of COPY_CAL_BYTES each: the plain copy kernel
+    whose counter readings calibrate FETCH_SIZE and WRITE_SIZE."""
+    src = torch.empty(COPY_CAL_BYTES, dtype=torch.uint8, device="cuda").random_(0, 255)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    n = 5
+    for _ in range(n):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": COPY_CAL_BYTES, "copies": n}), flush=True)
 
 
 class Attn:
@@ -161,6 +211,23 @@ def cpu_baseline(case, acc, seconds):
             "host_cores_available": len(os.sched_getaffinity(0)), "cpu_model": cpu}
 
 
+def roofline(kv_bytes, attn_ms):
+    """Roofline of the attention kernel on the verify workload: algorithmic
+    K/V bytes per launch over the mean launch time measured above, against
+    the HBM peak; `traffic` is the measured HBM bytes per launch."""
+    achieved = kv_bytes / (attn_ms * 1e-3) / 1e9
+    rec = stored_traffic()
+    traffic = None if rec is None else int(rec["hbm_bytes_per_launch"])
+    return {"bound": "hbm", "kernel": "attn_split_kernel<128, MfmaTile<128, 1>, 2, 4>",
+            "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+            "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+            "traffic_gbps": None if traffic is None else round(traffic / (attn_ms * 1e-3) / 1e9, 2),
+            "traffic_profile": TRAFFIC_PROFILE if rec is not None else None,
+            "algorithmic_bytes_per_launch": kv_bytes,
+            "avg_launch_us": round(attn_ms * 1e3, 3)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -174,6 +241,9 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
     props = torch.cuda.get_device_properties(0)
     R = max(1, args.replicas)
 
@@ -230,11 +300,7 @@ def main():
         "verified_tokens_per_s": round(accepted / (step_ms * 1e-3), 1),
         "accepted_per_step": accepted,
         "kv_bytes_per_step": kv_bytes,
-        "roofline": {"bound": "hbm", "kernel": "attn_split_kernel (MFMA row tile, 24 rows)",
-                     "achieved": round(attn_gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(attn_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "algorithmic_bytes_per_launch": kv_bytes,
-                     "avg_launch_us": round(attn_ms * 1e3, 3)},
+        "roofline": roofline(kv_bytes, attn_ms),
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
                    "cus": props.multi_processor_count, "hbm_gib": round(props.total_memory / 2**30, 1)},
     }
