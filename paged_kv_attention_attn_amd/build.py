@@ -20,6 +20,9 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-inline-asm", "-Wno-unused-command-line-argument",
+    # leading scalar kernel arguments arrive in SGPRs at wave launch (gfx950
+    # kernarg preloading), so the first loads do not wait on the argument buffer
+    "-mllvm", "-amdgpu-kernarg-preload-count=8",
 ]
 
 

@@ -91,7 +91,11 @@ __device__ __forceinline__ int wave_scan(int x) {
 // store; the last workgroup of a sequence (a per-sequence counter) merges its
 // rows' pairs in chunk order and applies the accept rule.
 template <bool VEC4>
-__global__ __launch_bounds__(kArgThreads) void accept_fused_kernel(AcceptParams p) {
+__global__ __launch_bounds__(kArgThreads) void accept_fused_kernel(
+    // leading scalars: what the first loads need, preloaded into SGPRs at
+    // wave launch instead of read from the argument buffer
+    const float* __restrict__ logits, const int32_t* __restrict__ n_draft, int V, int chunk_len, int B,
+    AcceptParams p) {
   const int c = blockIdx.x;
   const int r = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -100,9 +104,9 @@ __global__ __launch_bounds__(kArgThreads) void accept_fused_kernel(AcceptParams 
   __shared__ int s_seq[4];   // b, first row, first draft, n_draft
   __shared__ int s_last;
 
-  const int begin = c * p.chunk_len;
-  const int end = min(p.V, begin + p.chunk_len);
-  const float* row = p.logits + (size_t)r * p.V;
+  const int begin = c * chunk_len;
+  const int end = min(V, begin + chunk_len);
+  const float* row = logits + (size_t)r * V;
   float bv = -__builtin_inff();
   int bi = INT_MAX;
   float4 x[kArgUnroll];
@@ -116,13 +120,13 @@ __global__ __launch_bounds__(kArgThreads) void accept_fused_kernel(AcceptParams 
   // wave 0 finds the sequence that owns row r while the loads are in flight
   if (wave == 0) {
     int rb = 0, db = 0, found_b = -1, fr0 = 0, fd0 = 0, fn = 0;
-    for (int i0 = 0; i0 < p.B && found_b < 0; i0 += 64) {
+    for (int i0 = 0; i0 < B && found_b < 0; i0 += 64) {
       const int i = i0 + lane;
-      const int n = i < p.B ? p.n_draft[i] : 0;
-      const int inc_r = wave_scan(i < p.B ? n + 1 : 0);
-      const int inc_d = wave_scan(i < p.B ? n : 0);
+      const int n = i < B ? n_draft[i] : 0;
+      const int inc_r = wave_scan(i < B ? n + 1 : 0);
+      const int inc_d = wave_scan(i < B ? n : 0);
       const int my_r0 = rb + inc_r - (n + 1), my_d0 = db + inc_d - n;
-      const bool mine = i < p.B && r >= my_r0 && r < my_r0 + n + 1;
+      const bool mine = i < B && r >= my_r0 && r < my_r0 + n + 1;
       const unsigned long long ballot = __ballot(mine);
       if (ballot) {
         const int src = __ffsll((long long)ballot) - 1;
@@ -165,7 +169,7 @@ __global__ __launch_bounds__(kArgThreads) void accept_fused_kernel(AcceptParams 
   const int b = s_seq[0], r0 = s_seq[1], d0 = s_seq[2], n = s_seq[3];
   // a row no sequence owns, or a sequence breaking its contract: nothing to do
   const bool ok = b >= 0 && n >= 0 && n <= p.max_draft && r0 + n + 1 <= p.total_rows &&
-                  d0 + n <= p.total_rows - p.B;
+                  d0 + n <= p.total_rows - B;
   const auto val_rsrc = __builtin_amdgcn_make_buffer_rsrc(p.chunk_val, 0, (u32)(p.total_rows * p.chunks * 4),
                                                           0x00020000);
   const auto idx_rsrc = __builtin_amdgcn_make_buffer_rsrc(p.chunk_idx, 0, (u32)(p.total_rows * p.chunks * 4),
@@ -273,9 +277,11 @@ hipError_t launch_accept(const AcceptParams& p, hipStream_t stream) {
   if (p.B == 0 || p.total_rows == 0) return hipSuccess;
   dim3 grid(p.chunks, p.total_rows);
   if (p.V % 4 == 0 && p.chunk_len <= kArgThreads * kArgUnroll * 4)
-    hipLaunchKernelGGL(accept_fused_kernel<true>, grid, dim3(kArgThreads), 0, stream, p);
+    hipLaunchKernelGGL(accept_fused_kernel<true>, grid, dim3(kArgThreads), 0, stream, p.logits, p.n_draft, p.V,
+                       p.chunk_len, p.B, p);
   else
-    hipLaunchKernelGGL(accept_fused_kernel<false>, grid, dim3(kArgThreads), 0, stream, p);
+    hipLaunchKernelGGL(accept_fused_kernel<false>, grid, dim3(kArgThreads), 0, stream, p.logits, p.n_draft, p.V,
+                       p.chunk_len, p.B, p);
   return hipGetLastError();
 }
 

@@ -554,7 +554,11 @@ __device__ __forceinline__ void wait_ahead(int ahead) {
 }
 
 template <int D, class Tile, int NBUF, int WAVES>
-__global__ __launch_bounds__(WAVES * 64) void attn_split_kernel(AttnParams p) {
+__global__ __launch_bounds__(WAVES * 64) void attn_split_kernel(
+    // leading scalars: what the first loads need, preloaded into SGPRs at
+    // wave launch instead of read from the argument buffer
+    const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
+    const int32_t* __restrict__ q_lens, int num_items, int B, int Hkv, int pps, int W, AttnParams p) {
   using C = KernelCfg<D, Tile, NBUF, WAVES>;
   constexpr int kWaves = WAVES;
   constexpr int kThreads = WAVES * 64;
@@ -571,28 +575,28 @@ __global__ __launch_bounds__(WAVES * 64) void attn_split_kernel(AttnParams p) {
   // XCD-aware item order: consecutive logical items (the same split and KV
   // head over consecutive sequences, which share prefix pages under dedup)
   // land on the same XCD and its L2.
-  const int per_xcd = (p.num_items + kNumXcd - 1) / kNumXcd;
+  const int per_xcd = (num_items + kNumXcd - 1) / kNumXcd;
   const int item = (blockIdx.x % kNumXcd) * per_xcd + blockIdx.x / kNumXcd;
-  if (item >= p.num_items) return;
-  const int b = item % p.B;
-  const int rest = item / p.B;
-  const int g = rest % p.Hkv;
-  const int s = rest / p.Hkv;
+  if (item >= num_items) return;
+  const int b = item % B;
+  const int rest = item / B;
+  const int g = rest % Hkv;
+  const int s = rest / Hkv;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
 
   // independent loads first, so their latencies overlap: the sequence's
   // lengths, the split's table entries and the window-row prefix sum
-  const int page0 = s * p.pps;
+  const int page0 = s * pps;
   int tbl = -1;
-  if ((int)threadIdx.x < p.pps && page0 + (int)threadIdx.x < p.W)
-    tbl = p.block_table[(size_t)b * p.W + page0 + threadIdx.x];
-  const int seq_len = p.seq_lens[b];
-  const int q_len = p.q_lens[b];
-  const int q_start = __builtin_amdgcn_readfirstlane(wave_prefix(p.q_lens, b));
+  if ((int)threadIdx.x < pps && page0 + (int)threadIdx.x < W)
+    tbl = block_table[(size_t)b * W + page0 + threadIdx.x];
+  const int seq_len = seq_lens[b];
+  const int q_len = q_lens[b];
+  const int q_start = __builtin_amdgcn_readfirstlane(wave_prefix(q_lens, b));
   if (q_len <= 0) return;
   const int n_pages = (seq_len + kPage - 1) / kPage;
-  const int n_splits = (n_pages + p.pps - 1) / p.pps;
-  if (q_len > p.max_q_len || q_len > seq_len || n_pages > p.W) {
+  const int n_splits = (n_pages + pps - 1) / pps;
+  if (q_len > p.max_q_len || q_len > seq_len || n_pages > W) {
     if (s == 0 && g == 0 && threadIdx.x == 0) atomicOr(p.err, PKV_EFLAG_QLEN_BIT);
     return;
   }
@@ -601,7 +605,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_split_kernel(AttnParams p) {
     if (s == 0 && g == 0 && threadIdx.x == 0) atomicOr(p.err, PKV_EFLAG_ROWS_BIT);
     return;
   }
-  const int npg = min(p.pps, n_pages - page0);
+  const int npg = min(pps, n_pages - page0);
   if ((int)threadIdx.x < npg) {
     if (tbl < 0 || tbl >= p.P) {
       atomicOr(p.err, PKV_EFLAG_PAGE_BIT);
@@ -660,7 +664,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_split_kernel(AttnParams p) {
     const int page_valid = min(kPage, seq_len - (page0 + jp) * kPage);
     int nvt = min(TC, page_valid - in_page);
     if (phys < 0) nvt = 0;
-    const size_t off = ((size_t)(phys < 0 ? 0 : phys) * p.Hkv + g) * head_stride + (size_t)in_page * D;
+    const size_t off = ((size_t)(phys < 0 ? 0 : phys) * Hkv + g) * head_stride + (size_t)in_page * D;
     const u32 bytes = nvt > 0 ? (u32)(nvt * G::RB) : 0u;
     const u32x4 rk = make_rsrc(p.k_pool + off, bytes);
     const u32x4 rv = make_rsrc(p.v_pool + off, bytes);
@@ -709,7 +713,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_split_kernel(AttnParams p) {
   __syncthreads();
 
   constexpr int D4 = D / 4;
-  const size_t bg = (size_t)b * p.Hkv + g;
+  const size_t bg = (size_t)b * Hkv + g;
   const u32 acc_bytes = (u32)(p.max_splits * p.rows_max * D * 4);
   const u32 ml_bytes = (u32)(p.max_splits * p.rows_max * 2 * 4);
   const auto acc_rsrc = buf_rsrc(p.part_acc + bg * p.max_splits * p.rows_max * D, acc_bytes);
@@ -755,39 +759,61 @@ __global__ __launch_bounds__(WAVES * 64) void attn_split_kernel(AttnParams p) {
   }
   __syncthreads();
   if (!s_last) return;
-  for (int e = threadIdx.x; e < rows * D4; e += kThreads) {
-    const int r = e / D4, dq = e % D4;
-    float M = kNegInf, L = 0.f;
-    f32x4 A = {0.f, 0.f, 0.f, 0.f};
-    for (int sp0 = 0; sp0 < n_splits; sp0 += 8) {
-      f32x2 ml[8];
-      f32x4 pa[8];
+  // Each thread owns EPT elements (row, 4 dims) and takes the splits in
+  // batches of SB, issuing every load of a batch before using any: one
+  // memory round trip per batch instead of one per element.
+  constexpr int EPT = (RP * D4 + kThreads - 1) / kThreads;
+  constexpr int SB = EPT <= 2 ? 8 : (EPT <= 4 ? 4 : 2);
+  float M[EPT], L[EPT];
+  f32x4 A[EPT];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+  for (int u = 0; u < EPT; ++u) {
+    M[u] = kNegInf;
+    L[u] = 0.f;
+    A[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  for (int sp0 = 0; sp0 < n_splits; sp0 += SB) {
+    f32x2 ml[EPT][SB];
+    f32x4 pa[EPT][SB];
+#pragma unroll
+    for (int u = 0; u < EPT; ++u) {
+      const int e = threadIdx.x + u * kThreads;
+      const int r = e < rows * D4 ? e / D4 : 0, dq = e % D4;
+#pragma unroll
+      for (int j = 0; j < SB; ++j) {
         // splits past the end read out of range (zeros) and are dropped below
         const int sp = sp0 + j < n_splits ? sp0 + j : p.max_splits;
-        ml[j] = __builtin_amdgcn_raw_buffer_load_b64(ml_rsrc, (sp * p.rows_max + r) * 8, 0, kSc1);
-        pa[j] = __builtin_amdgcn_raw_buffer_load_b128(acc_rsrc, ((sp * p.rows_max + r) * D + 4 * dq) * 4, 0,
-                                                      kSc1);
+        ml[u][j] = __builtin_amdgcn_raw_buffer_load_b64(ml_rsrc, (sp * p.rows_max + r) * 8, 0, kSc1);
+        pa[u][j] = __builtin_amdgcn_raw_buffer_load_b128(acc_rsrc, ((sp * p.rows_max + r) * D + 4 * dq) * 4, 0,
+                                                         kSc1);
       }
-      float Mn = M;
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (sp0 + j < n_splits) Mn = fmaxf(Mn, ml[j].x);
-      if (Mn == kNegInf) continue;
-      const float f = (M == kNegInf) ? 0.f : exp2f_fast(M - Mn);
-      L *= f;
-      A *= f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float wt = (sp0 + j >= n_splits || ml[j].x == kNegInf) ? 0.f : exp2f_fast(ml[j].x - Mn);
-        L += wt * ml[j].y;
-        A += wt * pa[j];
-      }
-      M = Mn;
     }
+#pragma unroll
+    for (int u = 0; u < EPT; ++u) {
+      float Mn = M[u];
+#pragma unroll
+      for (int j = 0; j < SB; ++j)
+        if (sp0 + j < n_splits) Mn = fmaxf(Mn, ml[u][j].x);
+      if (Mn == kNegInf) continue;
+      const float f = (M[u] == kNegInf) ? 0.f : exp2f_fast(M[u] - Mn);
+      L[u] *= f;
+      A[u] *= f;
+#pragma unroll
+      for (int j = 0; j < SB; ++j) {
+        const float wt = (sp0 + j >= n_splits || ml[u][j].x == kNegInf) ? 0.f : exp2f_fast(ml[u][j].x - Mn);
+        L[u] += wt * ml[u][j].y;
+        A[u] += wt * pa[u][j];
+      }
+      M[u] = Mn;
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < EPT; ++u) {
+    const int e = threadIdx.x + u * kThreads;
+    if (e >= rows * D4) continue;
+    const int r = e / D4, dq = e % D4;
     const int h = g * p.group + r % p.group;
-    *reinterpret_cast<f32x4*>(p.out + ((size_t)(q_start + r / p.group) * p.Hq + h) * D + 4 * dq) = A / L;
+    *reinterpret_cast<f32x4*>(p.out + ((size_t)(q_start + r / p.group) * p.Hq + h) * D + 4 * dq) = A[u] / L[u];
   }
   if (threadIdx.x == 0) __hip_atomic_store(p.counters + bg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -796,7 +822,8 @@ template <int D, class Tile, int NBUF, int WAVES>
 hipError_t launch_one(const AttnParams& p, hipStream_t stream) {
   const int per_xcd = (p.num_items + kNumXcd - 1) / kNumXcd;
   const int grid = per_xcd * kNumXcd;
-  hipLaunchKernelGGL((attn_split_kernel<D, Tile, NBUF, WAVES>), dim3(grid), dim3(WAVES * 64), 0, stream, p);
+  hipLaunchKernelGGL((attn_split_kernel<D, Tile, NBUF, WAVES>), dim3(grid), dim3(WAVES * 64), 0, stream,
+                     p.block_table, p.seq_lens, p.q_lens, p.num_items, p.B, p.Hkv, p.pps, p.W, p);
   return hipGetLastError();
 }
 
