@@ -8,12 +8,17 @@
 // dropped; the window grows by 2 after a full match and shrinks by 1
 // otherwise.
 //
-// Kernel 1 scans row chunks (an HBM-bound fp32 stream; one row alone is far
-// too small to fill the chip, so rows are cut into chunks) and writes a
-// (value, index) pair per chunk. Kernel 2 gives one wave per sequence: it
-// merges the chunk pairs of the sequence's rows and applies the accept rule.
+// Two kernels. argmax_kernel scans row chunks (an HBM-bound fp32 stream; one
+// row alone is far too small to fill the chip) and folds each chunk's
+// (value, index) into its row's 64-bit key with one atomic max, issued and
+// never waited on. accept_rule_kernel, one workgroup launched behind it on
+// the same stream, reads the row keys, applies the accept rule and the
+// window update, and clears the keys for the next call. The kernel boundary
+// is the only synchronisation between the two.
+//
 // argmax order: larger value first; NaN above every number; lower index on
-// equal values (and between NaNs), so the result is exact and unique.
+// equal values (and between NaNs); -0 equals +0. The key encodes exactly this
+// order, so the result is exact and unique.
 
 #include "internal.h"
 
@@ -25,7 +30,18 @@ namespace pkv {
 namespace {
 
 using u32 = uint32_t;
-constexpr int kThreads = 256;
+using u64 = unsigned long long;
+
+#ifndef PKV_ARG_THREADS
+#define PKV_ARG_THREADS 512
+#endif
+constexpr int kArgThreads = PKV_ARG_THREADS;  // threads per argmax workgroup
+constexpr int kArgUnroll = 8;                 // float4 loads in flight per thread, at most
+#ifndef PKV_ARG_TARGET_WGS
+#define PKV_ARG_TARGET_WGS 768
+#endif
+constexpr int kArgTargetWgs = PKV_ARG_TARGET_WGS;  // about three workgroups per CU
+constexpr int kRuleThreads = 1024;
 
 // (a, ia) ranks before (b, ib): the larger value, a NaN above every number,
 // the lower index on equal values (and between NaNs). Branch-free.
@@ -59,93 +75,48 @@ __device__ __forceinline__ void wave_best(float& v, int& i) {
   for (int m = 32; m >= 1; m >>= 1) shfl_pair(v, i, m);
 }
 
-#ifndef PKV_ARG_THREADS
-#define PKV_ARG_THREADS 512
-#endif
-#ifndef PKV_ARG_UNROLL
-#define PKV_ARG_UNROLL 8
-#endif
-constexpr int kArgThreads = PKV_ARG_THREADS;  // threads per argmax workgroup
-constexpr int kArgUnroll = PKV_ARG_UNROLL;    // float4 loads in flight per thread
-constexpr int kSc1 = 16;       // cache-policy bit: coherent across XCDs
-
-__device__ __forceinline__ int wave_sum(int s) {
-  const int lane = threadIdx.x & 63;
-  for (int m = 32; m >= 1; m >>= 1) s += __builtin_amdgcn_ds_bpermute(((lane ^ m) << 2), s);
-  return s;
-}
-
-// Inclusive prefix sum over the 64 lanes of a wave.
-__device__ __forceinline__ int wave_scan(int x) {
-  const int lane = threadIdx.x & 63;
-  for (int d = 1; d < 64; d <<= 1) {
-    const int y = __builtin_amdgcn_ds_bpermute(((lane - d) & 63) << 2, x);
-    if (lane >= d) x += y;
+// Order-preserving 64-bit key of (value, index): unsigned comparison of keys
+// is `better` on pairs. High word: the float's bits mapped to an unsigned
+// order (negatives flipped, positives offset), every NaN above +inf, -0 as
+// +0. Low word: the index inverted, so the lower index is the larger key.
+// Key 0 is below every pair (an untouched row).
+__device__ __forceinline__ u64 argmax_key(float v, int i) {
+  u32 hi;
+  if (v != v) {
+    hi = 0xFFFFFFFFu;
+  } else {
+    const u32 bits = __float_as_uint(v == 0.f ? 0.f : v);
+    hi = (bits & 0x80000000u) ? ~bits : (bits | 0x80000000u);
   }
-  return x;
+  return ((u64)hi << 32) | (u64)(0xFFFFFFFFu - (u32)i);
 }
 
-// One kernel for the whole accept step. Workgroup (c, r) scans chunk c of
-// logits row r with every load of a thread issued before any is consumed,
-// reduces to a (value, index) pair and publishes it with a write-through
-// store; the last workgroup of a sequence (a per-sequence counter) merges its
-// rows' pairs in chunk order and applies the accept rule.
+__device__ __forceinline__ int key_index(u64 k) { return (int)(0xFFFFFFFFu - (u32)(k & 0xFFFFFFFFull)); }
+
+// Workgroup (c, r): chunk c of logits row r. Every load of a thread is issued
+// before any is consumed; the chunk's best pair goes into the row key.
 template <bool VEC4>
-__global__ __launch_bounds__(kArgThreads) void accept_fused_kernel(
-    // leading scalars: what the first loads need, preloaded into SGPRs at
-    // wave launch instead of read from the argument buffer
-    const float* __restrict__ logits, const int32_t* __restrict__ n_draft, int V, int chunk_len, int B,
-    AcceptParams p) {
+__global__ __launch_bounds__(kArgThreads) void argmax_kernel(
+    // leading scalars, preloaded into SGPRs at wave launch
+    const float* __restrict__ logits, int V, int chunk_len, u64* __restrict__ keys) {
   const int c = blockIdx.x;
   const int r = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   __shared__ float sv[kArgThreads / 64];
   __shared__ int si[kArgThreads / 64];
-  __shared__ int s_seq[4];   // b, first row, first draft, n_draft
-  __shared__ int s_last;
 
   const int begin = c * chunk_len;
   const int end = min(V, begin + chunk_len);
   const float* row = logits + (size_t)r * V;
   float bv = -__builtin_inff();
   int bi = INT_MAX;
-  float4 x[kArgUnroll];
   if (VEC4) {
+    float4 x[kArgUnroll];
 #pragma unroll
     for (int u = 0; u < kArgUnroll; ++u) {
       const int e = begin + (u * kArgThreads + threadIdx.x) * 4;
       x[u] = e < end ? *reinterpret_cast<const float4*>(row + e) : float4{0.f, 0.f, 0.f, 0.f};
     }
-  }
-  // wave 0 finds the sequence that owns row r while the loads are in flight
-  if (wave == 0) {
-    int rb = 0, db = 0, found_b = -1, fr0 = 0, fd0 = 0, fn = 0;
-    for (int i0 = 0; i0 < B && found_b < 0; i0 += 64) {
-      const int i = i0 + lane;
-      const int n = i < B ? n_draft[i] : 0;
-      const int inc_r = wave_scan(i < B ? n + 1 : 0);
-      const int inc_d = wave_scan(i < B ? n : 0);
-      const int my_r0 = rb + inc_r - (n + 1), my_d0 = db + inc_d - n;
-      const bool mine = i < B && r >= my_r0 && r < my_r0 + n + 1;
-      const unsigned long long ballot = __ballot(mine);
-      if (ballot) {
-        const int src = __ffsll((long long)ballot) - 1;
-        found_b = __shfl(i, src);
-        fr0 = __shfl(my_r0, src);
-        fd0 = __shfl(my_d0, src);
-        fn = __shfl(n, src);
-      }
-      rb += __shfl(inc_r, 63);
-      db += __shfl(inc_d, 63);
-    }
-    if (lane == 0) {
-      s_seq[0] = found_b;
-      s_seq[1] = fr0;
-      s_seq[2] = fd0;
-      s_seq[3] = fn;
-    }
-  }
-  if (VEC4) {
     // each thread visits its elements in increasing index order
 #pragma unroll
     for (int u = 0; u < kArgUnroll; ++u) {
@@ -166,109 +137,113 @@ __global__ __launch_bounds__(kArgThreads) void accept_fused_kernel(
     si[wave] = bi;
   }
   __syncthreads();
-  const int b = s_seq[0], r0 = s_seq[1], d0 = s_seq[2], n = s_seq[3];
-  // a row no sequence owns, or a sequence breaking its contract: nothing to do
-  const bool ok = b >= 0 && n >= 0 && n <= p.max_draft && r0 + n + 1 <= p.total_rows &&
-                  d0 + n <= p.total_rows - B;
-  const auto val_rsrc = __builtin_amdgcn_make_buffer_rsrc(p.chunk_val, 0, (u32)(p.total_rows * p.chunks * 4),
-                                                          0x00020000);
-  const auto idx_rsrc = __builtin_amdgcn_make_buffer_rsrc(p.chunk_idx, 0, (u32)(p.total_rows * p.chunks * 4),
-                                                          0x00020000);
-  if (wave == 0) {
-    float v = lane < kArgThreads / 64 ? sv[lane] : -__builtin_inff();
-    int i = lane < kArgThreads / 64 ? si[lane] : INT_MAX;
-    wave_best(v, i);
-    if (lane == 0) {
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), val_rsrc, (r * p.chunks + c) * 4, 0, kSc1);
-      __builtin_amdgcn_raw_buffer_store_b32((u32)i, idx_rsrc, (r * p.chunks + c) * 4, 0, kSc1);
-      __builtin_amdgcn_s_waitcnt(0);  // the pair is device-visible before the count
-      int last = 0;
-      if (ok) {
-        const u32 prev = __hip_atomic_fetch_add(p.counters + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        last = prev == (u32)((n + 1) * p.chunks - 1);
-      } else if (b >= 0 && c == 0 && r == r0) {
+  if (wave != 0) return;
+  float v = lane < kArgThreads / 64 ? sv[lane] : -__builtin_inff();
+  int i = lane < kArgThreads / 64 ? si[lane] : INT_MAX;
+  wave_best(v, i);
+  if (lane == 0 && i != INT_MAX)
+    __hip_atomic_fetch_max(keys + r, argmax_key(v, i), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_scan(int x) {
+  const int lane = threadIdx.x & 63;
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __builtin_amdgcn_ds_bpermute(((lane - d) & 63) << 2, x);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+
+// One workgroup: thread b (in tiles of kRuleThreads sequences) finds its
+// sequence's first logits row by a block-wide prefix sum of n_draft + 1,
+// reads its rows' keys and drafts (all requested together), applies the
+// accept rule and the window update. Then every row key is cleared.
+__global__ __launch_bounds__(kRuleThreads) void accept_rule_kernel(AcceptParams p) {
+  constexpr int kWaves = kRuleThreads / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ int s_wsum[kWaves];
+  __shared__ int s_carry;
+  __shared__ u64 s_keys[kRuleThreads];
+  __shared__ int s_draft[kRuleThreads];
+  // Up to kRuleThreads rows, every key and draft is fetched up front, in the
+  // same memory round trip as n_draft, and read from LDS below.
+  const bool staged = p.total_rows <= kRuleThreads;
+  if (staged) {
+    if ((int)threadIdx.x < p.total_rows) s_keys[threadIdx.x] = p.keys[threadIdx.x];
+    if ((int)threadIdx.x < p.total_rows - p.B) s_draft[threadIdx.x] = p.draft_ids[threadIdx.x];
+  }
+  if (threadIdx.x == 0) s_carry = 0;
+  __syncthreads();
+  for (int t0 = 0; t0 < p.B; t0 += kRuleThreads) {
+    const int b = t0 + threadIdx.x;
+    const int n = b < p.B ? p.n_draft[b] : 0;
+    const int w_old = (b < p.B && p.window) ? p.window[b] : 0;
+    const int inc = wave_scan(b < p.B ? n + 1 : 0);
+    if (lane == 63) s_wsum[wave] = inc;
+    __syncthreads();
+    int before = s_carry;
+    for (int w = 0; w < wave; ++w) before += s_wsum[w];
+    const int r0 = before + inc - (n + 1);  // first row of sequence b
+    const int d0 = r0 - b;                  // first draft: the sum of n_draft before b
+    if (b < p.B) {
+      const bool ok = n >= 0 && n <= p.max_draft && r0 >= 0 && r0 + n + 1 <= p.total_rows && d0 >= 0 &&
+                      d0 + n <= p.total_rows - p.B;
+      if (!ok) {
         p.out_accept[b] = 0;
         p.out_next[b] = -1;
-      }
-      s_last = last;
-    }
-  }
-  __syncthreads();
-  if (!s_last || wave != 0) return;
-
-  // ---- last workgroup of sequence b: per-row argmax over chunks, then accept.
-  // Everything it reads is requested up front, in one batch.
-  const int w_old = p.window ? p.window[b] : 0;
-  int draft[PKV_MAX_Q_LEN - 1];
+      } else {
+        // clamped, unconditional loads: all in flight together
+        u64 key[PKV_MAX_Q_LEN];
+        int draft[PKV_MAX_Q_LEN - 1];
 #pragma unroll
-  for (int i = 0; i < PKV_MAX_Q_LEN - 1; ++i) draft[i] = -1;
-  if (n > 0) {
-    // clamped, unconditional loads: all in flight together
+        for (int i = 0; i < PKV_MAX_Q_LEN; ++i) key[i] = staged ? s_keys[r0 + min(i, n)] : p.keys[r0 + min(i, n)];
 #pragma unroll
-    for (int i = 0; i < PKV_MAX_Q_LEN - 1; ++i) draft[i] = p.draft_ids[d0 + min(i, n - 1)];
-  }
-  // lane c holds chunk c of every row of the sequence (64 chunks per pass)
-  float rv[PKV_MAX_Q_LEN];
-  int ri[PKV_MAX_Q_LEN];
+        for (int i = 0; i < PKV_MAX_Q_LEN - 1; ++i)
+          draft[i] = n <= 0 ? -1 : staged ? s_draft[d0 + min(i, n - 1)] : p.draft_ids[d0 + min(i, n - 1)];
+        // drafts compared from the left; the first mismatch keeps the base token
+        int m = n;
 #pragma unroll
-  for (int i = 0; i < PKV_MAX_Q_LEN; ++i) {
-    rv[i] = -__builtin_inff();
-    ri[i] = INT_MAX;
-  }
-  for (int c0 = 0; c0 < p.chunks; c0 += 64) {
-    const int cc = c0 + lane;
-    float cv[PKV_MAX_Q_LEN];
-    int ci[PKV_MAX_Q_LEN];
+        for (int i = PKV_MAX_Q_LEN - 2; i >= 0; --i)
+          if (i < n && key_index(key[i]) != draft[i]) m = i;
+        int next = 0;
 #pragma unroll
-    for (int i = 0; i < PKV_MAX_Q_LEN; ++i) {
-      // rows past the sequence and chunks past the row read out of range: zeros, skipped below
-      const int off = (i <= n && cc < p.chunks ? (r0 + i) * p.chunks + cc : p.total_rows * p.chunks) * 4;
-      cv[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(val_rsrc, off, 0, kSc1));
-      ci[i] = (int)__builtin_amdgcn_raw_buffer_load_b32(idx_rsrc, off, 0, kSc1);
-    }
-#pragma unroll
-    for (int i = 0; i < PKV_MAX_Q_LEN; ++i) {
-      const bool take = (i <= n) & (cc < p.chunks) & better(cv[i], ci[i], rv[i], ri[i]);
-      rv[i] = take ? cv[i] : rv[i];
-      ri[i] = take ? ci[i] : ri[i];
-    }
-  }
-  int m = n, next = 0;
-  bool found = false;
-#pragma unroll
-  for (int i = 0; i < PKV_MAX_Q_LEN; ++i) {
-    if (i <= n) {
-      wave_best(rv[i], ri[i]);
-      // drafts compared from the left; the first mismatch keeps the base token
-      if (!found && (i == n || ri[i] != draft[i < PKV_MAX_Q_LEN - 1 ? i : 0])) {
-        m = i;
-        next = ri[i];
-        found = true;
+        for (int i = 0; i < PKV_MAX_Q_LEN; ++i)
+          if (i == m) next = key_index(key[i]);
+        p.out_accept[b] = m + 1;
+        p.out_next[b] = next;
+        if (p.window) p.window[b] = (m == n) ? w_old + 2 : max(1, w_old - 1);
       }
     }
+    __syncthreads();
+    if (threadIdx.x == kRuleThreads - 1) s_carry = before + inc;
+    __syncthreads();
   }
-  if (lane == 0) {
-    p.out_accept[b] = m + 1;
-    p.out_next[b] = next;
-    if (p.window) p.window[b] = (m == n) ? w_old + 2 : max(1, w_old - 1);
-    __hip_atomic_store(p.counters + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+  // every key has been read (its value was used before the barrier): clear
+  // all rows, owned or not, for the next call
+  for (int r = threadIdx.x; r < p.total_rows; r += kRuleThreads) p.keys[r] = 0ull;
 }
 
 }  // namespace
 
 AcceptWorkspace accept_workspace(int B, int total_rows, int V) {
+  (void)B;
   AcceptWorkspace ws;
-  // each workgroup scans what one round of its threads' loads covers
-  const int len = kArgThreads * kArgUnroll * 4;
-  const int chunks = (V + len - 1) / len;
-  ws.chunks = chunks;
-  ws.chunk_len = len;
-  const size_t n = (size_t)total_rows * chunks;
-  ws.counters_off = 0;
-  ws.val_off = ((size_t)B * 4 + 255) / 256 * 256;
-  ws.idx_off = ws.val_off + (n * 4 + 255) / 256 * 256;
-  ws.total = ws.idx_off + (n * 4 + 255) / 256 * 256;
+  // about three workgroups per CU; a chunk is at most one round of every
+  // thread's loads and at least one float4 per thread
+  const long rows = total_rows > 0 ? total_rows : 1;
+  long chunks = (kArgTargetWgs + rows - 1) / rows;
+  const long most = ((long)V + (long)kArgThreads * 4 - 1) / ((long)kArgThreads * 4);
+  const long least = ((long)V + (long)kArgThreads * kArgUnroll * 4 - 1) / ((long)kArgThreads * kArgUnroll * 4);
+  if (chunks > most) chunks = most;
+  if (chunks < least) chunks = least;
+  if (chunks < 1) chunks = 1;
+  long len = (V + chunks - 1) / chunks;
+  len = (len + 3) / 4 * 4;
+  ws.chunk_len = (int)len;
+  ws.chunks = (int)((V + len - 1) / len);
+  ws.keys_off = 0;
+  ws.total = ((size_t)total_rows * 8 + 255) / 256 * 256;
   if (ws.total == 0) ws.total = 256;
   return ws;
 }
@@ -276,12 +251,16 @@ AcceptWorkspace accept_workspace(int B, int total_rows, int V) {
 hipError_t launch_accept(const AcceptParams& p, hipStream_t stream) {
   if (p.B == 0 || p.total_rows == 0) return hipSuccess;
   dim3 grid(p.chunks, p.total_rows);
-  if (p.V % 4 == 0 && p.chunk_len <= kArgThreads * kArgUnroll * 4)
-    hipLaunchKernelGGL(accept_fused_kernel<true>, grid, dim3(kArgThreads), 0, stream, p.logits, p.n_draft, p.V,
-                       p.chunk_len, p.B, p);
+  const bool vec4 = p.V % 4 == 0 && (reinterpret_cast<uintptr_t>(p.logits) & 15) == 0 &&
+                    p.chunk_len <= kArgThreads * kArgUnroll * 4;
+  if (vec4)
+    hipLaunchKernelGGL(argmax_kernel<true>, grid, dim3(kArgThreads), 0, stream, p.logits, p.V, p.chunk_len, p.keys);
   else
-    hipLaunchKernelGGL(accept_fused_kernel<false>, grid, dim3(kArgThreads), 0, stream, p.logits, p.n_draft, p.V,
-                       p.chunk_len, p.B, p);
+    hipLaunchKernelGGL(argmax_kernel<false>, grid, dim3(kArgThreads), 0, stream, p.logits, p.V, p.chunk_len,
+                       p.keys);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(accept_rule_kernel, dim3(1), dim3(kRuleThreads), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -36,8 +36,6 @@ bool accept_shape_ok(const pkv_accept_shape* s) {
   if (s->total_rows < s->num_seqs) return false;
   if ((long)s->total_rows * s->vocab > (1L << 40)) return false;
   if (s->total_rows > 65535) return false;  // one grid row per logits row
-  const pkv::AcceptWorkspace ws = pkv::accept_workspace(s->num_seqs, s->total_rows, s->vocab);
-  if ((long)s->total_rows * ws.chunks * 4 >= (1L << 31)) return false;  // chunk-pair offsets
   return true;
 }
 
@@ -139,9 +137,7 @@ int pkv_accept(const float* logits, const int32_t* draft_ids, const int32_t* n_d
   p.out_accept = out_accept;
   p.out_next = out_next;
   p.window = window;
-  p.chunk_val = reinterpret_cast<float*>(w + ws.val_off);
-  p.chunk_idx = reinterpret_cast<int32_t*>(w + ws.idx_off);
-  p.counters = reinterpret_cast<uint32_t*>(w + ws.counters_off);
+  p.keys = reinterpret_cast<unsigned long long*>(w + ws.keys_off);
   p.B = s->num_seqs;
   p.V = s->vocab;
   p.total_rows = s->total_rows;

@@ -52,15 +52,13 @@ struct AcceptParams {
   const int32_t* n_draft;
   int32_t* out_accept;
   int32_t* out_next;
-  int32_t* window;       // nullable
-  float* chunk_val;      // [total_rows][chunks]
-  int32_t* chunk_idx;    // [total_rows][chunks]
-  uint32_t* counters;    // [B] chunks finished per sequence
+  int32_t* window;              // nullable
+  unsigned long long* keys;     // [total_rows] argmax key per row; zero between calls
   int32_t B, V, total_rows, max_draft, chunks, chunk_len;
 };
 
 struct AcceptWorkspace {
-  size_t counters_off, val_off, idx_off, total;
+  size_t keys_off, total;
   int chunks, chunk_len;
 };
 

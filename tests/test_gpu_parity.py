@@ -146,6 +146,48 @@ def test_accept_random_rows_ties_and_nan(pk):
     np.testing.assert_array_equal(n, en)
 
 
+def test_accept_signed_zeros_and_nan_signs(pk):
+    say("accept: -0 equals +0, NaN of either sign ranks first")
+    acc = make_accept_case(11, [1, 1, 1, 1], 4096)
+    lg = acc.logits
+    lg[0, :] = -1.0
+    lg[0, [70, 3000]] = [-0.0, 0.0]          # equal maxima: the lower index
+    lg[1, :] = -1.0
+    lg[1, [70, 3000]] = [0.0, -0.0]
+    neg_nan = np.array([0xFFC00000], dtype=np.uint32).view(np.float32)[0]
+    lg[2, 2000] = neg_nan                    # a NaN with the sign bit set still wins
+    lg[3, [100, 200]] = [neg_nan, np.nan]    # the first NaN wins, whatever its sign
+    a, n, _ = accept_gpu(acc, pk, window=False)
+    ea, en, _ = oracle.accept(lg, acc.draft_ids, acc.n_draft)
+    np.testing.assert_array_equal(n, en)
+    np.testing.assert_array_equal(n, [70, 70, 2000, 100])
+    np.testing.assert_array_equal(a, ea)
+
+
+def test_accept_workspace_is_clean_after_each_call(pk):
+    say("accept: one workspace over calls with different logits and shapes")
+    import torch
+    big = make_accept_case(12, [6, 6, 6], 5000)
+    big.logits[:, 4000] = 50.0               # the first call's maxima are large
+    small = make_accept_case(13, [3, 2], 5000)
+    ws = None
+    for acc in (big, small, big):
+        logits = torch.from_numpy(np.ascontiguousarray(acc.logits)).cuda()
+        drafts = torch.from_numpy(acc.draft_ids.astype(np.int32)).cuda()
+        nd = torch.from_numpy(acc.n_draft.astype(np.int32)).cuda()
+        oa = torch.full((acc.num_seqs,), -7, dtype=torch.int32, device="cuda")
+        on = torch.full_like(oa, -7)
+        shape = pk.accept_shape(logits, nd, acc.max_draft)
+        if ws is None:
+            ws = pk.new_accept_workspace(shape)
+        assert ws.numel() >= pk.pkv_accept_workspace_bytes(shape)
+        pk.pkv_accept(logits, drafts, nd, oa, on, None, shape, ws)
+        torch.cuda.synchronize()
+        ea, en, _ = oracle.accept(acc.logits, acc.draft_ids, acc.n_draft)
+        np.testing.assert_array_equal(oa.cpu().numpy(), ea)
+        np.testing.assert_array_equal(on.cpu().numpy(), en)
+
+
 def test_accept_large_vocab_many_sequences(pk):
     say("accept: 200 sequences over 128256 logits")
     rng = np.random.default_rng(5)
