@@ -46,6 +46,9 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef u32 u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 #ifndef PKV_VALU_NBUF
 #define PKV_VALU_NBUF 2  // LDS ring depth (chunks) per wave, VALU row tile
@@ -391,10 +394,17 @@ struct MfmaTile {
   }
 
   // Copy one chunk's MFMA operands out of its LDS slot: the K rows as the
-  // A operand of S^T, and V^T gathered 16 bits at a time as the A operand of
-  // O^T (k index j of lane half h at k-step ks is token 16*ks + 8*(j/4) +
-  // 4*h + j%4, matching where P sits in the S^T result).
-  __device__ __forceinline__ void fetch(const char* kt, const char* vt, int nv) {
+  // A operand of S^T, and V^T as the A operand of O^T, where k index j of
+  // lane half h at k-step ks is token 16*ks + 8*(j/4) + 4*h + j%4 (matching
+  // where P sits in the S^T result).
+  //
+  // V^T comes from transposing LDS reads (ds_read_b64_tr_b16). Within each
+  // 16-lane group, source lane j names 4 consecutive bf16 of one tile row and
+  // destination lane i receives element i%4 of source lanes i/4, i/4 + 4,
+  // i/4 + 8 and i/4 + 12. With source lane j at token t0 + j/4 and dims
+  // d0 + 4*(j%4) .. + 3, lane i gets tokens t0 .. t0 + 3 of dim d0 + i. Rows
+  // past the sequence end were zero-filled by the chunk load, so no mask.
+  __device__ __forceinline__ void fetch(const char* kt, const char* vt, int) {
     const int lane = threadIdx.x & 63;
     const int row = lane & 31, half = lane >> 5;
     const u32x4* kl = reinterpret_cast<const u32x4*>(kt);
@@ -403,27 +413,21 @@ struct MfmaTile {
       const int c = 2 * kk + half;
       ka[kk] = kl[row * NC + (c ^ (row & (NC - 1)))];
     }
-    const uint16_t* vl = reinterpret_cast<const uint16_t*>(vt);
+    const int tq = (lane & 15) >> 2;                         // token within the 4-token group
+    const int dsub = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // dims within the 32-dim block
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-      const int d = mb * 32 + row;
-      const int dch = d >> 3, dw = d & 7;
+      const int d = mb * 32 + dsub;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        u32 w4[4];
+        u32x2 w[2];
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          u32 lohi[2];
-#pragma unroll
-          for (int z = 0; z < 2; ++z) {
-            const int j = 2 * jj + z;
-            const int tt = 16 * ks + 8 * (j >> 2) + 4 * half + (j & 3);
-            const u32 v = vl[(tt * NC + (dch ^ (tt & (NC - 1)))) * 8 + dw];
-            lohi[z] = (tt < nv) ? v : 0u;
-          }
-          w4[jj] = lohi[0] | (lohi[1] << 16);
+        for (int hh = 0; hh < 2; ++hh) {
+          const int t = 16 * ks + 8 * hh + 4 * half + tq;
+          const char* src = vt + (t * NC + ((d >> 3) ^ (t & (NC - 1)))) * 16 + (d & 7) * 2;
+          w[hh] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)src));
         }
-        va[mb][ks] = u32x4{w4[0], w4[1], w4[2], w4[3]};
+        va[mb][ks] = u32x4{w[0].x, w[0].y, w[1].x, w[1].y};
       }
     }
   }
