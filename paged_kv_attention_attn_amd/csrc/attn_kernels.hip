@@ -295,25 +295,32 @@ struct ValuTile {
         for (int e = 0; e < 8; ++e) acc[g4 + 4 * j][e] *= a;
       }
     }
-    // P.V
+    // P.V on bf16 pairs: tokens tA = 2*sp*TG + tg and tB = tA + TG are
+    // interleaved per dim, P is rounded to bf16 (as on the MFMA path), and
+    // one v_dot2 per (row, dim) takes both tokens.
     const int tg = lane / NC;
     const f32x4* pl = reinterpret_cast<const f32x4*>(pb);
+    static_assert(STEPS % 2 == 0, "token pairs");
 #pragma unroll
-    for (int st = 0; st < STEPS; ++st) {
-      const int tt = st * TG + tg;
-      const u32x4 w = vv[st];
-      float v8[8] = {bf16lo(w.x), bf16hi(w.x), bf16lo(w.y), bf16hi(w.y),
-                     bf16lo(w.z), bf16hi(w.z), bf16lo(w.w), bf16hi(w.w)};
+    for (int sp = 0; sp < STEPS / 2; ++sp) {
+      const int tA = 2 * sp * TG + tg, tB = tA + TG;
+      const u32x4 wa = vv[2 * sp], wb = vv[2 * sp + 1];
+      const u32 va4[4] = {wa.x, wa.y, wa.z, wa.w}, vb4[4] = {wb.x, wb.y, wb.z, wb.w};
+      u32 vp[8];  // (V[tA][d], V[tB][d]) for the lane's 8 dims
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        vp[2 * k] = (va4[k] & 0xFFFFu) | (vb4[k] << 16);
+        vp[2 * k + 1] = (va4[k] >> 16) | (vb4[k] & 0xFFFF0000u);
+      }
 #pragma unroll
       for (int r4 = 0; r4 < RP / 4; ++r4) {
-        const f32x4 pp = pl[tt * (RP / 4) + r4];
+        const f32x4 pa = pl[tA * (RP / 4) + r4], pc = pl[tB * (RP / 4) + r4];
+        const u32 pp[4] = {pack_bf16(pa.x, pc.x), pack_bf16(pa.y, pc.y), pack_bf16(pa.z, pc.z),
+                           pack_bf16(pa.w, pc.w)};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          acc[4 * r4 + 0][e] = __builtin_fmaf(pp.x, v8[e], acc[4 * r4 + 0][e]);
-          acc[4 * r4 + 1][e] = __builtin_fmaf(pp.y, v8[e], acc[4 * r4 + 1][e]);
-          acc[4 * r4 + 2][e] = __builtin_fmaf(pp.z, v8[e], acc[4 * r4 + 2][e]);
-          acc[4 * r4 + 3][e] = __builtin_fmaf(pp.w, v8[e], acc[4 * r4 + 3][e]);
-        }
+        for (int e = 0; e < 8; ++e)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) acc[4 * r4 + rr][e] = dot2(pp[rr], vp[e], acc[4 * r4 + rr][e]);
       }
     }
   }
