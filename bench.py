@@ -162,6 +162,23 @@ def time_ms(torch, fn, steps, warmup):
     return e0.elapsed_time(e1) / steps
 
 
+def launch_percentiles(torch, fn, steps, warmup):
+    """Median, p10 and p90 microseconds of single calls of fn(i), each
+    bracketed by its own pair of HIP events on the current stream."""
+    for i in range(warmup):
+        fn(i)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(evs):
+        a.record()
+        fn(warmup + i)
+        b.record()
+    torch.cuda.synchronize()
+    us = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+    return {"median": round(float(np.median(us)), 3), "p10": round(float(np.percentile(us, 10)), 3),
+            "p90": round(float(np.percentile(us, 90)), 3)}
+
+
 def cpu_baseline(case, acc, seconds):
     """The CPU oracle on the verify step: whole sequences (attention over
     their cached tokens + accept over their logits rows) in order, passes
@@ -263,6 +280,9 @@ def main():
     accept.win.copy_(accept.win0)
     torch.cuda.synchronize()
     step_ms = time_ms(torch, step, args.steps, args.warmup)
+    attn_pct = launch_percentiles(torch, attn, args.steps, args.warmup)
+    accept.win.copy_(accept.win0)
+    accept_pct = launch_percentiles(torch, accept, args.steps, args.warmup)
     # one checked step: the window update is applied per call, so reset and run once
     accept.win.copy_(accept.win0)
     step(0)
@@ -297,6 +317,8 @@ def main():
         "attn_hbm_fraction": round(attn_gbps / HBM_PEAK_GBPS, 4),
         "attn_us": round(attn_ms * 1e3, 3),
         "accept_us": round(accept_ms * 1e3, 3),
+        "attn_us_per_launch": attn_pct,
+        "accept_us_per_call": accept_pct,
         "verified_tokens_per_s": round(accepted / (step_ms * 1e-3), 1),
         "accepted_per_step": accepted,
         "kv_bytes_per_step": kv_bytes,

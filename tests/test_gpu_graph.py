@@ -1,0 +1,78 @@
+"""Both entry points under HIP graph capture: a verify step (attention over a
+split-K shape whose splits merge through the workspace counters, then the
+accept over its logits) is captured once and replayed several times, with
+eager work and synchronisations in between. Every replay must reproduce the
+eager result bit for bit, which also shows that each call leaves its
+workspace clean for the next (counters back at zero, row keys cleared)."""
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+import oracle
+from workloads import make_tiny_case, make_accept_case
+from tests.gpu_util import say, DeviceCase, dev_i32, assert_close
+
+
+@pytest.fixture(scope="module")
+def pk():
+    import torch
+    assert torch.cuda.is_available()
+    import paged_kv_attention_attn_amd as pk
+    return pk
+
+
+def test_verify_step_replays_bit_exact(pk):
+    import torch
+    say("graph: attention (split merge) + accept, 4 replays")
+    # long enough that every (sequence, KV head) is cut into several splits
+    case = make_tiny_case(21, [4000, 2600, 900], [6, 4, 2], Hq=8, Hkv=2, D=128, num_pages=64)
+    dc = DeviceCase(case, pk)
+    acc = make_accept_case(22, [6, 4, 2], 32000)
+    logits = torch.from_numpy(np.ascontiguousarray(acc.logits)).cuda()
+    drafts, nd = dev_i32(acc.draft_ids), dev_i32(acc.n_draft)
+    B = acc.num_seqs
+    oa = torch.zeros(B, dtype=torch.int32, device="cuda")
+    on = torch.zeros_like(oa)
+    ashape = pk.accept_shape(logits, nd, acc.max_draft)
+    aws = pk.new_accept_workspace(ashape)
+
+    def step(stream=None):
+        dc.run(stream)
+        pk.pkv_accept(logits, drafts, nd, oa, on, None, ashape, aws, stream)
+
+    # eager reference (and a check against the oracle)
+    step()
+    torch.cuda.synchronize()
+    ref_out, ref_a, ref_n = dc.out.clone(), oa.clone(), on.clone()
+    assert_close(ref_out.cpu().numpy(), oracle.attention(case.q, case.k_pool, case.v_pool, case.block_table,
+                                                         case.seq_lens, case.q_lens, case.scale),
+                 "graph eager")
+    ea, en, _ = oracle.accept(acc.logits, acc.draft_ids, acc.n_draft)
+    np.testing.assert_array_equal(ref_a.cpu().numpy(), ea)
+    np.testing.assert_array_equal(ref_n.cpu().numpy(), en)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step(s)  # warm the capture stream once, outside the graph
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        dc.out.fill_(float("nan"))
+        oa.fill_(-7)
+        on.fill_(-7)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(dc.out, ref_out), f"replay {rep}: attention differs"
+        assert torch.equal(oa, ref_a) and torch.equal(on, ref_n), f"replay {rep}: accept differs"
+        step()  # eager work between replays, on the same workspaces
+        torch.cuda.synchronize()
+        assert torch.equal(dc.out, ref_out), f"eager after replay {rep}: attention differs"
+    assert dc.errors() == 0
