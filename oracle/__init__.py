@@ -14,6 +14,9 @@ What it computes is the plain definition, in float64:
 * ``greedy_accept.argmax_rows`` / ``.accept`` / ``.window_next`` -- the
   vocab-wide argmax, the left-to-right draft comparison with one correction
   token, and the +2 / -1 draft-window rule.
+* ``kv_cache.append`` / ``.rollback`` -- writing a verify window's K/V into
+  the pages (popping new pages from a free stack) and, after the accept,
+  keeping the accepted prefix and releasing the pages past it.
 * ``brute`` -- an independent pure-Python loop version of the attention, per
   token and per element, used to pin ``paged_attention`` on tiny inputs.
 
@@ -26,6 +29,7 @@ checks.
 
 from .paged_attention import decode_bf16, gather_sequence, attention, attention_rows
 from .greedy_accept import argmax_rows, accept, window_next
+from . import kv_cache
 
 __all__ = ["decode_bf16", "gather_sequence", "attention", "attention_rows",
-           "argmax_rows", "accept", "window_next"]
+           "argmax_rows", "accept", "window_next", "kv_cache"]

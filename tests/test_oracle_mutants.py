@@ -151,3 +151,53 @@ ORIG_ARGMAX = oa.argmax_rows
 def test_accept_mutant_is_caught(monkeypatch, attr, fn):
     monkeypatch.setattr(oa, attr, fn)
     assert not _accept_pins_pass()
+
+
+# ---- K/V append and rollback: each mutant is the oracle's own source with one
+# planted defect, swapped in for the pin battery of tests/test_oracle_kv.py.
+
+import inspect
+import oracle.kv_cache as kvc
+import tests.test_oracle_kv as kvpins
+
+KV_MUTANTS = {
+    "slot one late": ("append", "page, slot = int(table[b, pos // PAGE]), pos % PAGE",
+                      "page, slot = int(table[b, pos // PAGE]), (pos + 1) % PAGE"),
+    "no page for a window ending on a boundary": ("append", "for j in range(_pages(L), _pages(L + n)):",
+                                                  "for j in range(_pages(L), _pages(L + n - 1)):"),
+    "rows of the first sequence for every sequence": ("append", "k_pool[page, :, slot, :] = k_new[row + i]",
+                                                      "k_pool[page, :, slot, :] = k_new[i]"),
+    "rollback keeps one token too many": ("rollback", "new_len = S - n + a", "new_len = min(S, S - n + a + 1)"),
+    "rollback releases one page too many": ("rollback",
+                                            "for j in range(_pages(new_len), _pages(S)):",
+                                            "for j in range(max(0, _pages(new_len) - 1), _pages(S)):"),
+}
+
+
+def _kv_mutant(fn_name, old, new):
+    src = inspect.getsource(getattr(kvc, fn_name))
+    assert old in src, old
+    ns = dict(vars(kvc))
+    exec(compile(src.replace(old, new), f"<mutant {fn_name}>", "exec"), ns)
+    return ns[fn_name]
+
+
+def _kv_battery():
+    kvpins.test_worked_example()
+    for seed in range(6):
+        kvpins.test_append_extends_every_sequence_by_its_window(seed)
+        kvpins.test_rollback_keeps_the_accepted_prefix(seed)
+    for seed in range(4):
+        kvpins.test_full_accept_changes_nothing_and_empty_accept_undoes_the_append(seed)
+
+
+@pytest.mark.parametrize("name", list(KV_MUTANTS))
+def test_kv_mutant_is_caught(name, monkeypatch):
+    fn_name, old, new = KV_MUTANTS[name]
+    monkeypatch.setattr(kvc, fn_name, _kv_mutant(fn_name, old, new))
+    with pytest.raises(Exception):
+        _kv_battery()
+
+
+def test_kv_battery_passes_on_the_oracle():
+    _kv_battery()
