@@ -54,7 +54,9 @@ typedef enum {
 /* Error-word bits a kernel sets when a device array breaks its contract. */
 #define PKV_EFLAG_PAGE 1u  /* a block-table entry the sequence needs is not in [0, num_pages) */
 #define PKV_EFLAG_QLEN 2u  /* q_len > max_q_len, q_len > seq_len, or seq_len > max_pages_per_seq*256 */
-#define PKV_EFLAG_ROWS 4u  /* sum(q_lens) exceeds total_q                                           */
+#define PKV_EFLAG_ROWS 4u  /* sum(q_lens) exceeds total_q (append: differs from total_q)           */
+#define PKV_EFLAG_SPACE 8u /* append: too few free pages, or a page on the free stack is not in
+                              [0, num_pages); rollback: the free stack would pass num_pages        */
 
 /* ------------------------------------------------------------------ attention */
 
@@ -160,6 +162,79 @@ int pkv_accept(const float* logits, const int32_t* draft_ids, const int32_t* n_d
 /* The draft-window rule on the host: window + 2 when accepted == n_draft + 1
  * (every draft matched, including n_draft == 0), else max(1, window - 1). */
 int32_t pkv_window_next(int32_t window, int32_t n_draft, int32_t accepted);
+
+/* -------------------------------------------------------- cache append / rollback */
+
+/*
+ * Sources: ExLlamaV2 "Dynamic Generator" page, "Continuous Batching" (sequences
+ * grow into 256-token pages reached through block tables; a batch changes by
+ * rewriting block indices; freed pages leave holes that later jobs fill) and
+ * Hugging Face "Assisted Generation" page, "Assisted Generation loop", step 4
+ * (candidates after the first mismatch are discarded).
+ *
+ * One verify step runs: pkv_kv_append (the window's K/V into the pages,
+ * seq_lens grows by q_len) -> pkv_attn_fwd (seq_lens includes the window) ->
+ * pkv_accept -> pkv_kv_rollback (keep the accepted tokens, release pages).
+ *
+ * Free pages are a caller-owned device stack free_pages[0 .. *free_count) of
+ * capacity num_pages. Allocation pops from the top, sequences in index order,
+ * each sequence's new pages in table order; release pushes on top in the same
+ * order. Page placement is therefore deterministic. A page that receives
+ * appended tokens must belong to that sequence alone (shared dedup pages are
+ * full prefix pages).
+ *
+ * Both calls check every contract before changing anything: on a violation
+ * they set PKV_EFLAG_* bits in the workspace error word (read with
+ * pkv_kv_check_errors) and leave every buffer as it was.
+ */
+
+typedef struct {
+  int32_t num_seqs;          /* B >= 0                                              */
+  int32_t num_kv_heads;      /* Hkv >= 1                                            */
+  int32_t head_dim;          /* D, 64 or 128                                        */
+  int32_t page_size;         /* must be PKV_PAGE_SIZE                               */
+  int32_t num_pages;         /* P >= 1: pages in each pool; capacity of free_pages  */
+  int32_t max_pages_per_seq; /* W >= 1: row stride of block_table                   */
+  int32_t total_q;           /* rows of k_new / v_new = sum(q_lens) (append)        */
+} pkv_kv_shape;
+
+/* Bytes of device workspace for pkv_kv_append / pkv_kv_rollback with this
+ * shape (0 on a bad shape): an error word, a flag and one int per window row.
+ * Zero-fill it before its first use. One call at a time per workspace. */
+size_t pkv_kv_workspace_bytes(const pkv_kv_shape* shape);
+
+/*
+ * Append window token i of sequence b (row sum(q_lens[0..b)) + i of k_new /
+ * v_new) at position seq_lens[b] + i: slot pos % 256 of page
+ * block_table[b][pos / 256], popping a free page for every table entry the
+ * window grows into. Then seq_lens[b] += q_lens[b].
+ * k_new, v_new bf16 [total_q, Hkv, D] (read); k_pool, v_pool bf16
+ * [P, Hkv, 256, D] (written at the window's slots only); block_table int32
+ * [B, W] (new entries written); seq_lens int32 [B] (in/out); q_lens int32 [B];
+ * free_pages int32 [P], free_count int32 [1] (in/out).
+ * Contract: 0 <= seq_len, 0 <= q_len, seq_len + q_len <= W * 256; the entry of a
+ * partly filled last page that receives tokens lies in [0, P); sum(q_lens) ==
+ * total_q; enough free pages, each in [0, P).
+ */
+int pkv_kv_append(const void* k_new, const void* v_new, void* k_pool, void* v_pool, int32_t* block_table,
+                  int32_t* seq_lens, const int32_t* q_lens, int32_t* free_pages, int32_t* free_count,
+                  const pkv_kv_shape* shape, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Keep accepted[b] of the q_lens[b] window tokens that end each sequence:
+ * seq_lens[b] becomes seq_lens[b] - q_lens[b] + accepted[b]; every table entry
+ * wholly past the new length is pushed on the free stack and set to -1.
+ * accepted is pkv_accept's out_accept (0 for a sequence it rejected).
+ * Contract: 0 <= accepted <= q_len <= seq_len; ceil(seq_len / 256) <= W; the
+ * stack stays within num_pages.
+ */
+int pkv_kv_rollback(int32_t* block_table, int32_t* seq_lens, const int32_t* q_lens, const int32_t* accepted,
+                    int32_t* free_pages, int32_t* free_count, const pkv_kv_shape* shape, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/* Synchronise `stream`, copy the error word of a cache workspace into *flags
+ * and clear it. */
+int pkv_kv_check_errors(void* workspace, void* stream, uint32_t* flags);
 
 /* ---------------------------------------------------------------------- misc */
 

@@ -1,4 +1,5 @@
-"""pkv: paged K/V attention and greedy speculative accept for AMD MI355X.
+"""pkv: paged K/V attention, greedy speculative accept, and the cache append /
+rollback around them, for AMD MI355X.
 
 The compute lives in libpkv.so (hand-written HIP for gfx950, C ABI in
 include/pkv.h). This package is its thin Python binding; importing it loads
@@ -7,9 +8,11 @@ the library and fails loudly when it has not been built.
 
 from ._lib import (  # noqa: F401
     PKV_PAGE_SIZE, PKV_MAX_Q_LEN, PKV_MAX_ROWS, PKV_OK, PKV_ERR_NULL, PKV_ERR_SHAPE,
-    PKV_ERR_WORKSPACE, PKV_ERR_HIP, PKV_EFLAG_PAGE, PKV_EFLAG_QLEN, PKV_EFLAG_ROWS, EXPORTS, LIB,
+    PKV_ERR_WORKSPACE, PKV_ERR_HIP, PKV_EFLAG_PAGE, PKV_EFLAG_QLEN, PKV_EFLAG_ROWS, PKV_EFLAG_SPACE,
+    EXPORTS, LIB,
     LIB_PATH, PkvError, pkv_attn_shape, pkv_accept_shape, attn_shape, accept_shape,
     pkv_attn_workspace_bytes, pkv_attn_workspace_init, new_attn_workspace, pkv_attn_fwd,
     pkv_attn_check_errors, pkv_accept_workspace_bytes, new_accept_workspace, pkv_accept,
-    pkv_window_next, pkv_status_string, pkv_version,
+    pkv_window_next, pkv_status_string, pkv_version, pkv_kv_shape, kv_shape, pkv_kv_workspace_bytes,
+    new_kv_workspace, pkv_kv_append, pkv_kv_rollback, pkv_kv_check_errors,
 )

@@ -19,11 +19,12 @@ PKV_PAGE_SIZE = 256
 PKV_MAX_Q_LEN = 16
 PKV_MAX_ROWS = 64
 PKV_OK, PKV_ERR_NULL, PKV_ERR_SHAPE, PKV_ERR_WORKSPACE, PKV_ERR_HIP = 0, -1, -2, -3, -4
-PKV_EFLAG_PAGE, PKV_EFLAG_QLEN, PKV_EFLAG_ROWS = 1, 2, 4
+PKV_EFLAG_PAGE, PKV_EFLAG_QLEN, PKV_EFLAG_ROWS, PKV_EFLAG_SPACE = 1, 2, 4, 8
 
 EXPORTS = ("pkv_attn_workspace_bytes", "pkv_attn_workspace_init", "pkv_attn_fwd",
            "pkv_attn_check_errors", "pkv_accept_workspace_bytes", "pkv_accept",
-           "pkv_window_next", "pkv_status_string", "pkv_version")
+           "pkv_window_next", "pkv_status_string", "pkv_version", "pkv_kv_workspace_bytes",
+           "pkv_kv_append", "pkv_kv_rollback", "pkv_kv_check_errors")
 
 
 class pkv_attn_shape(ctypes.Structure):
@@ -37,6 +38,13 @@ class pkv_attn_shape(ctypes.Structure):
 class pkv_accept_shape(ctypes.Structure):
     _fields_ = [("num_seqs", ctypes.c_int32), ("vocab", ctypes.c_int32),
                 ("total_rows", ctypes.c_int32), ("max_draft", ctypes.c_int32)]
+
+
+class pkv_kv_shape(ctypes.Structure):
+    _fields_ = [("num_seqs", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("num_pages", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32),
+                ("total_q", ctypes.c_int32)]
 
 
 class PkvError(RuntimeError):
@@ -68,6 +76,14 @@ def _load():
     lib.pkv_status_string.restype = ctypes.c_char_p
     lib.pkv_version.argtypes = []
     lib.pkv_version.restype = ctypes.c_int
+    lib.pkv_kv_workspace_bytes.argtypes = [ctypes.POINTER(pkv_kv_shape)]
+    lib.pkv_kv_workspace_bytes.restype = sz
+    lib.pkv_kv_append.argtypes = [vp] * 9 + [ctypes.POINTER(pkv_kv_shape), vp, sz, vp]
+    lib.pkv_kv_append.restype = ctypes.c_int
+    lib.pkv_kv_rollback.argtypes = [vp] * 6 + [ctypes.POINTER(pkv_kv_shape), vp, sz, vp]
+    lib.pkv_kv_rollback.restype = ctypes.c_int
+    lib.pkv_kv_check_errors.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_uint32)]
+    lib.pkv_kv_check_errors.restype = ctypes.c_int
     return lib
 
 
@@ -188,3 +204,60 @@ def pkv_status_string(status):
 
 def pkv_version():
     return int(LIB.pkv_version())
+
+
+def kv_shape(k_pool, block_table, total_q):
+    """pkv_kv_shape from tensor extents (pool [P, Hkv, 256, D], block_table [B, W])."""
+    P, Hkv, page, D = k_pool.shape
+    B, W = block_table.shape
+    return pkv_kv_shape(B, Hkv, D, page, P, W, int(total_q))
+
+
+def pkv_kv_workspace_bytes(shape):
+    return int(LIB.pkv_kv_workspace_bytes(ctypes.byref(shape)))
+
+
+def new_kv_workspace(shape, device="cuda"):
+    n = pkv_kv_workspace_bytes(shape)
+    if n == 0:
+        raise PkvError("pkv_kv_workspace_bytes: shape rejected")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def pkv_kv_append(k_new, v_new, k_pool, v_pool, block_table, seq_lens, q_lens, free_pages, free_count,
+                  shape, workspace, stream=None):
+    """k_new, v_new, pools: bf16; block_table, seq_lens, q_lens, free_pages, free_count: int32."""
+    for t, dt, n in ((k_pool, torch.bfloat16, "k_pool"), (v_pool, torch.bfloat16, "v_pool"),
+                     (block_table, torch.int32, "block_table"), (seq_lens, torch.int32, "seq_lens"),
+                     (q_lens, torch.int32, "q_lens"), (free_pages, torch.int32, "free_pages"),
+                     (free_count, torch.int32, "free_count"), (workspace, torch.uint8, "workspace")):
+        _need(t, dt, n)
+    if k_new.numel():
+        _need(k_new, torch.bfloat16, "k_new")
+        _need(v_new, torch.bfloat16, "v_new")
+    kn = k_new if k_new.numel() else None
+    vn = v_new if v_new.numel() else None
+    rc = LIB.pkv_kv_append(_ptr(kn), _ptr(vn), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(seq_lens),
+                           _ptr(q_lens), _ptr(free_pages), _ptr(free_count), ctypes.byref(shape),
+                           _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(rc, "pkv_kv_append")
+
+
+def pkv_kv_rollback(block_table, seq_lens, q_lens, accepted, free_pages, free_count, shape, workspace,
+                    stream=None):
+    """All int32 device tensors; accepted is pkv_accept's out_accept."""
+    for t, n in ((block_table, "block_table"), (seq_lens, "seq_lens"), (q_lens, "q_lens"),
+                 (accepted, "accepted"), (free_pages, "free_pages"), (free_count, "free_count")):
+        _need(t, torch.int32, n)
+    _need(workspace, torch.uint8, "workspace")
+    rc = LIB.pkv_kv_rollback(_ptr(block_table), _ptr(seq_lens), _ptr(q_lens), _ptr(accepted),
+                             _ptr(free_pages), _ptr(free_count), ctypes.byref(shape), _ptr(workspace),
+                             workspace.numel(), _stream(stream))
+    _check(rc, "pkv_kv_rollback")
+
+
+def pkv_kv_check_errors(workspace, stream=None):
+    flags = ctypes.c_uint32(0)
+    _check(LIB.pkv_kv_check_errors(_ptr(workspace), _stream(stream), ctypes.byref(flags)),
+           "pkv_kv_check_errors")
+    return int(flags.value)

@@ -39,6 +39,35 @@ bool accept_shape_ok(const pkv_accept_shape* s) {
   return true;
 }
 
+bool kv_shape_ok(const pkv_kv_shape* s) {
+  if (!s) return false;
+  if (s->num_seqs < 0 || s->num_kv_heads < 1 || s->total_q < 0) return false;
+  if (s->head_dim != 64 && s->head_dim != 128) return false;
+  if (s->page_size != PKV_PAGE_SIZE) return false;
+  if (s->num_pages < 1 || s->max_pages_per_seq < 1) return false;
+  // 32-bit indexing limits inside the kernels
+  if ((long)s->num_pages * PKV_PAGE_SIZE > (1L << 31) - 1) return false;                  // page * 256 + slot
+  if ((long)s->max_pages_per_seq * PKV_PAGE_SIZE > (1L << 31) - 1) return false;          // token positions
+  if ((long)s->total_q * s->num_kv_heads * s->head_dim > (1L << 31) - 1) return false;     // copy pieces
+  return true;
+}
+
+pkv::KvParams kv_params(const pkv_kv_shape* s, void* workspace) {
+  const pkv::KvWorkspace ws = pkv::kv_workspace(s->total_q);
+  char* w = static_cast<char*>(workspace);
+  pkv::KvParams p{};
+  p.err = reinterpret_cast<uint32_t*>(w + ws.err_off);
+  p.go = reinterpret_cast<uint32_t*>(w + ws.go_off);
+  p.row_tok = reinterpret_cast<int32_t*>(w + ws.rows_off);
+  p.B = s->num_seqs;
+  p.Hkv = s->num_kv_heads;
+  p.D = s->head_dim;
+  p.P = s->num_pages;
+  p.W = s->max_pages_per_seq;
+  p.total_q = s->total_q;
+  return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -146,6 +175,57 @@ int pkv_accept(const float* logits, const int32_t* draft_ids, const int32_t* n_d
   p.chunk_len = ws.chunk_len;
   if (pkv::launch_accept(p, static_cast<hipStream_t>(stream)) != hipSuccess) return PKV_ERR_HIP;
   return PKV_OK;
+}
+
+size_t pkv_kv_workspace_bytes(const pkv_kv_shape* s) {
+  if (!kv_shape_ok(s)) return 0;
+  return pkv::kv_workspace(s->total_q).total;
+}
+
+int pkv_kv_append(const void* k_new, const void* v_new, void* k_pool, void* v_pool, int32_t* block_table,
+                  int32_t* seq_lens, const int32_t* q_lens, int32_t* free_pages, int32_t* free_count,
+                  const pkv_kv_shape* s, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!s) return PKV_ERR_NULL;
+  if (!kv_shape_ok(s)) return PKV_ERR_SHAPE;
+  if (s->num_seqs == 0) return PKV_OK;
+  if (!k_pool || !v_pool || !block_table || !seq_lens || !q_lens || !free_pages || !free_count) return PKV_ERR_NULL;
+  if (s->total_q > 0 && (!k_new || !v_new)) return PKV_ERR_NULL;
+  if (!workspace || workspace_bytes < pkv::kv_workspace(s->total_q).total) return PKV_ERR_WORKSPACE;
+  pkv::KvParams p = kv_params(s, workspace);
+  p.k_new = static_cast<const uint16_t*>(k_new);
+  p.v_new = static_cast<const uint16_t*>(v_new);
+  p.k_pool = static_cast<uint16_t*>(k_pool);
+  p.v_pool = static_cast<uint16_t*>(v_pool);
+  p.block_table = block_table;
+  p.seq_lens = seq_lens;
+  p.q_lens = q_lens;
+  p.free_pages = free_pages;
+  p.free_count = free_count;
+  if (pkv::launch_kv_append(p, static_cast<hipStream_t>(stream)) != hipSuccess) return PKV_ERR_HIP;
+  return PKV_OK;
+}
+
+int pkv_kv_rollback(int32_t* block_table, int32_t* seq_lens, const int32_t* q_lens, const int32_t* accepted,
+                    int32_t* free_pages, int32_t* free_count, const pkv_kv_shape* s, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  if (!s) return PKV_ERR_NULL;
+  if (!kv_shape_ok(s)) return PKV_ERR_SHAPE;
+  if (s->num_seqs == 0) return PKV_OK;
+  if (!block_table || !seq_lens || !q_lens || !accepted || !free_pages || !free_count) return PKV_ERR_NULL;
+  if (!workspace || workspace_bytes < pkv::kv_workspace(s->total_q).total) return PKV_ERR_WORKSPACE;
+  pkv::KvParams p = kv_params(s, workspace);
+  p.block_table = block_table;
+  p.seq_lens = seq_lens;
+  p.q_lens = q_lens;
+  p.accepted = accepted;
+  p.free_pages = free_pages;
+  p.free_count = free_count;
+  if (pkv::launch_kv_rollback(p, static_cast<hipStream_t>(stream)) != hipSuccess) return PKV_ERR_HIP;
+  return PKV_OK;
+}
+
+int pkv_kv_check_errors(void* workspace, void* stream, uint32_t* flags) {
+  return pkv_attn_check_errors(workspace, stream, flags);  // same word at offset 0
 }
 
 int32_t pkv_window_next(int32_t window, int32_t n_draft, int32_t accepted) {

@@ -62,6 +62,31 @@ struct AcceptWorkspace {
   int chunks, chunk_len;
 };
 
+struct KvParams {
+  const uint16_t* k_new;     // [total_q, Hkv, D] bf16 bits
+  const uint16_t* v_new;
+  uint16_t* k_pool;          // [P, Hkv, 256, D]
+  uint16_t* v_pool;
+  int32_t* block_table;      // [B, W]
+  int32_t* seq_lens;         // [B]
+  const int32_t* q_lens;     // [B]
+  const int32_t* accepted;   // [B] (rollback only)
+  int32_t* free_pages;       // [P] stack of free page ids
+  int32_t* free_count;       // stack height
+  uint32_t* err;             // workspace error word
+  uint32_t* go;              // append: 1 once the plan passed its checks
+  int32_t* row_tok;          // append: [total_q] destination page * 256 + slot
+  int32_t B, Hkv, D, P, W, total_q;
+};
+
+struct KvWorkspace {
+  size_t err_off, go_off, rows_off, total;
+};
+
+KvWorkspace kv_workspace(int total_q);
+hipError_t launch_kv_append(const KvParams& p, hipStream_t stream);
+hipError_t launch_kv_rollback(const KvParams& p, hipStream_t stream);
+
 AcceptWorkspace accept_workspace(int B, int total_rows, int V);
 hipError_t launch_accept(const AcceptParams& p, hipStream_t stream);
 

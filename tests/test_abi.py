@@ -43,6 +43,7 @@ def test_library_exports_every_declared_symbol(pk):
 def test_struct_layouts_match_the_header(pk):
     assert ctypes.sizeof(pk.pkv_attn_shape) == 40
     assert ctypes.sizeof(pk.pkv_accept_shape) == 16
+    assert ctypes.sizeof(pk.pkv_kv_shape) == 28
 
 
 def test_window_rule_on_the_host(pk):
@@ -123,3 +124,31 @@ def test_status_strings(pk):
     for code in (0, -1, -2, -3, -4):
         assert pk.pkv_status_string(code)
     assert pk.pkv_version() >= 100
+
+
+@pytest.mark.parametrize("bad", [dict(head_dim=96), dict(page_size=128), dict(num_pages=0),
+                                 dict(max_pages_per_seq=0), dict(total_q=-1), dict(num_seqs=-1),
+                                 dict(num_pages=1 << 24)])
+def test_bad_cache_shapes_are_rejected(pk, bad):
+    f = dict(num_seqs=4, num_kv_heads=8, head_dim=128, page_size=256, num_pages=256,
+             max_pages_per_seq=32, total_q=24)
+    f.update(bad)
+    s = pk.pkv_kv_shape(**f)
+    assert pk.pkv_kv_workspace_bytes(s) == 0
+    rc = pk.LIB.pkv_kv_append(*([None] * 9), ctypes.byref(s), None, 0, None)
+    assert rc == pk.PKV_ERR_SHAPE
+    rc = pk.LIB.pkv_kv_rollback(*([None] * 6), ctypes.byref(s), None, 0, None)
+    assert rc == pk.PKV_ERR_SHAPE
+
+
+def test_cache_calls_check_pointers_and_workspace(pk):
+    s = pk.pkv_kv_shape(4, 8, 128, 256, 256, 32, 24)
+    need = pk.pkv_kv_workspace_bytes(s)
+    assert need >= 256 + 24 * 4
+    d = ctypes.c_void_p(0x1000)
+    assert pk.LIB.pkv_kv_append(*([d] * 9), ctypes.byref(s), d, need - 1, None) == pk.PKV_ERR_WORKSPACE
+    assert pk.LIB.pkv_kv_append(*([d] * 8), None, ctypes.byref(s), d, need, None) == pk.PKV_ERR_NULL
+    assert pk.LIB.pkv_kv_rollback(*([d] * 6), ctypes.byref(s), d, need - 1, None) == pk.PKV_ERR_WORKSPACE
+    assert pk.LIB.pkv_kv_rollback(d, d, d, None, d, d, ctypes.byref(s), d, need, None) == pk.PKV_ERR_NULL
+    empty = pk.pkv_kv_shape(0, 8, 128, 256, 256, 32, 0)
+    assert pk.LIB.pkv_kv_append(*([None] * 9), ctypes.byref(empty), None, 0, None) == pk.PKV_OK
