@@ -179,6 +179,50 @@ def launch_percentiles(torch, fn, steps, warmup):
             "p90": round(float(np.percentile(us, 90)), 3)}
 
 
+def cache_leg(torch, pk, case, attn, accept, steps, warmup):
+    """The cache calls around the verify pass on the same workload: append the
+    window's K/V (sequences hold seq_len - q_len tokens before it), and roll
+    back with accepted = 0, which restores the state so every repetition is
+    the same work. Also one whole loop step: append, attention, accept,
+    rollback (to the same restored state)."""
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+    B, rows = case.num_seqs, int(case.q_lens.sum())
+    Hkv, D = case.num_kv_heads, case.head_dim
+    rng = np.random.default_rng(1)
+    k_new = torch.from_numpy(rng.integers(0x3C00, 0x3F80, (rows, Hkv, D), dtype=np.uint16).view(np.int16)) \
+        .view(torch.bfloat16).cuda()
+    v_new = k_new.clone()
+    before = i32(case.seq_lens - case.q_lens)
+    lens = before.clone()
+    free = i32(np.full(case.k_pool.shape[0], -1))
+    count = i32([0])
+    zeros = i32(np.zeros(B))
+    shape = pk.kv_shape(attn.k[0], attn.bt, rows)
+    ws = pk.new_kv_workspace(shape)
+
+    def append_rollback(i):
+        r = i % attn.R
+        pk.pkv_kv_append(k_new, v_new, attn.k[r], attn.v[r], attn.bt, lens, attn.ql, free, count, shape, ws)
+        pk.pkv_kv_rollback(attn.bt, lens, attn.ql, zeros, free, count, shape, ws)
+
+    def loop_step(i):
+        r = i % attn.R
+        pk.pkv_kv_append(k_new, v_new, attn.k[r], attn.v[r], attn.bt, lens, attn.ql, free, count, shape, ws)
+        pk.pkv_attn_fwd(attn.q, attn.k[r], attn.v[r], attn.bt, lens, attn.ql, attn.out, attn.shape, attn.ws)
+        accept(i)
+        pk.pkv_kv_rollback(attn.bt, lens, attn.ql, zeros, free, count, shape, ws)
+
+    pair_ms = time_ms(torch, append_rollback, steps, warmup)
+    loop_ms = time_ms(torch, loop_step, steps, warmup)
+    torch.cuda.synchronize()
+    assert torch.equal(lens, before), "append + rollback(0) must restore the lengths"
+    assert pk.pkv_kv_check_errors(ws) == 0
+    return {"append_rollback_us": round(pair_ms * 1e3, 3), "verify_loop_step_us": round(loop_ms * 1e3, 3),
+            "window_kv_bytes_written": rows * Hkv * D * 2 * 2,
+            "note": "append writes the window's K/V (q_len rows per sequence); rollback with accepted = 0 "
+                    "restores the state; the loop step is append + attention + accept + rollback"}
+
+
 def cpu_baseline(case, acc, seconds):
     """The CPU oracle on the verify step: whole sequences (attention over
     their cached tokens + accept over their logits rows) in order, passes
@@ -326,6 +370,9 @@ def main():
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
                    "cus": props.multi_processor_count, "hbm_gib": round(props.total_memory / 2**30, 1)},
     }
+    log("cache append / rollback")
+    accept.win.copy_(accept.win0)
+    result["cache"] = cache_leg(torch, pk, case, attn, accept, args.steps, args.warmup)
     del attn, accept
     torch.cuda.empty_cache()
 
