@@ -36,6 +36,8 @@
 
 #include "internal.h"
 
+#include "pkv.h"
+
 namespace pkv {
 namespace {
 
@@ -61,6 +63,9 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 #endif
 #ifndef PKV_MFMA_WAVES
 #define PKV_MFMA_WAVES 4  // waves per workgroup, MFMA row tile
+#endif
+#ifndef PKV_PREFILL_NBUF
+#define PKV_PREFILL_NBUF 8  // K/V chunks in the ring shared by a prefill workgroup
 #endif
 #ifndef PKV_FORCE_PPS
 #define PKV_FORCE_PPS 0  // pages per split; 0 = planned per shape
@@ -385,6 +390,24 @@ struct MfmaTile {
     }
   }
 
+  // Rows row0 .. row0 + 32 * NRB of a longer row set, where row r is window
+  // token r / group and rows outside [r_lo, r_hi) are padding: row r sees
+  // keys 0 .. lim_base + r / group.
+  __device__ __forceinline__ void init_rows(int row0, int group, int lim_base, int r_lo, int r_hi) {
+    const int row = threadIdx.x & 31;
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      const int r = row0 + rb * 32 + row;
+      m[rb] = kNegInf;
+      l[rb] = 0.f;
+      lim[rb] = (r >= r_lo && r < r_hi) ? lim_base + r / group : -1;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[rb][mb][i] = 0.f;
+    }
+  }
+
   __device__ __forceinline__ void load_q(const char* qlds) {
     const int lane = threadIdx.x & 63;
     const int row = lane & 31, half = lane >> 5;
@@ -439,6 +462,11 @@ struct MfmaTile {
     }
   }
 
+  // SPLIT_P: P enters the P.V product as two bf16 terms (its rounding and
+  // the rounding remainder), so P carries about 16 significant bits instead
+  // of 8. Worth it where a row sees few keys and nothing averages the
+  // rounding out.
+  template <bool SPLIT_P = false>
   __device__ __forceinline__ void compute(float*, int tok0, int nv, float scale_log2) {
     const int lane = threadIdx.x & 63;
     const int half = lane >> 5;
@@ -458,6 +486,7 @@ struct MfmaTile {
     }
     // this lane holds tokens 8*(i/4) + 4*half + i%4 of q row `row`
     u32x4 pb[NRB][2];
+    u32x4 pl[NRB][2];
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
       float x[16];
@@ -489,6 +518,14 @@ struct MfmaTile {
         pb[rb][ks].y = pack_bf16(p[8 * ks + 2], p[8 * ks + 3]);
         pb[rb][ks].z = pack_bf16(p[8 * ks + 4], p[8 * ks + 5]);
         pb[rb][ks].w = pack_bf16(p[8 * ks + 6], p[8 * ks + 7]);
+        if constexpr (SPLIT_P) {
+          const u32 h[4] = {pb[rb][ks].x, pb[rb][ks].y, pb[rb][ks].z, pb[rb][ks].w};
+          u32 lo[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            lo[e] = pack_bf16(p[8 * ks + 2 * e] - bf16lo(h[e]), p[8 * ks + 2 * e + 1] - bf16hi(h[e]));
+          pl[rb][ks] = u32x4{lo[0], lo[1], lo[2], lo[3]};
+        }
       }
     }
     // O^T[d][q row] += sum_token V[token][d] * P[q row][token]
@@ -497,10 +534,15 @@ struct MfmaTile {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-        for (int rb = 0; rb < NRB; ++rb)
+        for (int rb = 0; rb < NRB; ++rb) {
           acc[rb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va[mb][ks]),
                                                                 __builtin_bit_cast(bf16x8, pb[rb][ks]),
                                                                 acc[rb][mb], 0, 0, 0);
+          if constexpr (SPLIT_P)
+            acc[rb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va[mb][ks]),
+                                                                  __builtin_bit_cast(bf16x8, pl[rb][ks]),
+                                                                  acc[rb][mb], 0, 0, 0);
+        }
   }
 
   __device__ __forceinline__ void spill(float* rm, float* rl, float* racc) {
@@ -829,6 +871,182 @@ __global__ __launch_bounds__(WAVES * 64) void attn_split_kernel(
   if (threadIdx.x == 0) __hip_atomic_store(p.counters + bg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// ------------------------------------------------------------ prefill kernel
+
+// Long windows (q_len * group > 64 rows: prefill, or a long chunk of it over a
+// cached prefix). A workgroup takes a query tile of kPrefillRows rows (rows =
+// window tokens times the head group) of one (sequence, KV head) and streams
+// every key the tile may see, 0 .. the tile's last token, through a ring of
+// K/V chunks shared by its waves. Each wave owns 64 of the rows on the MFMA
+// row tile, so a K/V chunk staged once in LDS feeds 4 x 64 rows; the ring is
+// filled by direct buffer->LDS loads, each wave issuing a quarter of every
+// chunk. Tiles are aligned to the end of the window, so tile 0 of every
+// sequence is the one with the most keys, and the launch takes tile 0 of every
+// (sequence, KV head) first (longest work first). All tiles of a (sequence,
+// KV head) land on the same XCD when B * Hkv is a multiple of 8, so the K/V
+// they share is served from that XCD's L2. No split of the key range: every
+// tile writes its rows of `out` itself.
+
+constexpr int kPrefillWaves = 4;
+constexpr int kPrefillRows = kPrefillWaves * 64;
+constexpr int kPrefillMaxPages = 2048;  // table entries staged per tile (524288 tokens)
+
+template <int LPC, int A>
+__device__ __forceinline__ void wait_chunks(int ahead) {
+  if constexpr (A > 0) {
+    if (ahead >= A) {
+      wait_vmcnt<LPC * A>();
+      return;
+    }
+    wait_chunks<LPC, A - 1>(ahead);
+  } else {
+    wait_vmcnt<0>();
+  }
+}
+
+template <int D, int NBUF>
+__global__ __launch_bounds__(kPrefillRows) void attn_prefill_kernel(
+    const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
+    const int32_t* __restrict__ q_lens, int B, int Hkv, int qtok, int W, AttnParams p) {
+  using Tile = MfmaTile<D, 2>;
+  using G = TileGeom<D, 32>;
+  constexpr int TC = 32;
+  constexpr int NI = G::NI;   // 1 KiB loads per K (or V) chunk
+  constexpr int NC = G::NC;
+  constexpr int KPW = NI / kPrefillWaves;  // this wave's share of them
+  constexpr int LPC = 2 * KPW;             // load instructions per chunk per wave
+  static_assert(NI % kPrefillWaves == 0, "chunk loads split evenly over the waves");
+  static_assert(NBUF >= 2 && LPC * (NBUF - 2) < 64, "ring depth");
+  __shared__ __attribute__((aligned(16))) char ring[NBUF * 2 * G::TILE];
+  __shared__ int s_pages[kPrefillMaxPages];
+
+  const int bh = B * Hkv;
+  const int bg = blockIdx.x % bh, qr = blockIdx.x / bh;
+  const int b = bg / Hkv, g = bg % Hkv;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+
+  const int seq_len = seq_lens[b];
+  const int q_len = q_lens[b];
+  const int q_start = __builtin_amdgcn_readfirstlane(wave_prefix(q_lens, b));
+  if (q_len <= 0) return;
+  const int n_tiles = (q_len + qtok - 1) / qtok;
+  if (qr >= n_tiles) return;
+  const int n_pages = (seq_len + kPage - 1) / kPage;
+  if (q_len > p.max_q_len || q_len > seq_len || n_pages > W || n_pages > kPrefillMaxPages) {
+    if (qr == 0 && g == 0 && threadIdx.x == 0) atomicOr(p.err, PKV_EFLAG_QLEN_BIT);
+    return;
+  }
+  if (q_start + q_len > p.total_q) {
+    if (qr == 0 && g == 0 && threadIdx.x == 0) atomicOr(p.err, PKV_EFLAG_ROWS_BIT);
+    return;
+  }
+  // this tile: window tokens tq0 .. tq0 + qtok - 1 (those >= 0), keys 0 .. key_end - 1
+  const int tq0 = q_len - (qr + 1) * qtok;
+  const int key_end = seq_len - qr * qtok;
+  const int n_chunks = (key_end + TC - 1) / TC;
+  const int need_pages = (key_end + kPage - 1) / kPage;
+  for (int j = threadIdx.x; j < need_pages; j += kPrefillRows) {
+    int e = block_table[(size_t)b * W + j];
+    if (e < 0 || e >= p.P) {
+      atomicOr(p.err, PKV_EFLAG_PAGE_BIT);
+      e = -1;
+    }
+    s_pages[j] = e;
+  }
+
+  // q rows of this wave straight into the MFMA operand registers: row r of
+  // the tile is window token tq0 + r / group, q head g * group + r % group
+  Tile tile;
+  const int r_lo = (tq0 < 0 ? -tq0 : 0) * p.group, r_hi = qtok * p.group;
+  tile.init_rows(wave * 64, p.group, seq_len - q_len + tq0, r_lo, r_hi);
+  {
+    const int half = lane >> 5;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const int r = wave * 64 + rb * 32 + (lane & 31);
+      const bool ok = r >= r_lo && r < r_hi;
+      const u32x4* src = reinterpret_cast<const u32x4*>(
+          p.q + ((size_t)(q_start + tq0 + (ok ? r / p.group : 0 - tq0)) * p.Hq + g * p.group + r % p.group) * D);
+#pragma unroll
+      for (int kk = 0; kk < Tile::KK; ++kk) tile.qb[rb][kk] = ok ? src[2 * kk + half] : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  __syncthreads();  // table entries staged
+
+  // per-lane byte offsets of this wave's share of a chunk's direct loads
+  u32 voff[KPW];
+#pragma unroll
+  for (int i = 0; i < KPW; ++i) {
+    const int slot = (wave * KPW + i) * 64 + lane;
+    const int t = slot / NC, pos = slot % NC;
+    voff[i] = t * G::RB + ((pos ^ (t & (NC - 1))) * 16);
+  }
+  const u32 ring_lds = lds_addr_of(ring);
+  const size_t head_stride = (size_t)kPage * D;
+  auto issue = [&](int c) {
+    const int t0 = c * TC;
+    const int phys = __builtin_amdgcn_readfirstlane(s_pages[t0 / kPage]);
+    int nvt = min(TC, key_end - t0);
+    if (phys < 0) nvt = 0;
+    const size_t off = ((size_t)(phys < 0 ? 0 : phys) * Hkv + g) * head_stride + (size_t)(t0 % kPage) * D;
+    const u32 bytes = nvt > 0 ? (u32)(nvt * G::RB) : 0u;
+    const u32x4 rk = make_rsrc(p.k_pool + off, bytes);
+    const u32x4 rv = make_rsrc(p.v_pool + off, bytes);
+    const u32 base = uniform(ring_lds + (c % NBUF) * 2 * G::TILE + wave * KPW * 1024);
+#pragma unroll
+    for (int i = 0; i < KPW; ++i) dma16(rk, voff[i], base + i * 1024);
+#pragma unroll
+    for (int i = 0; i < KPW; ++i) dma16(rv, voff[i], base + G::TILE + i * 1024);
+  };
+
+#pragma unroll
+  for (int c = 0; c < NBUF - 1; ++c)
+    if (c < n_chunks) issue(c);
+
+  // chunk c has landed once at most the chunks issued after it are pending
+  // (this wave's share); the barrier then covers the other waves' shares and
+  // tells that every wave is done reading chunk c - 1's slot, which takes
+  // chunk c + NBUF - 1
+  auto arrive = [&](int c) {
+    wait_chunks<LPC, NBUF - 2>(min(NBUF - 2, n_chunks - 1 - c));
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (c + NBUF - 1 < n_chunks) issue(c + NBUF - 1);
+    tile.fetch(ring + (c % NBUF) * 2 * G::TILE, ring + (c % NBUF) * 2 * G::TILE + G::TILE, 0);
+  };
+  // the first 64 keys with P in two bf16 terms: rows that see fewer than 64
+  // keys see nothing else, and their few terms would not average out the
+  // rounding of a single bf16 P
+  const int n_split = min(n_chunks, 64 / TC);
+  for (int c = 0; c < n_split; ++c) {
+    arrive(c);
+    tile.template compute<true>(nullptr, c * TC, min(TC, key_end - c * TC), p.scale_log2);
+  }
+  for (int c = n_split; c < n_chunks; ++c) {
+    arrive(c);
+    tile.compute(nullptr, c * TC, min(TC, key_end - c * TC), p.scale_log2);
+  }
+
+  // rows -> out
+  {
+    const int half = lane >> 5;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const int r = wave * 64 + rb * 32 + (lane & 31);
+      const float ls = tile.l[rb] + shfl_xor(tile.l[rb], 32);
+      if (r < r_lo || r >= r_hi) continue;
+      float* dst = p.out + ((size_t)(q_start + tq0 + r / p.group) * p.Hq + g * p.group + r % p.group) * D;
+#pragma unroll
+      for (int mb = 0; mb < Tile::MB; ++mb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f32x4 v = {tile.acc[rb][mb][4 * j], tile.acc[rb][mb][4 * j + 1], tile.acc[rb][mb][4 * j + 2],
+                           tile.acc[rb][mb][4 * j + 3]};
+          *reinterpret_cast<f32x4*>(dst + mb * 32 + 8 * j + 4 * half) = v / ls;
+        }
+    }
+  }
+}
+
 template <int D, class Tile, int NBUF, int WAVES>
 hipError_t launch_one(const AttnParams& p, hipStream_t stream) {
   const int per_xcd = (p.num_items + kNumXcd - 1) / kNumXcd;
@@ -858,6 +1076,14 @@ AttnPlan attn_plan(int B, int Hkv, int W, int max_q_len, int group) {
   AttnPlan pl;
   pl.rows = max_q_len * group;
   pl.mfma = pl.rows > 12;
+  pl.prefill = pl.rows > PKV_MAX_ROWS;
+  pl.qtok = kPrefillRows / group;
+  pl.tiles = (max_q_len + pl.qtok - 1) / pl.qtok;
+  if (pl.prefill) {  // no split of the key range, no partials
+    pl.pps = W;
+    pl.max_splits = 1;
+    return pl;
+  }
   // Workgroups resident per CU, from the LDS each variant claims.
   int smem;
   if (pl.mfma)
@@ -887,7 +1113,7 @@ static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 AttnWorkspace attn_workspace(int B, int Hkv, int W, int max_q_len, int group, int D) {
   const AttnPlan pl = attn_plan(B, Hkv, W, max_q_len, group);
   AttnWorkspace ws;
-  const size_t items = (size_t)B * Hkv * pl.max_splits;
+  const size_t items = pl.prefill ? 0 : (size_t)B * Hkv * pl.max_splits;
   ws.err_off = 0;
   ws.counters_off = 256;
   ws.ml_off = align_up(ws.counters_off + (size_t)B * Hkv * 4, 256);
@@ -898,6 +1124,15 @@ AttnWorkspace attn_workspace(int B, int Hkv, int W, int max_q_len, int group, in
 
 hipError_t launch_attn(const AttnParams& p, const AttnPlan& plan, hipStream_t stream) {
   if (p.num_items == 0) return hipSuccess;
+  if (plan.prefill) {
+    if (p.D == 64)
+      hipLaunchKernelGGL((attn_prefill_kernel<64, PKV_PREFILL_NBUF>), dim3(p.num_items), dim3(kPrefillRows), 0,
+                         stream, p.block_table, p.seq_lens, p.q_lens, p.B, p.Hkv, plan.qtok, p.W, p);
+    else
+      hipLaunchKernelGGL((attn_prefill_kernel<128, PKV_PREFILL_NBUF>), dim3(p.num_items), dim3(kPrefillRows), 0,
+                         stream, p.block_table, p.seq_lens, p.q_lens, p.B, p.Hkv, plan.qtok, p.W, p);
+    return hipGetLastError();
+  }
   if (p.D == 64) return launch_d<64>(p, plan, stream);
   return launch_d<128>(p, plan, stream);
 }

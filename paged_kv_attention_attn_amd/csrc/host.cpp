@@ -17,9 +17,9 @@ bool attn_shape_ok(const pkv_attn_shape* s) {
   if (s->head_dim != 64 && s->head_dim != 128) return false;
   if (s->page_size != PKV_PAGE_SIZE) return false;
   if (s->num_pages < 1 || s->max_pages_per_seq < 1 || s->total_q < 0) return false;
-  if (s->max_q_len < 1 || s->max_q_len > PKV_MAX_Q_LEN) return false;
-  const long rows = (long)s->max_q_len * (s->num_q_heads / s->num_kv_heads);
-  if (rows > PKV_MAX_ROWS) return false;
+  // windows up to the table's capacity; a head group up to the rows of one wave
+  if (s->max_q_len < 1 || (long)s->max_q_len > (long)s->max_pages_per_seq * PKV_PAGE_SIZE) return false;
+  if (s->num_q_heads / s->num_kv_heads > PKV_MAX_ROWS) return false;
   if (!std::isfinite(s->scale)) return false;
   // 32-bit indexing limits inside the kernels
   if ((long)s->num_seqs * s->max_pages_per_seq > (1L << 31) - 1) return false;
@@ -125,7 +125,7 @@ int pkv_attn_fwd(const void* q, const void* k_pool, const void* v_pool, const in
   p.rows_max = plan.rows;
   p.pps = plan.pps;
   p.max_splits = plan.max_splits;
-  p.num_items = s->num_seqs * s->num_kv_heads * plan.max_splits;
+  p.num_items = s->num_seqs * s->num_kv_heads * (plan.prefill ? plan.tiles : plan.max_splits);
   p.scale_log2 = static_cast<float>(static_cast<double>(s->scale) * 1.4426950408889634);
   if (pkv::launch_attn(p, plan, static_cast<hipStream_t>(stream)) != hipSuccess) return PKV_ERR_HIP;
   return PKV_OK;

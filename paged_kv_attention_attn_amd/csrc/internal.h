@@ -40,6 +40,9 @@ struct AttnPlan {
   int max_splits;
   int rows;      // rows_max = max_q_len * group
   bool mfma;     // row tile on matrix cores (rows >= 16)
+  bool prefill;  // rows > PKV_MAX_ROWS: the long-window kernel
+  int qtok;      // prefill: window tokens per query tile
+  int tiles;     // prefill: query tiles of the longest window
 };
 
 AttnPlan attn_plan(int B, int Hkv, int W, int max_q_len, int group);

@@ -64,8 +64,9 @@ def good_shape(pk, **kw):
     dict(num_q_heads=30),            # Hq % Hkv != 0
     dict(head_dim=96),               # unsupported D
     dict(page_size=128),             # pages are 256 tokens
-    dict(max_q_len=0), dict(max_q_len=17),
-    dict(num_q_heads=64, max_q_len=16),   # 16 * 8 rows > 64
+    dict(max_q_len=0),
+    dict(max_q_len=8 * 256 + 1),          # longer than a table row can hold
+    dict(num_q_heads=8 * 65),             # a head group wider than 64 rows
     dict(num_pages=0), dict(max_pages_per_seq=0), dict(num_seqs=-1),
     dict(scale=float("nan")),
 ])
@@ -74,6 +75,13 @@ def test_bad_attention_shapes_are_rejected_before_launch(pk, bad):
     assert pk.pkv_attn_workspace_bytes(s) == 0
     rc = pk.LIB.pkv_attn_fwd(None, None, None, None, None, None, None, ctypes.byref(s), None, 0, None)
     assert rc == pk.PKV_ERR_SHAPE
+
+
+@pytest.mark.parametrize("ok", [dict(max_q_len=16), dict(max_q_len=17), dict(max_q_len=8 * 256),
+                                dict(num_q_heads=64, max_q_len=16), dict(num_q_heads=8 * 64, max_q_len=1)])
+def test_long_windows_and_wide_groups_are_accepted(pk, ok):
+    # more than 64 rows per (sequence, KV head) runs the long-window kernel
+    assert pk.pkv_attn_workspace_bytes(good_shape(pk, **ok)) > 0
 
 
 def test_null_pointers_and_small_workspace_are_rejected(pk):

@@ -195,3 +195,48 @@ def test_rejects_window_longer_than_sequence():
                    case.block_table, case.seq_lens, np.array([4], np.int32), case.scale)
     with pytest.raises(ValueError):
         run(bad)
+
+
+# Long windows (prefill, or a prefill chunk over cached tokens) use the same
+# definition: window row i sees keys 0 .. seq_len - q_len + i.
+
+@pytest.mark.parametrize("seq_lens,q_lens,Hq,Hkv,D", [
+    ([20], [20], 2, 1, 4),          # a whole prompt, no cached prefix
+    ([290, 40], [33, 40], 4, 2, 4),  # a chunk over 257 cached tokens; a whole short prompt
+])
+def test_long_window_matches_brute_force(seq_lens, q_lens, Hq, Hkv, D):
+    case = make_tiny_case(16, seq_lens, q_lens, Hq=Hq, Hkv=Hkv, D=D)
+    got = run(case)
+    ref = np.array(attention_brute(case.q, case.k_pool, case.v_pool, case.block_table,
+                                   case.seq_lens, case.q_lens, case.scale))
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-13)
+
+
+def test_whole_prompt_equals_library_causal_attention():
+    """With no cached prefix (q_len = seq_len) the window is ordinary causal
+    self-attention; torch's CPU scaled_dot_product_attention(is_causal=True)
+    in float64, over K/V heads repeated to the q heads, must agree."""
+    import torch
+    L, Hq, Hkv, D = 300, 8, 2, 16
+    case = make_tiny_case(17, [L], [L], Hq=Hq, Hkv=Hkv, D=D)
+    got = run(case)
+    q = torch.from_numpy(oracle.decode_bf16(case.q)).permute(1, 0, 2)               # [Hq, L, D]
+    K = oracle.decode_bf16(oracle.gather_sequence(case.k_pool, case.block_table[0], L))
+    V = oracle.decode_bf16(oracle.gather_sequence(case.v_pool, case.block_table[0], L))
+    k = torch.from_numpy(K).repeat_interleave(Hq // Hkv, dim=0)                      # [Hq, L, D]
+    v = torch.from_numpy(V).repeat_interleave(Hq // Hkv, dim=0)
+    ref = torch.nn.functional.scaled_dot_product_attention(q[None], k[None], v[None], is_causal=True,
+                                                           scale=case.scale)[0].permute(1, 0, 2).numpy()
+    np.testing.assert_allclose(got, ref, rtol=1e-11, atol=1e-13)
+
+
+def test_prefill_in_chunks_equals_whole_prompt():
+    """Prefilling a prompt in chunks, each chunk's window attending to the
+    tokens cached before it, gives the rows of the whole-prompt window."""
+    L = 530
+    case = make_tiny_case(18, [L], [L], Hq=4, Hkv=2, D=8)
+    whole = run(case)
+    for lo, hi in ((0, 100), (100, 256), (256, 257), (257, 530)):
+        part = AttnCase("chunk", case.q[lo:hi], case.k_pool, case.v_pool, case.block_table,
+                        np.array([hi], np.int32), np.array([hi - lo], np.int32), case.scale)
+        np.testing.assert_array_equal(run(part), whole[lo:hi])

@@ -21,6 +21,7 @@ from .configs import (
     AttnCase,
     AcceptCase,
     make_config,
+    make_prefill_config,
     make_tiny_case,
     make_accept_case,
     kv_logical_bytes,
@@ -32,6 +33,6 @@ from .churn import Config5Queue
 
 __all__ = [
     "f32_to_bf16_bits", "bf16_bits_to_f32", "BF16_QNAN", "PAGE", "AttnCase", "AcceptCase",
-    "make_config", "make_tiny_case", "make_accept_case", "kv_logical_bytes",
+    "make_config", "make_prefill_config", "make_tiny_case", "make_accept_case", "kv_logical_bytes",
     "contiguous_twin", "permute_pages", "duplicate_shared_pages", "Config5Queue",
 ]

@@ -263,6 +263,32 @@ def make_config(cfg, seed=0, poison=True):
     return case, acc
 
 
+def make_prefill_config(which, seed=0, poison=True):
+    """Long-window (prefill) workloads on the shapes of configurations 3 and 4.
+
+    * ``"full"``: the verify configuration's cache (8 sequences of 8192 tokens
+      filling the 256-page pool, 32/8 heads, head_dim 128), every token a
+      window row: q_len = seq_len = 8192, a whole-prompt prefill.
+    * ``"dedup"``: the prefix-dedup layout of configuration 4 (100 sequences
+      sharing 16 pages of prompt prefix, one private page of 1..256 tokens
+      each); only the private tail is a window (q_len = tail length), the
+      work that remains when the shared prefix is already cached.
+    """
+    if which == "full":
+        case, _ = make_config(3, seed, poison)
+        q_lens = case.seq_lens.copy()
+    elif which == "dedup":
+        case, _ = make_config(4, seed, poison)
+        q_lens = (case.seq_lens - 4096).astype(np.int32)
+    else:
+        raise ValueError("which is 'full' or 'dedup'")
+    Hq, D = case.num_q_heads, case.head_dim
+    q = _q_for(_rng(200 + case.meta["cfg"], seed, 1), q_lens, Hq, D)
+    return AttnCase(f"prefill-{which}", q, case.k_pool, case.v_pool, case.block_table, case.seq_lens,
+                    q_lens.astype(np.int32), case.scale, meta={"cfg": case.meta["cfg"], "seed": seed,
+                                                               "prefill": which})
+
+
 # ---------------------------------------------------------------- layout transforms
 
 def contiguous_twin(case):
