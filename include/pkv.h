@@ -40,8 +40,9 @@ extern "C" {
 #endif
 
 #define PKV_PAGE_SIZE 256 /* tokens per page; fixed by the Dynamic Generator page */
-#define PKV_MAX_Q_LEN 16  /* longest verify window (k drafts + 1) per sequence  */
-#define PKV_MAX_ROWS 64   /* q_len * (Hq / Hkv) per sequence and KV head        */
+#define PKV_MAX_Q_LEN 16  /* longest verify window (k drafts + 1) of the accept step   */
+#define PKV_MAX_ROWS 64   /* q_len * (Hq / Hkv) served by the decode / verify kernel;
+                             longer windows run the long-window (prefill) kernel     */
 
 typedef enum {
   PKV_OK = 0,
@@ -69,8 +70,7 @@ typedef struct {
   int32_t num_pages;         /* P >= 1: pages in each pool                          */
   int32_t max_pages_per_seq; /* W >= 1: row stride of block_table                   */
   int32_t total_q;           /* rows of q and out; must equal sum(q_lens)           */
-  int32_t max_q_len;         /* 1..PKV_MAX_Q_LEN, >= every q_lens[b]; and           */
-                             /* max_q_len * (Hq/Hkv) <= PKV_MAX_ROWS                */
+  int32_t max_q_len;         /* 1 .. W * 256, >= every q_lens[b]; Hq/Hkv <= 64      */
   float scale;               /* softmax scale applied to q.k (e.g. 1/sqrt(D))       */
 } pkv_attn_shape;
 
@@ -86,7 +86,14 @@ int pkv_attn_workspace_init(void* workspace, size_t bytes, void* stream);
 
 /*
  * Paged attention for decode (q_len = 1) and speculative verification
- * (q_len = k + 1, causal inside the window), in one kernel.
+ * (q_len = k + 1, causal inside the window), in one kernel; and for long
+ * windows (a prompt prefill, or a chunk of one over cached tokens) with the
+ * same definition: when max_q_len * (Hq/Hkv) > PKV_MAX_ROWS the whole batch
+ * runs the long-window kernel (query tiles of 256 rows, no split of the key
+ * range). Sources: the Dynamic Generator page, "Deduplication" (a job whose
+ * prompt prefix is already cached only processes the rest: a window over
+ * cached tokens), and the Assisted Generation page, "How Assisted Generation
+ * works" (one pass scores every position of a window).
  *
  * q           bf16 [total_q, Hq, D]; rows packed by sequence, then window row.
  * k_pool      bf16 [P, Hkv, 256, D]: K of page p, KV head g, slot s at
@@ -107,7 +114,13 @@ int pkv_attn_workspace_init(void* workspace, size_t bytes, void* stream);
  * they never affect `out`. Results are deterministic: they depend only on the
  * contents a sequence references, not on which physical pages hold them.
  * Contract: block-table entries a sequence needs lie in [0, P); sum(q_lens) ==
- * total_q; q_len <= max_q_len; q_len <= seq_len <= W * 256.
+ * total_q; q_len <= max_q_len; q_len <= seq_len <= W * 256; on the long-window
+ * kernel also seq_len <= 2048 * 256 (longer sequences are skipped and flagged
+ * PKV_EFLAG_QLEN).
+ * Precision: fp32 scores and softmax; on matrix cores (rows >= 13) P enters
+ * P.V rounded to bf16, except for the first 64 keys on the long-window kernel,
+ * where it enters as two bf16 terms (rows with few keys would not average the
+ * rounding out).
  */
 int pkv_attn_fwd(const void* q, const void* k_pool, const void* v_pool,
                  const int32_t* block_table, const int32_t* seq_lens, const int32_t* q_lens,

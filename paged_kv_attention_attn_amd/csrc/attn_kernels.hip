@@ -38,6 +38,8 @@
 
 #include "pkv.h"
 
+#include <type_traits>
+
 namespace pkv {
 namespace {
 
@@ -434,7 +436,7 @@ struct MfmaTile {
   // i/4 + 8 and i/4 + 12. With source lane j at token t0 + j/4 and dims
   // d0 + 4*(j%4) .. + 3, lane i gets tokens t0 .. t0 + 3 of dim d0 + i. Rows
   // past the sequence end were zero-filled by the chunk load, so no mask.
-  __device__ __forceinline__ void fetch(const char* kt, const char* vt, int) {
+  __device__ __forceinline__ void fetch_k(const char* kt) {
     const int lane = threadIdx.x & 63;
     const int row = lane & 31, half = lane >> 5;
     const u32x4* kl = reinterpret_cast<const u32x4*>(kt);
@@ -443,6 +445,11 @@ struct MfmaTile {
       const int c = 2 * kk + half;
       ka[kk] = kl[row * NC + (c ^ (row & (NC - 1)))];
     }
+  }
+
+  __device__ __forceinline__ void fetch_v(const char* vt) {
+    const int lane = threadIdx.x & 63;
+    const int half = lane >> 5;
     const int tq = (lane & 15) >> 2;                         // token within the 4-token group
     const int dsub = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // dims within the 32-dim block
 #pragma unroll
@@ -462,11 +469,11 @@ struct MfmaTile {
     }
   }
 
-  // SPLIT_P: P enters the P.V product as two bf16 terms (its rounding and
-  // the rounding remainder), so P carries about 16 significant bits instead
-  // of 8. Worth it where a row sees few keys and nothing averages the
-  // rounding out.
-  template <bool SPLIT_P = false>
+  __device__ __forceinline__ void fetch(const char* kt, const char* vt, int) {
+    fetch_k(kt);
+    fetch_v(vt);
+  }
+
   __device__ __forceinline__ void compute(float*, int tok0, int nv, float scale_log2) {
     const int lane = threadIdx.x & 63;
     const int half = lane >> 5;
@@ -486,7 +493,6 @@ struct MfmaTile {
     }
     // this lane holds tokens 8*(i/4) + 4*half + i%4 of q row `row`
     u32x4 pb[NRB][2];
-    u32x4 pl[NRB][2];
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
       float x[16];
@@ -518,8 +524,125 @@ struct MfmaTile {
         pb[rb][ks].y = pack_bf16(p[8 * ks + 2], p[8 * ks + 3]);
         pb[rb][ks].z = pack_bf16(p[8 * ks + 4], p[8 * ks + 5]);
         pb[rb][ks].w = pack_bf16(p[8 * ks + 6], p[8 * ks + 7]);
+      }
+    }
+    // O^T[d][q row] += sum_token V[token][d] * P[q row][token]
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb)
+          acc[rb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va[mb][ks]),
+                                                                __builtin_bit_cast(bf16x8, pb[rb][ks]),
+                                                                acc[rb][mb], 0, 0, 0);
+  }
+
+  // Long-window variant of compute (query tiles that see thousands of keys),
+  // in steps the caller can interleave across chunks:
+  //  * qk(): S^T on matrix cores; scores(): S^T scaled (and masked unless
+  //    MASK is false, for chunks every row of the wave sees in full) into xs,
+  //    and the chunk's row maxima into cmax. Lazy rescale: a row keeps its reference
+  //    max m while the chunk stays below m + kLazyLog2, so P = 2^(x - m) may
+  //    reach 2^kLazyLog2 and the softmax ratio is unchanged; scores() returns
+  //    whether some row of the wave outgrew that;
+  //  * rescale(): moves those rows' m and rescales their l and O^T;
+  //  * accumulate(): P, l and O^T += V^T . P^T. SPLIT_P: P enters as two bf16
+  //    terms (its rounding and the remainder), about 16 significant bits
+  //    instead of 8, for rows that see so few keys that nothing averages the
+  //    rounding out.
+  static constexpr float kLazyLog2 = 8.f;
+  float xs[NRB][16], cmax[NRB];
+
+  // S^T of the current K operand for every row block.
+  __device__ __forceinline__ void qk(f32x16* S) const {
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) S[rb][i] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb)
+        S[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ka[kk]),
+                                                        __builtin_bit_cast(bf16x8, qb[rb][kk]), S[rb], 0, 0,
+                                                        0);
+    }
+  }
+
+  template <bool MASK>
+  __device__ __forceinline__ bool scores(const f32x16* S, int tok0, int nv, float scale_log2) {
+    const int lane = threadIdx.x & 63;
+    const int half = lane >> 5;
+    bool grow = false;
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      float cm = kNegInf;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int tt = 8 * (i >> 2) + 4 * half + (i & 3);
+        if constexpr (MASK)
+          xs[rb][i] = (tok0 + tt <= lim[rb] && tt < nv) ? S[rb][i] * scale_log2 : kNegInf;
+        else
+          xs[rb][i] = S[rb][i] * scale_log2;
+        cm = fmaxf(cm, xs[rb][i]);
+      }
+      cmax[rb] = fmaxf(cm, shfl_xor(cm, 32));
+      grow |= cmax[rb] > m[rb] + kLazyLog2;
+    }
+    return __builtin_amdgcn_ballot_w64(grow) != 0;
+  }
+
+  // O^T lives in the accumulation registers; the rescale multiplies it in
+  // place there (read, multiply, write back per element), so the compiler
+  // never needs a VALU-side copy of it in the chunk loop. The s_nop runs
+  // cover the matrix-core result latency before the first read and the
+  // write-to-operand latency after the last write.
+  __device__ __forceinline__ void rescale() {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::: "memory");
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      const bool g = cmax[rb] > m[rb] + kLazyLog2;
+      const float alpha = g ? exp2f_fast(m[rb] - cmax[rb]) : 1.f;
+      m[rb] = g ? cmax[rb] : m[rb];
+      l[rb] *= alpha;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float x = acc[rb][mb][i], t;
+          asm volatile(
+              "v_accvgpr_read_b32 %1, %0\n\t"
+              "v_mul_f32 %1, %1, %2\n\t"
+              "v_accvgpr_write_b32 %0, %1"
+              : "+a"(x), "=&v"(t)
+              : "v"(alpha));
+          acc[rb][mb][i] = x;
+        }
+    }
+    asm volatile("s_nop 3" ::: "memory");
+  }
+
+  template <bool SPLIT_P>
+  __device__ __forceinline__ void accumulate() {
+    u32x4 pb[NRB][2], pl[NRB][2];
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      const float mu = (m[rb] == kNegInf) ? 0.f : m[rb];
+      float p[16], ps = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        p[i] = exp2f_fast(xs[rb][i] - mu);
+        ps += p[i];
+      }
+      l[rb] += ps;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        u32 h[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) h[e] = pack_bf16(p[8 * ks + 2 * e], p[8 * ks + 2 * e + 1]);
+        pb[rb][ks] = u32x4{h[0], h[1], h[2], h[3]};
         if constexpr (SPLIT_P) {
-          const u32 h[4] = {pb[rb][ks].x, pb[rb][ks].y, pb[rb][ks].z, pb[rb][ks].w};
           u32 lo[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e)
@@ -528,7 +651,6 @@ struct MfmaTile {
         }
       }
     }
-    // O^T[d][q row] += sum_token V[token][d] * P[q row][token]
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -916,7 +1038,7 @@ __global__ __launch_bounds__(kPrefillRows) void attn_prefill_kernel(
   constexpr int KPW = NI / kPrefillWaves;  // this wave's share of them
   constexpr int LPC = 2 * KPW;             // load instructions per chunk per wave
   static_assert(NI % kPrefillWaves == 0, "chunk loads split evenly over the waves");
-  static_assert(NBUF >= 2 && LPC * (NBUF - 2) < 64, "ring depth");
+  static_assert(NBUF >= 3 && LPC * (NBUF - 3) < 64, "ring depth");
   __shared__ __attribute__((aligned(16))) char ring[NBUF * 2 * G::TILE];
   __shared__ int s_pages[kPrefillMaxPages];
 
@@ -970,6 +1092,13 @@ __global__ __launch_bounds__(kPrefillRows) void attn_prefill_kernel(
 #pragma unroll
       for (int kk = 0; kk < Tile::KK; ++kk) tile.qb[rb][kk] = ok ? src[2 * kk + half] : u32x4{0u, 0u, 0u, 0u};
     }
+    // wait for the q operands here: a load still pending at the chunk loop
+    // would make the compiler wait for every load in flight (the whole K/V
+    // ring, which it does not see) at each chunk
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int kk = 0; kk < Tile::KK; ++kk) asm volatile("" ::"v"(tile.qb[rb][kk]));
   }
   __syncthreads();  // table entries staged
 
@@ -1000,31 +1129,59 @@ __global__ __launch_bounds__(kPrefillRows) void attn_prefill_kernel(
   };
 
 #pragma unroll
-  for (int c = 0; c < NBUF - 1; ++c)
+  for (int c = 0; c < NBUF - 2; ++c)
     if (c < n_chunks) issue(c);
 
-  // chunk c has landed once at most the chunks issued after it are pending
-  // (this wave's share); the barrier then covers the other waves' shares and
-  // tells that every wave is done reading chunk c - 1's slot, which takes
-  // chunk c + NBUF - 1
-  auto arrive = [&](int c) {
-    wait_chunks<LPC, NBUF - 2>(min(NBUF - 2, n_chunks - 1 - c));
+  // The chunk loop is software-pipelined: while the VALU turns chunk c's
+  // scores into P, the matrix cores already compute chunk c + 1's scores.
+  // arrive(k): chunk k has landed once at most the chunks issued after it are
+  // pending (this wave's share); the barrier then covers the other waves'
+  // shares and tells that every wave is done with chunk k - 2 (its V was read
+  // in the iteration that ended before it), whose slot takes chunk
+  // k + NBUF - 2. It then copies chunk k's K operand out.
+  auto slot = [&](int c) { return ring + (c % NBUF) * 2 * G::TILE; };
+  auto arrive = [&](int k) {
+    wait_chunks<LPC, NBUF - 3>(min(NBUF - 3, n_chunks - 1 - k));
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (c + NBUF - 1 < n_chunks) issue(c + NBUF - 1);
-    tile.fetch(ring + (c % NBUF) * 2 * G::TILE, ring + (c % NBUF) * 2 * G::TILE + G::TILE, 0);
+    if (k + NBUF - 2 < n_chunks) issue(k + NBUF - 2);
+    tile.fetch_k(slot(k));
   };
   // the first 64 keys with P in two bf16 terms: rows that see fewer than 64
   // keys see nothing else, and their few terms would not average out the
-  // rounding of a single bf16 P
+  // rounding of a single bf16 P. Then the chunks every valid row of this
+  // wave sees in full go unmasked; the rest (the diagonal) are masked.
   const int n_split = min(n_chunks, 64 / TC);
-  for (int c = 0; c < n_split; ++c) {
-    arrive(c);
-    tile.template compute<true>(nullptr, c * TC, min(TC, key_end - c * TC), p.scale_log2);
-  }
-  for (int c = n_split; c < n_chunks; ++c) {
-    arrive(c);
-    tile.compute(nullptr, c * TC, min(TC, key_end - c * TC), p.scale_log2);
-  }
+  const int wrow = max(r_lo, wave * 64);
+  const int wave_min_lim = wrow < r_hi ? seq_len - q_len + tq0 + wrow / p.group : key_end;
+  const int n_free = max(n_split, min(key_end / TC, (wave_min_lim + 1) / TC));
+  f32x16 S[2];
+  arrive(0);
+  tile.qk(S);
+  auto run = [&](auto split_p, auto mask, int c0, int c1) {
+    constexpr bool kSplit = decltype(split_p)::value, kMask = decltype(mask)::value;
+    for (int c = c0; c < c1; ++c) {
+      f32x16 Sn[2];
+      const bool more = c + 1 < n_chunks;
+      if (more) arrive(c + 1);
+      tile.fetch_v(slot(c) + G::TILE);
+      tile.qk(Sn);  // past the last chunk this repeats it, unused: no branch between it and the softmax
+      const bool grow = tile.template scores<kMask>(S, c * TC, min(TC, key_end - c * TC), p.scale_log2);
+      // interleave the next chunk's score products with this chunk's softmax
+      // VALU work, one matrix-core op at a time
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+      }
+      if (grow) tile.rescale();
+      tile.template accumulate<kSplit>();
+      S[0] = Sn[0];
+      S[1] = Sn[1];
+    }
+  };
+  run(std::true_type{}, std::true_type{}, 0, n_split);
+  run(std::false_type{}, std::false_type{}, n_split, n_free);
+  run(std::false_type{}, std::true_type{}, n_free, n_chunks);
 
   // rows -> out
   {
