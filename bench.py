@@ -31,6 +31,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, AMD's published figure
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core rate, AMD's published figure
 METRIC = "paged-attn KV read GB/s (fraction of HBM peak); verified tokens/s"
 
 
@@ -47,6 +48,7 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-configs", action="store_true", help="skip the per-configuration sweep")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the long-window (prefill) leg")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="time budget of the CPU oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -223,6 +225,47 @@ def cache_leg(torch, pk, case, attn, accept, steps, warmup):
                     "restores the state; the loop step is append + attention + accept + rollback"}
 
 
+def prefill_flops(case):
+    """Algorithmic flops of a long-window pass: every window row of every q
+    head does 2 * D multiply-adds per visible key for q.k and as many for p.v
+    (4 * D flops); row i of a q_len window over seq_len cached tokens sees
+    seq_len - q_len + i + 1 keys. Padding rows and masked keys are not counted."""
+    tot = 0
+    for L, ql in zip(case.seq_lens, case.q_lens):
+        L, ql = int(L), int(ql)
+        tot += ql * (L - ql) + ql * (ql + 1) // 2
+    return tot * case.num_q_heads * 4 * case.head_dim
+
+
+def prefill_leg(torch, pk, seed, steps, warmup):
+    """The long-window kernel on two prefill workloads: the verify
+    configuration's cache as a whole-prompt prefill (8 x 8192 tokens), and
+    the prefix-dedup layout prefilling only each sequence's private tail over
+    the shared 4096-token prefix. Rates are algorithmic bf16 flops against
+    the dense bf16 matrix-core peak."""
+    from workloads import make_prefill_config
+    out = {}
+    for which in ("full", "dedup"):
+        log(f"prefill {which}")
+        c = make_prefill_config(which, seed=seed)
+        a = Attn(c, pk, torch, 1)
+        ms = time_ms(torch, a, steps, warmup)
+        pct = launch_percentiles(torch, a, steps, warmup)
+        torch.cuda.synchronize()
+        assert pk.pkv_attn_check_errors(a.ws) == 0
+        fl = prefill_flops(c)
+        tflops = fl / (ms * 1e-3) / 1e12
+        out[which] = {"us": round(ms * 1e3, 1), "us_per_launch": pct, "flops": int(fl),
+                      "tflops": round(tflops, 1), "mfma_fraction": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                      "tokens_per_s": round(float(c.q_lens.sum()) / (ms * 1e-3), 1),
+                      "window_tokens": int(c.q_lens.sum()), "cached_tokens": int(c.seq_lens.sum())}
+        del a
+        torch.cuda.empty_cache()
+    out["note"] = ("algorithmic flops = 4 * head_dim * q_heads * sum over window rows of visible keys; "
+                   "peak = dense bf16 matrix-core rate")
+    return out
+
+
 def cpu_baseline(case, acc, seconds):
     """The CPU oracle on the verify step: whole sequences (attention over
     their cached tokens + accept over their logits rows) in order, passes
@@ -393,6 +436,9 @@ def main():
         sweep["config3"] = {"attn_us": result["attn_us"], "kv_bytes": kv_bytes,
                             "kv_gbps": result["attn_kv_gbps"], "hbm_fraction": result["attn_hbm_fraction"]}
         result["configs"] = sweep
+
+    if not args.no_prefill:
+        result["prefill"] = prefill_leg(torch, pk, args.seed, max(5, args.steps // 5), max(2, args.warmup // 2))
 
     if not args.no_cpu_baseline:
         log("CPU oracle sample")

@@ -402,6 +402,8 @@ struct MfmaTile {
       const int r = row0 + rb * 32 + row;
       m[rb] = kNegInf;
       l[rb] = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) lacc[rb][i] = 0.f;
       lim[rb] = (r >= r_lo && r < r_hi) ? lim_base + r / group : -1;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
@@ -547,12 +549,17 @@ struct MfmaTile {
   //    reach 2^kLazyLog2 and the softmax ratio is unchanged; scores() returns
   //    whether some row of the wave outgrew that;
   //  * rescale(): moves those rows' m and rescales their l and O^T;
-  //  * accumulate(): P, l and O^T += V^T . P^T. SPLIT_P: P enters as two bf16
-  //    terms (its rounding and the remainder), about 16 significant bits
-  //    instead of 8, for rows that see so few keys that nothing averages the
-  //    rounding out.
+  //  * probs(): P, packed to bf16; pv(): O^T += V^T . P^T and the row sums.
+  //    SPLIT_P: P enters as two bf16 terms (its rounding and the remainder),
+  //    about 16 significant bits instead of 8, for rows that see so few keys
+  //    that nothing averages the rounding out.
   static constexpr float kLazyLog2 = 8.f;
   float xs[NRB][16], cmax[NRB];
+  // Row sums on the matrix cores: an all-ones block in place of V^T, so each
+  // row's sum is taken over the same bf16 P that multiplies V and the output
+  // is an exact weighted mean of the rounded weights (every element of
+  // lacc[rb] holds the sum of the lane's row).
+  f32x16 lacc[NRB];
 
   // S^T of the current K operand for every row block.
   __device__ __forceinline__ void qk(f32x16* S) const {
@@ -582,12 +589,13 @@ struct MfmaTile {
       for (int i = 0; i < 16; ++i) {
         const int tt = 8 * (i >> 2) + 4 * half + (i & 3);
         if constexpr (MASK)
-          xs[rb][i] = (tok0 + tt <= lim[rb] && tt < nv) ? S[rb][i] * scale_log2 : kNegInf;
+          xs[rb][i] = (tok0 + tt <= lim[rb] && tt < nv) ? S[rb][i] : kNegInf;
         else
-          xs[rb][i] = S[rb][i] * scale_log2;
+          xs[rb][i] = S[rb][i];
         cm = fmaxf(cm, xs[rb][i]);
       }
-      cmax[rb] = fmaxf(cm, shfl_xor(cm, 32));
+      // scale_log2 > 0 here, so scaling commutes with the max
+      cmax[rb] = fmaxf(cm, shfl_xor(cm, 32)) * scale_log2;
       grow |= cmax[rb] > m[rb] + kLazyLog2;
     }
     return __builtin_amdgcn_ballot_w64(grow) != 0;
@@ -605,7 +613,16 @@ struct MfmaTile {
       const bool g = cmax[rb] > m[rb] + kLazyLog2;
       const float alpha = g ? exp2f_fast(m[rb] - cmax[rb]) : 1.f;
       m[rb] = g ? cmax[rb] : m[rb];
-      l[rb] *= alpha;
+      {  // only element 0 of the row sums is read
+        float x = lacc[rb][0], t;
+        asm volatile(
+            "v_accvgpr_read_b32 %1, %0\n\t"
+            "v_mul_f32 %1, %1, %2\n\t"
+            "v_accvgpr_write_b32 %0, %1"
+            : "+a"(x), "=&v"(t)
+            : "v"(alpha));
+        lacc[rb][0] = x;
+      }
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -623,19 +640,34 @@ struct MfmaTile {
     asm volatile("s_nop 3" ::: "memory");
   }
 
-  template <bool SPLIT_P>
-  __device__ __forceinline__ void accumulate() {
-    u32x4 pb[NRB][2], pl[NRB][2];
+  // Whether the current chunk needs P in two bf16 terms: some row of the
+  // wave has a key whose weight, against the row sum so far, exceeds
+  // kSplitWeight. A key's final weight can only be lower than that, so with a
+  // single bf16 P no key weighs more than kSplitWeight when rounded.
+  static constexpr float kSplitWeight = 1.f / 8.f;
+  __device__ __forceinline__ bool needs_split() const {
+    bool any = false;
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
       const float mu = (m[rb] == kNegInf) ? 0.f : m[rb];
-      float p[16], ps = 0.f;
+      float lsum;  // read in place: the row sums stay in the accumulation registers
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3\n\tv_accvgpr_read_b32 %0, %1" : "=v"(lsum) : "a"(lacc[rb][0]));
+      any |= exp2f_fast(cmax[rb] - mu) > kSplitWeight * lsum;
+    }
+    return __builtin_amdgcn_ballot_w64(any) != 0;
+  }
+
+  // P of the current scores, packed to bf16 operand pairs (and the rounding
+  // remainders under SPLIT_P).
+  u32x4 pb[NRB][2], pl[NRB][2];
+  template <bool SPLIT_P>
+  __device__ __forceinline__ void probs(float scale_log2) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        p[i] = exp2f_fast(xs[rb][i] - mu);
-        ps += p[i];
-      }
-      l[rb] += ps;
+    for (int rb = 0; rb < NRB; ++rb) {
+      const float mu = (m[rb] == kNegInf) ? 0.f : m[rb];
+      float p[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) p[i] = exp2f_fast(__builtin_fmaf(xs[rb][i], scale_log2, -mu));
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         u32 h[4];
@@ -651,6 +683,11 @@ struct MfmaTile {
         }
       }
     }
+  }
+
+  // O^T += V^T . P^T and the row sums, from probs() and the current V operand.
+  template <bool SPLIT_P>
+  __device__ __forceinline__ void pv() {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -665,6 +702,19 @@ struct MfmaTile {
                                                                   __builtin_bit_cast(bf16x8, pl[rb][ks]),
                                                                   acc[rb][mb], 0, 0, 0);
         }
+    const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // bf16 1.0 pairs
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) {
+        lacc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ones),
+                                                           __builtin_bit_cast(bf16x8, pb[rb][ks]), lacc[rb], 0, 0,
+                                                           0);
+        if constexpr (SPLIT_P)
+          lacc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ones),
+                                                             __builtin_bit_cast(bf16x8, pl[rb][ks]), lacc[rb], 0,
+                                                             0, 0);
+      }
   }
 
   __device__ __forceinline__ void spill(float* rm, float* rl, float* racc) {
@@ -1076,6 +1126,13 @@ __global__ __launch_bounds__(kPrefillRows) void attn_prefill_kernel(
     s_pages[j] = e;
   }
 
+  // The softmax below takes scale_log2 > 0 (it scales row maxima, not every
+  // score, and masked scores are -inf): a negative scale becomes a positive
+  // one on -q (negating bf16, its sign bits, is exact), and a zero scale is
+  // scale 1 on q = 0 (every visible key weighs the same either way).
+  const u32 qsign = p.scale_log2 < 0.f ? 0x80008000u : 0u;
+  const u32 qkeep = p.scale_log2 == 0.f ? 0u : 0xFFFFFFFFu;
+  const float scale_log2 = p.scale_log2 == 0.f ? 1.f : fabsf(p.scale_log2);
   // q rows of this wave straight into the MFMA operand registers: row r of
   // the tile is window token tq0 + r / group, q head g * group + r % group
   Tile tile;
@@ -1090,7 +1147,10 @@ __global__ __launch_bounds__(kPrefillRows) void attn_prefill_kernel(
       const u32x4* src = reinterpret_cast<const u32x4*>(
           p.q + ((size_t)(q_start + tq0 + (ok ? r / p.group : 0 - tq0)) * p.Hq + g * p.group + r % p.group) * D);
 #pragma unroll
-      for (int kk = 0; kk < Tile::KK; ++kk) tile.qb[rb][kk] = ok ? src[2 * kk + half] : u32x4{0u, 0u, 0u, 0u};
+      for (int kk = 0; kk < Tile::KK; ++kk) {
+        tile.qb[rb][kk] = ok ? src[2 * kk + half] : u32x4{0u, 0u, 0u, 0u};
+        tile.qb[rb][kk] = (tile.qb[rb][kk] & u32x4{qkeep, qkeep, qkeep, qkeep}) ^ u32x4{qsign, qsign, qsign, qsign};
+      }
     }
     // wait for the q operands here: a load still pending at the chunk loop
     // would make the compiler wait for every load in flight (the whole K/V
@@ -1154,34 +1214,47 @@ __global__ __launch_bounds__(kPrefillRows) void attn_prefill_kernel(
   const int wrow = max(r_lo, wave * 64);
   const int wave_min_lim = wrow < r_hi ? seq_len - q_len + tq0 + wrow / p.group : key_end;
   const int n_free = max(n_split, min(key_end / TC, (wave_min_lim + 1) / TC));
+  // Prologue: chunk 0's scores. Iteration c then runs, in one stretch of
+  // straight-line code: chunk c's exponentials beside chunk c + 1's score
+  // products, and chunk c's P.V products beside chunk c + 1's row maxima;
+  // the rare rescale of chunk c + 1 closes it.
   f32x16 S[2];
   arrive(0);
   tile.qk(S);
-  auto run = [&](auto split_p, auto mask, int c0, int c1) {
-    constexpr bool kSplit = decltype(split_p)::value, kMask = decltype(mask)::value;
-    for (int c = c0; c < c1; ++c) {
-      f32x16 Sn[2];
-      const bool more = c + 1 < n_chunks;
-      if (more) arrive(c + 1);
-      tile.fetch_v(slot(c) + G::TILE);
-      tile.qk(Sn);  // past the last chunk this repeats it, unused: no branch between it and the softmax
-      const bool grow = tile.template scores<kMask>(S, c * TC, min(TC, key_end - c * TC), p.scale_log2);
-      // interleave the next chunk's score products with this chunk's softmax
-      // VALU work, one matrix-core op at a time
+  if (tile.template scores<true>(S, 0, min(TC, key_end), scale_log2)) tile.rescale();
+  auto step = [&](auto split_p, auto mask_next, int c) {
+    constexpr bool kSplit = decltype(split_p)::value, kMask = decltype(mask_next)::value;
+    const int cn = c + 1;  // past the last chunk its products repeat chunk c's, unused
+    if (cn < n_chunks) arrive(cn);
+    tile.fetch_v(slot(c) + G::TILE);
+    tile.template probs<kSplit>(scale_log2);
+    tile.qk(S);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
-      }
-      if (grow) tile.rescale();
-      tile.template accumulate<kSplit>();
-      S[0] = Sn[0];
-      S[1] = Sn[1];
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, kSplit ? 7 : 5, 0);
     }
+    tile.template pv<kSplit>();
+    const bool grow = tile.template scores<kMask>(S, cn * TC, min(TC, key_end - cn * TC), scale_log2);
+#pragma unroll
+    for (int i = 0; i < (kSplit ? 36 : 20); ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, kSplit ? 2 : 4, 0);
+    }
+    if (grow && cn < n_chunks) tile.rescale();
   };
-  run(std::true_type{}, std::true_type{}, 0, n_split);
-  run(std::false_type{}, std::false_type{}, n_split, n_free);
-  run(std::false_type{}, std::true_type{}, n_free, n_chunks);
+  // chunk c's P: two bf16 terms for the first 64 keys (rows that see fewer
+  // than 64 keys see nothing else) and wherever a key still weighs more than
+  // 1/32 of its row; chunk c + 1's mask: the unmasked stretch ends one chunk
+  // early so its next chunk is unmasked too
+  const int c_mask = max(n_split, n_free - 1);
+  int c = 0;
+  for (; c < n_split; ++c) step(std::true_type{}, std::true_type{}, c);
+  while (c < n_chunks) {
+    for (; c < c_mask && !tile.needs_split(); ++c) step(std::false_type{}, std::false_type{}, c);
+    for (; c >= c_mask && c < n_chunks && !tile.needs_split(); ++c) step(std::false_type{}, std::true_type{}, c);
+    if (c < n_chunks) step(std::true_type{}, std::true_type{}, c++);
+  }
 
   // rows -> out
   {
@@ -1189,7 +1262,7 @@ __global__ __launch_bounds__(kPrefillRows) void attn_prefill_kernel(
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
       const int r = wave * 64 + rb * 32 + (lane & 31);
-      const float ls = tile.l[rb] + shfl_xor(tile.l[rb], 32);
+      const float ls = tile.lacc[rb][0];
       if (r < r_lo || r >= r_hi) continue;
       float* dst = p.out + ((size_t)(q_start + tq0 + r / p.group) * p.Hq + g * p.group + r % p.group) * D;
 #pragma unroll

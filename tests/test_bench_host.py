@@ -35,3 +35,15 @@ def test_traffic_is_dropped_when_kernel_sources_change(monkeypatch):
     monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0" * 64)
     assert bench.stored_traffic() is None
     assert bench.roofline(268435456, 0.0625)["traffic"] is None
+
+
+def test_prefill_flops_count_visible_keys_only():
+    """Whole-prompt window of 10 tokens: rows see 1..10 keys (55 in all);
+    a 5-token chunk over 15 cached tokens: rows see 16..20 keys (90)."""
+    from workloads import AttnCase
+    import numpy as np
+    q = np.zeros((15, 2, 4), np.uint16)
+    pool = np.zeros((1, 1, 256, 4), np.uint16)
+    case = AttnCase("t", q, pool, pool, np.zeros((2, 1), np.int32), np.array([10, 20], np.int32),
+                    np.array([10, 5], np.int32), 0.5)
+    assert bench.prefill_flops(case) == (55 + 90) * 2 * 4 * 4

@@ -73,6 +73,20 @@ def test_long_windows_match_the_oracle(pk, i):
     assert_close(got, oracle_attn(case), f"prefill {i}")
 
 
+@pytest.mark.parametrize("scale", [-0.09, 0.0, 0.3, 0.5])
+def test_any_finite_scale(pk, scale):
+    """The long-window softmax runs on a positive scale (a negative one is
+    applied to -q); zero gives the plain mean of the visible values. Scales
+    0.3 and 0.5 on head_dim 64 (2.4x and 4x the usual 1/sqrt(64)) make rows
+    peaky, where a few keys carry most of the weight and bf16 rounding of
+    their P would not average out."""
+    say(f"prefill scale {scale}")
+    case = make_tiny_case(340, [400, 150], [200, 150], Hq=8, Hkv=2, D=64, scale=scale)
+    got, flags = attn_gpu(case, pk)
+    assert flags == 0
+    assert_close(got, oracle_attn(case), f"prefill scale {scale}")
+
+
 def test_layout_invariance_and_repeat_are_bit_exact(pk):
     say("prefill: permuted pool and repeated calls, bit-exact")
     case = make_tiny_case(320, [900, 600, 300], [900, 300, 70], Hq=8, Hkv=2, D=128, table_width=6)
