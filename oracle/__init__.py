@@ -17,6 +17,10 @@ What it computes is the plain definition, in float64:
 * ``kv_cache.append`` / ``.rollback`` -- writing a verify window's K/V into
   the pages (popping new pages from a free stack) and, after the accept,
   keeping the accepted prefix and releasing the pages past it.
+* ``page_pool.PagePool`` -- the page allocator: reference counts, prefix
+  reuse at admission, prompt caching with least-recently-released eviction,
+  and defragmentation; ``page_pool.copy_pages`` / ``.remap_table`` for the
+  data movement a defragmentation plans.
 * ``brute`` -- an independent pure-Python loop version of the attention, per
   token and per element, used to pin ``paged_attention`` on tiny inputs.
 
@@ -30,6 +34,7 @@ checks.
 from .paged_attention import decode_bf16, gather_sequence, attention, attention_rows
 from .greedy_accept import argmax_rows, accept, window_next
 from . import kv_cache
+from . import page_pool
 
 __all__ = ["decode_bf16", "gather_sequence", "attention", "attention_rows",
-           "argmax_rows", "accept", "window_next", "kv_cache"]
+           "argmax_rows", "accept", "window_next", "kv_cache", "page_pool"]
