@@ -266,6 +266,44 @@ def prefill_leg(torch, pk, seed, steps, warmup):
     return out
 
 
+def pool_leg(torch, pk, steps, warmup):
+    """The page allocator: host admissions of the prefix-dedup job mix (100
+    prompts of a shared 4096-token prefix plus a private tail of 1..256
+    tokens into a 256-page pool: page lookups by prefix, reference counts),
+    and the device side of a defragmentation, page copies of the verify
+    configuration's pools (8 KV heads x 256 x 128, K and V: 1 MiB a page),
+    timed on 128 disjoint moves."""
+    rng = np.random.default_rng(4)
+    prefix = rng.integers(0, 128000, 4096).tolist()
+    prompts = [prefix + rng.integers(0, 128000, int(rng.integers(1, 257))).tolist() for _ in range(100)]
+    tokens = sum(len(p) for p in prompts)
+    reps = 5
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        pool = pk.pkv_pool_create(256)
+        held = [pk.pkv_pool_admit(pool, p)[0] for p in prompts]
+        for pages in held:
+            pk.pkv_pool_release(pool, pages)
+        pk.pkv_pool_destroy(pool)
+    host_s = (time.perf_counter() - t0) / reps
+    P, Hkv, D, n = 256, 8, 128, 128
+    k = torch.empty((P, Hkv, 256, D), dtype=torch.bfloat16, device="cuda").normal_()
+    v = torch.empty_like(k).normal_()
+    src = torch.arange(P - n, P, dtype=torch.int32, device="cuda")
+    dst = torch.arange(0, n, dtype=torch.int32, device="cuda")
+    ms = time_ms(torch, lambda i: pk.pkv_pool_copy_pages(k, v, src, dst), steps, warmup)
+    moved = n * 2 * Hkv * 256 * D * 2
+    gbps = 2 * moved / (ms * 1e-3) / 1e9
+    del k, v
+    torch.cuda.empty_cache()
+    return {"admit_release_us_per_job": round(host_s / len(prompts) * 1e6, 2),
+            "host_tokens_per_s": round(tokens / host_s, 1),
+            "copy_pages_us": round(ms * 1e3, 2), "bytes_moved": moved,
+            "copy_gbps": round(gbps, 1), "copy_hbm_fraction": round(gbps / HBM_PEAK_GBPS, 4),
+            "note": "host: admit + release per job of the dedup mix (every job after the first reuses the "
+                    "16 prefix pages); device: 128 page moves, traffic = 2 x bytes moved"}
+
+
 def cpu_baseline(case, acc, seconds):
     """The CPU oracle on the verify step: whole sequences (attention over
     their cached tokens + accept over their logits rows) in order, passes
@@ -439,6 +477,8 @@ def main():
 
     if not args.no_prefill:
         result["prefill"] = prefill_leg(torch, pk, args.seed, max(5, args.steps // 5), max(2, args.warmup // 2))
+    log("page allocator")
+    result["pool"] = pool_leg(torch, pk, args.steps, args.warmup)
 
     if not args.no_cpu_baseline:
         log("CPU oracle sample")

@@ -49,7 +49,10 @@ typedef enum {
   PKV_ERR_NULL = -1,      /* a required pointer is NULL                         */
   PKV_ERR_SHAPE = -2,     /* a shape field is out of range (see each call)      */
   PKV_ERR_WORKSPACE = -3, /* workspace NULL or smaller than the queried size    */
-  PKV_ERR_HIP = -4        /* a HIP launch or runtime call failed                */
+  PKV_ERR_HIP = -4,       /* a HIP launch or runtime call failed                */
+  PKV_ERR_SPACE = -5,     /* page allocator: not enough pages (nothing changed) */
+  PKV_ERR_STATE = -6      /* page allocator: a page is not in the state the call
+                             needs, e.g. released more often than referenced    */
 } pkv_status;
 
 /* Error-word bits a kernel sets when a device array breaks its contract. */
@@ -248,6 +251,104 @@ int pkv_kv_rollback(int32_t* block_table, int32_t* seq_lens, const int32_t* q_le
 /* Synchronise `stream`, copy the error word of a cache workspace into *flags
  * and clear it. */
 int pkv_kv_check_errors(void* workspace, void* stream, uint32_t* flags);
+
+/* ------------------------------------------------------------ page allocator */
+
+/*
+ * Sources: ExLlamaV2 "Dynamic Generator" page, "Continuous Batching" (a job
+ * queue starts jobs while their pages fit; a finished job frees its pages; the
+ * holes are filled by later jobs; unreferenced pages are defragmented when the
+ * queue is empty), "Deduplication" (a new job references the K/V already cached
+ * for its prompt prefix) and "Prompt caching" (the most recently used pages are
+ * the last to be overwritten, so a later job sharing a prefix with a finished
+ * one still finds it).
+ *
+ * pkv_pool is a host object (created and freed by the calls below; the only
+ * memory this library allocates itself) that decides which page holds what;
+ * it never touches device memory. Block tables and free stacks built from its
+ * answers are the caller's to upload. Every page is FREE (holds nothing
+ * reusable), CACHED (unreferenced, holds a full prompt page a later job may
+ * reuse) or USED (referenced by block-table rows or free stacks the caller
+ * keeps; the reference count is the number of holders).
+ *
+ * A full prompt page is found again by its prefix, every token id up to the
+ * end of the page; the index keys it by a 64-bit FNV-1a hash chained over the
+ * prompt's pages and confirms a hit against the page's own 256 tokens,
+ * position and chain predecessor. New pages come from FREE pages, lowest index
+ * first (filling holes), then by evicting the CACHED page released longest ago
+ * (lowest index on ties), which forgets its prefix.
+ * Calls on one pool must not overlap; different pools are independent.
+ */
+typedef struct pkv_pool pkv_pool;
+
+/* A pool of num_pages pages (1 .. 2^23), all FREE; NULL on a bad size or when
+ * host memory runs out. */
+pkv_pool* pkv_pool_create(int32_t num_pages);
+void pkv_pool_destroy(pkv_pool* pool);
+
+/* out[0..2] = FREE, CACHED and USED page counts. */
+int pkv_pool_stats(const pkv_pool* pool, int32_t* out);
+
+/*
+ * Pages for a job's prompt (tokens[0 .. n_tokens)): pages[0 .. *n_pages) in
+ * table order, *n_pages = ceil(n_tokens / 256) <= max_pages. The prompt's full
+ * pages are matched against the cache from the start until the first miss; a
+ * page is matched only if at least one prompt token follows it, so the job
+ * always has a token to prefill and never writes into a shared page. Matched
+ * pages gain a reference (CACHED ones are revived); the rest are new USED
+ * pages, and the new full ones are keyed by their prefix. *cached_tokens =
+ * 256 x matched pages: the prefill starts there (its K/V is already in the
+ * pages). All or nothing: PKV_ERR_SPACE when too few pages can be had.
+ */
+int pkv_pool_admit(pkv_pool* pool, const int32_t* tokens, int32_t n_tokens, int32_t* pages,
+                   int32_t max_pages, int32_t* n_pages, int32_t* cached_tokens);
+
+/* n new private USED pages (reference count 1, no prefix), e.g. to fill the
+ * device free stack pkv_kv_append pops from. PKV_ERR_SPACE if too few. */
+int pkv_pool_alloc(pkv_pool* pool, int32_t n, int32_t* pages);
+
+/* One more reference on each USED page (a page may repeat): sharing a job's
+ * pages with another holder. PKV_ERR_STATE (nothing changed) if one is not USED. */
+int pkv_pool_retain(pkv_pool* pool, const int32_t* pages, int32_t n);
+
+/* One reference fewer on each page (a page may repeat): a finished job's
+ * table pages, or unused free-stack pages. At zero a keyed page becomes
+ * CACHED, any other FREE. PKV_ERR_STATE (nothing changed) if a page would go
+ * below zero. */
+int pkv_pool_release(pkv_pool* pool, const int32_t* pages, int32_t n);
+
+/*
+ * Defragmentation plan. n_occ = pages not FREE. Movable pages (CACHED; also
+ * USED when move_referenced != 0) at index >= n_occ move into the FREE pages
+ * below n_occ, both in ascending order, so that every target is FREE and no
+ * target is another move's source. With move_referenced every occupied page
+ * ends up below n_occ. Writes remap[0 .. P) (old index -> new; identity except
+ * moved pages), src/dst[0 .. *n_moves) (capacity P each), and updates the
+ * pool. The caller then moves the contents (pkv_pool_copy_pages) and, for
+ * moved USED pages, rewrites its block tables (pkv_table_remap) before using
+ * them again. The generator does this only when its queue is empty.
+ */
+int pkv_pool_defrag(pkv_pool* pool, int32_t move_referenced, int32_t* remap, int32_t* src, int32_t* dst,
+                    int32_t* n_moves);
+
+/*
+ * Device side of a defragmentation (or any page move): copy page src[i] of
+ * both pools to page dst[i], every KV head, for i < n_moves.
+ * k_pool, v_pool bf16 [P, Hkv, 256, D]; src, dst int32 device arrays [n_moves].
+ * Contract: entries in [0, P); no page is both a source and a target; targets
+ * distinct (pkv_pool_defrag's plans are). Moves with an entry outside [0, P)
+ * are skipped and set PKV_EFLAG_PAGE in *err (a caller-owned device word,
+ * may be NULL).
+ */
+int pkv_pool_copy_pages(void* k_pool, void* v_pool, const int32_t* src, const int32_t* dst, int32_t n_moves,
+                        int32_t num_pages, int32_t num_kv_heads, int32_t head_dim, uint32_t* err, void* stream);
+
+/* Rewrite block_table[rows, width] in place: every entry t in [0, num_pages)
+ * becomes remap[t] (remap: device int32 [num_pages], entries in [0,
+ * num_pages)); negative entries stay; entries >= num_pages stay and set
+ * PKV_EFLAG_PAGE in *err (device word, may be NULL). */
+int pkv_table_remap(int32_t* block_table, int32_t rows, int32_t width, const int32_t* remap,
+                    int32_t num_pages, uint32_t* err, void* stream);
 
 /* ---------------------------------------------------------------------- misc */
 

@@ -1,5 +1,6 @@
-"""pkv: paged K/V attention, greedy speculative accept, and the cache append /
-rollback around them, for AMD MI355X.
+"""pkv: paged K/V attention (decode, verify and prefill windows), greedy
+speculative accept, the cache append / rollback around them, and the page
+allocator, for AMD MI355X.
 
 The compute lives in libpkv.so (hand-written HIP for gfx950, C ABI in
 include/pkv.h). This package is its thin Python binding; importing it loads
@@ -15,4 +16,6 @@ from ._lib import (  # noqa: F401
     pkv_attn_check_errors, pkv_accept_workspace_bytes, new_accept_workspace, pkv_accept,
     pkv_window_next, pkv_status_string, pkv_version, pkv_kv_shape, kv_shape, pkv_kv_workspace_bytes,
     new_kv_workspace, pkv_kv_append, pkv_kv_rollback, pkv_kv_check_errors,
+    PKV_ERR_SPACE, PKV_ERR_STATE, pkv_pool_create, pkv_pool_destroy, pkv_pool_stats, pkv_pool_admit,
+    pkv_pool_alloc, pkv_pool_retain, pkv_pool_release, pkv_pool_defrag, pkv_pool_copy_pages, pkv_table_remap,
 )

@@ -19,12 +19,15 @@ PKV_PAGE_SIZE = 256
 PKV_MAX_Q_LEN = 16
 PKV_MAX_ROWS = 64
 PKV_OK, PKV_ERR_NULL, PKV_ERR_SHAPE, PKV_ERR_WORKSPACE, PKV_ERR_HIP = 0, -1, -2, -3, -4
+PKV_ERR_SPACE, PKV_ERR_STATE = -5, -6
 PKV_EFLAG_PAGE, PKV_EFLAG_QLEN, PKV_EFLAG_ROWS, PKV_EFLAG_SPACE = 1, 2, 4, 8
 
 EXPORTS = ("pkv_attn_workspace_bytes", "pkv_attn_workspace_init", "pkv_attn_fwd",
            "pkv_attn_check_errors", "pkv_accept_workspace_bytes", "pkv_accept",
            "pkv_window_next", "pkv_status_string", "pkv_version", "pkv_kv_workspace_bytes",
-           "pkv_kv_append", "pkv_kv_rollback", "pkv_kv_check_errors")
+           "pkv_kv_append", "pkv_kv_rollback", "pkv_kv_check_errors", "pkv_pool_create",
+           "pkv_pool_destroy", "pkv_pool_stats", "pkv_pool_admit", "pkv_pool_alloc", "pkv_pool_retain",
+           "pkv_pool_release", "pkv_pool_defrag", "pkv_pool_copy_pages", "pkv_table_remap")
 
 
 class pkv_attn_shape(ctypes.Structure):
@@ -84,6 +87,22 @@ def _load():
     lib.pkv_kv_rollback.restype = ctypes.c_int
     lib.pkv_kv_check_errors.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_uint32)]
     lib.pkv_kv_check_errors.restype = ctypes.c_int
+    i32 = ctypes.c_int32
+    lib.pkv_pool_create.argtypes = [i32]
+    lib.pkv_pool_create.restype = vp
+    lib.pkv_pool_destroy.argtypes = [vp]
+    lib.pkv_pool_destroy.restype = None
+    lib.pkv_pool_stats.argtypes = [vp, vp]
+    lib.pkv_pool_admit.argtypes = [vp, vp, i32, vp, i32, vp, vp]
+    lib.pkv_pool_alloc.argtypes = [vp, i32, vp]
+    lib.pkv_pool_retain.argtypes = [vp, vp, i32]
+    lib.pkv_pool_release.argtypes = [vp, vp, i32]
+    lib.pkv_pool_defrag.argtypes = [vp, i32, vp, vp, vp, vp]
+    lib.pkv_pool_copy_pages.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, vp, vp]
+    lib.pkv_table_remap.argtypes = [vp, i32, i32, vp, i32, vp, vp]
+    for name in ("pkv_pool_stats", "pkv_pool_admit", "pkv_pool_alloc", "pkv_pool_retain", "pkv_pool_release",
+                 "pkv_pool_defrag", "pkv_pool_copy_pages", "pkv_table_remap"):
+        getattr(lib, name).restype = ctypes.c_int
     return lib
 
 
@@ -261,3 +280,84 @@ def pkv_kv_check_errors(workspace, stream=None):
     _check(LIB.pkv_kv_check_errors(_ptr(workspace), _stream(stream), ctypes.byref(flags)),
            "pkv_kv_check_errors")
     return int(flags.value)
+
+
+# ------------------------------------------------------------ page allocator
+# Host object; these calls never touch the GPU. Page lists are Python ints.
+
+def _i32_array(values):
+    arr = (ctypes.c_int32 * max(1, len(values)))(*values)
+    return arr
+
+
+def pkv_pool_create(num_pages):
+    h = LIB.pkv_pool_create(int(num_pages))
+    if not h:
+        raise PkvError("pkv_pool_create: bad size or out of host memory")
+    return ctypes.c_void_p(h)
+
+
+def pkv_pool_destroy(pool):
+    LIB.pkv_pool_destroy(pool)
+
+
+def pkv_pool_stats(pool):
+    out = (ctypes.c_int32 * 3)()
+    _check(LIB.pkv_pool_stats(pool, out), "pkv_pool_stats")
+    return tuple(out)
+
+
+def pkv_pool_admit(pool, tokens, max_pages=None):
+    """(pages in table order, cached tokens) for a prompt."""
+    toks = [int(t) for t in tokens]
+    cap = max_pages if max_pages is not None else -(-len(toks) // PKV_PAGE_SIZE)
+    pages = (ctypes.c_int32 * max(1, cap))()
+    n, cached = ctypes.c_int32(0), ctypes.c_int32(0)
+    rc = LIB.pkv_pool_admit(pool, _i32_array(toks), len(toks), pages, cap, ctypes.byref(n), ctypes.byref(cached))
+    _check(rc, "pkv_pool_admit")
+    return list(pages[:n.value]), cached.value
+
+
+def pkv_pool_alloc(pool, n):
+    pages = (ctypes.c_int32 * max(1, n))()
+    _check(LIB.pkv_pool_alloc(pool, int(n), pages), "pkv_pool_alloc")
+    return list(pages[:n])
+
+
+def pkv_pool_retain(pool, pages):
+    _check(LIB.pkv_pool_retain(pool, _i32_array(pages), len(pages)), "pkv_pool_retain")
+
+
+def pkv_pool_release(pool, pages):
+    _check(LIB.pkv_pool_release(pool, _i32_array(pages), len(pages)), "pkv_pool_release")
+
+
+def pkv_pool_defrag(pool, num_pages, move_referenced=False):
+    """(remap list of num_pages entries, [(src, dst), ...])."""
+    remap = (ctypes.c_int32 * num_pages)()
+    src = (ctypes.c_int32 * num_pages)()
+    dst = (ctypes.c_int32 * num_pages)()
+    n = ctypes.c_int32(0)
+    _check(LIB.pkv_pool_defrag(pool, int(bool(move_referenced)), remap, src, dst, ctypes.byref(n)),
+           "pkv_pool_defrag")
+    return list(remap), list(zip(src[:n.value], dst[:n.value]))
+
+
+def pkv_pool_copy_pages(k_pool, v_pool, src, dst, err=None, stream=None):
+    """k_pool, v_pool: bf16 [P, Hkv, 256, D]; src, dst: int32 device tensors."""
+    for t, dt, n in ((k_pool, torch.bfloat16, "k_pool"), (v_pool, torch.bfloat16, "v_pool"),
+                     (src, torch.int32, "src"), (dst, torch.int32, "dst")):
+        _need(t, dt, n)
+    P, Hkv, page, D = k_pool.shape
+    rc = LIB.pkv_pool_copy_pages(_ptr(k_pool), _ptr(v_pool), _ptr(src), _ptr(dst), src.numel(), P, Hkv, D,
+                                 _ptr(err), _stream(stream))
+    _check(rc, "pkv_pool_copy_pages")
+
+
+def pkv_table_remap(block_table, remap, err=None, stream=None):
+    """block_table int32 [B, W] rewritten in place; remap int32 [P] (device)."""
+    _need(block_table, torch.int32, "block_table")
+    _need(remap, torch.int32, "remap")
+    B, W = block_table.shape
+    rc = LIB.pkv_table_remap(_ptr(block_table), B, W, _ptr(remap), remap.numel(), _ptr(err), _stream(stream))
+    _check(rc, "pkv_table_remap")

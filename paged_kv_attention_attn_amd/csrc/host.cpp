@@ -233,6 +233,37 @@ int32_t pkv_window_next(int32_t window, int32_t n_draft, int32_t accepted) {
   return window - 1 < 1 ? 1 : window - 1;
 }
 
+int pkv_pool_copy_pages(void* k_pool, void* v_pool, const int32_t* src, const int32_t* dst, int32_t n_moves,
+                        int32_t num_pages, int32_t num_kv_heads, int32_t head_dim, uint32_t* err, void* stream) {
+  if (n_moves < 0 || num_pages < 1 || num_kv_heads < 1 || (head_dim != 64 && head_dim != 128))
+    return PKV_ERR_SHAPE;
+  if (n_moves == 0) return PKV_OK;
+  if (!k_pool || !v_pool || !src || !dst) return PKV_ERR_NULL;
+  if ((long)num_pages * num_kv_heads * PKV_PAGE_SIZE * head_dim > (1L << 40)) return PKV_ERR_SHAPE;
+  pkv::PageMoveParams p{};
+  p.k_pool = static_cast<uint16_t*>(k_pool);
+  p.v_pool = static_cast<uint16_t*>(v_pool);
+  p.src = src;
+  p.dst = dst;
+  p.err = err;
+  p.n_moves = n_moves;
+  p.P = num_pages;
+  p.page_bytes = static_cast<long>(num_kv_heads) * PKV_PAGE_SIZE * head_dim * 2;
+  if (pkv::launch_copy_pages(p, static_cast<hipStream_t>(stream)) != hipSuccess) return PKV_ERR_HIP;
+  return PKV_OK;
+}
+
+int pkv_table_remap(int32_t* block_table, int32_t rows, int32_t width, const int32_t* remap, int32_t num_pages,
+                    uint32_t* err, void* stream) {
+  if (rows < 0 || width < 1 || num_pages < 1 || (long)rows * width > (1L << 31) - 1) return PKV_ERR_SHAPE;
+  if (rows == 0) return PKV_OK;
+  if (!block_table || !remap) return PKV_ERR_NULL;
+  if (pkv::launch_table_remap(block_table, rows * width, remap, num_pages, err, static_cast<hipStream_t>(stream)) !=
+      hipSuccess)
+    return PKV_ERR_HIP;
+  return PKV_OK;
+}
+
 const char* pkv_status_string(int status) {
   switch (status) {
     case PKV_OK: return "ok";
@@ -240,6 +271,8 @@ const char* pkv_status_string(int status) {
     case PKV_ERR_SHAPE: return "shape field out of range";
     case PKV_ERR_WORKSPACE: return "workspace missing or too small";
     case PKV_ERR_HIP: return "HIP launch or runtime call failed";
+    case PKV_ERR_SPACE: return "not enough pages";
+    case PKV_ERR_STATE: return "a page is not in the state the call needs";
     default: return "unknown status";
   }
 }

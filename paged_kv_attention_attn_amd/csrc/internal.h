@@ -90,6 +90,20 @@ KvWorkspace kv_workspace(int total_q);
 hipError_t launch_kv_append(const KvParams& p, hipStream_t stream);
 hipError_t launch_kv_rollback(const KvParams& p, hipStream_t stream);
 
+struct PageMoveParams {
+  uint16_t* k_pool;          // [P, Hkv, 256, D]
+  uint16_t* v_pool;
+  const int32_t* src;        // [n_moves]
+  const int32_t* dst;
+  uint32_t* err;             // nullable
+  int32_t n_moves, P;
+  long page_bytes;           // bytes of one page of one pool (all KV heads)
+};
+
+hipError_t launch_copy_pages(const PageMoveParams& p, hipStream_t stream);
+hipError_t launch_table_remap(int32_t* table, int32_t n, const int32_t* remap, int32_t P, uint32_t* err,
+                              hipStream_t stream);
+
 AcceptWorkspace accept_workspace(int B, int total_rows, int V);
 hipError_t launch_accept(const AcceptParams& p, hipStream_t stream);
 
