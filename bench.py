@@ -275,7 +275,8 @@ def pool_leg(torch, pk, steps, warmup):
     timed on 128 disjoint moves."""
     rng = np.random.default_rng(4)
     prefix = rng.integers(0, 128000, 4096).tolist()
-    prompts = [prefix + rng.integers(0, 128000, int(rng.integers(1, 257))).tolist() for _ in range(100)]
+    prompts = [np.array(prefix + rng.integers(0, 128000, int(rng.integers(1, 257))).tolist(), np.int32)
+               for _ in range(100)]
     tokens = sum(len(p) for p in prompts)
     reps = 5
     t0 = time.perf_counter()

@@ -10,6 +10,7 @@ the binding raises.
 import ctypes
 import os
 
+import numpy as np
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -308,12 +309,14 @@ def pkv_pool_stats(pool):
 
 
 def pkv_pool_admit(pool, tokens, max_pages=None):
-    """(pages in table order, cached tokens) for a prompt."""
-    toks = [int(t) for t in tokens]
-    cap = max_pages if max_pages is not None else -(-len(toks) // PKV_PAGE_SIZE)
+    """(pages in table order, cached tokens) for a prompt (token ids: any
+    int sequence or array)."""
+    toks = np.ascontiguousarray(tokens, dtype=np.int32)
+    cap = max_pages if max_pages is not None else -(-toks.size // PKV_PAGE_SIZE)
     pages = (ctypes.c_int32 * max(1, cap))()
     n, cached = ctypes.c_int32(0), ctypes.c_int32(0)
-    rc = LIB.pkv_pool_admit(pool, _i32_array(toks), len(toks), pages, cap, ctypes.byref(n), ctypes.byref(cached))
+    rc = LIB.pkv_pool_admit(pool, toks.ctypes.data_as(ctypes.c_void_p), toks.size, pages, cap, ctypes.byref(n),
+                            ctypes.byref(cached))
     _check(rc, "pkv_pool_admit")
     return list(pages[:n.value]), cached.value
 

@@ -7,9 +7,10 @@
 // queue is empty); a batch changes by rewriting block indices only.
 //
 // A page of one pool is Hkv * 256 * D bf16 values, contiguous. The copy grid
-// is (block, pool, move), flattened: every workgroup moves one 32 KiB block of
+// is (block, pool, move), flattened: every workgroup moves one 64 KiB block of
 // one page of one pool, each thread issuing all its 16-byte loads before any store, so
-// a move is 2 * page_bytes / 32 KiB independent workgroups. The HBM roofline is
+// a move is 2 * page_bytes / 64 KiB independent workgroups (plain loads: a
+// non-temporal hint halved the rate). The HBM roofline is
 // 2 bytes of traffic (one read, one write) per byte moved.
 
 #include "internal.h"
@@ -23,8 +24,8 @@ using u32 = uint32_t;
 typedef u32 u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kCopyThreads = 256;
-constexpr int kPerThread = 8;                                // 16-byte pieces per thread
-constexpr long kBlockBytes = kCopyThreads * kPerThread * 16;  // 32 KiB
+constexpr int kPerThread = 16;                               // 16-byte pieces per thread
+constexpr long kBlockBytes = kCopyThreads * kPerThread * 16;  // 64 KiB
 
 __global__ __launch_bounds__(kCopyThreads) void copy_pages_kernel(PageMoveParams p, int blocks) {
   // workgroup -> (block of the page, pool, move), block fastest
@@ -45,7 +46,7 @@ __global__ __launch_bounds__(kCopyThreads) void copy_pages_kernel(PageMoveParams
 #pragma unroll
   for (int i = 0; i < kPerThread; ++i) {
     const long e = (long)i * kCopyThreads + threadIdx.x;
-    if (e < n16) v[i] = __builtin_nontemporal_load(from + e);
+    if (e < n16) v[i] = from[e];
   }
 #pragma unroll
   for (int i = 0; i < kPerThread; ++i) {
