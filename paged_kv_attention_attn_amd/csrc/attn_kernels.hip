@@ -592,6 +592,9 @@ struct MfmaTile {
           xs[rb][i] = (tok0 + tt <= lim[rb] && tt < nv) ? S[rb][i] : kNegInf;
         else
           xs[rb][i] = S[rb][i];
+        // one read out of the accumulation registers serves the max here and
+        // the exponentials of the next step
+        asm volatile("" : "+v"(xs[rb][i]));
         cm = fmaxf(cm, xs[rb][i]);
       }
       // scale_log2 > 0 here, so scaling commutes with the max
@@ -613,16 +616,7 @@ struct MfmaTile {
       const bool g = cmax[rb] > m[rb] + kLazyLog2;
       const float alpha = g ? exp2f_fast(m[rb] - cmax[rb]) : 1.f;
       m[rb] = g ? cmax[rb] : m[rb];
-      {  // only element 0 of the row sums is read
-        float x = lacc[rb][0], t;
-        asm volatile(
-            "v_accvgpr_read_b32 %1, %0\n\t"
-            "v_mul_f32 %1, %1, %2\n\t"
-            "v_accvgpr_write_b32 %0, %1"
-            : "+a"(x), "=&v"(t)
-            : "v"(alpha));
-        lacc[rb][0] = x;
-      }
+      lacc[rb] *= alpha;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -650,9 +644,7 @@ struct MfmaTile {
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
       const float mu = (m[rb] == kNegInf) ? 0.f : m[rb];
-      float lsum;  // read in place: the row sums stay in the accumulation registers
-      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3\n\tv_accvgpr_read_b32 %0, %1" : "=v"(lsum) : "a"(lacc[rb][0]));
-      any |= exp2f_fast(cmax[rb] - mu) > kSplitWeight * lsum;
+      any |= exp2f_fast(cmax[rb] - mu) > kSplitWeight * lacc[rb][0];
     }
     return __builtin_amdgcn_ballot_w64(any) != 0;
   }
