@@ -160,3 +160,35 @@ def test_cache_calls_check_pointers_and_workspace(pk):
     assert pk.LIB.pkv_kv_rollback(d, d, d, None, d, d, ctypes.byref(s), d, need, None) == pk.PKV_ERR_NULL
     empty = pk.pkv_kv_shape(0, 8, 128, 256, 256, 32, 0)
     assert pk.LIB.pkv_kv_append(*([None] * 9), ctypes.byref(empty), None, 0, None) == pk.PKV_OK
+
+
+def test_page_move_calls_check_shapes_and_pointers_before_any_launch(pk):
+    d = ctypes.c_void_p(0x1000)
+    L = pk.LIB
+    assert L.pkv_pool_copy_pages(d, d, d, d, -1, 8, 2, 64, None, None) == pk.PKV_ERR_SHAPE
+    assert L.pkv_pool_copy_pages(d, d, d, d, 1, 8, 2, 96, None, None) == pk.PKV_ERR_SHAPE
+    assert L.pkv_pool_copy_pages(d, d, d, d, 1, 0, 2, 64, None, None) == pk.PKV_ERR_SHAPE
+    assert L.pkv_pool_copy_pages(None, d, d, d, 1, 8, 2, 64, None, None) == pk.PKV_ERR_NULL
+    assert L.pkv_pool_copy_pages(None, None, None, None, 0, 8, 2, 64, None, None) == pk.PKV_OK
+    assert L.pkv_table_remap(d, -1, 4, d, 8, None, None) == pk.PKV_ERR_SHAPE
+    assert L.pkv_table_remap(d, 2, 0, d, 8, None, None) == pk.PKV_ERR_SHAPE
+    assert L.pkv_table_remap(None, 2, 4, d, 8, None, None) == pk.PKV_ERR_NULL
+    assert L.pkv_table_remap(None, 0, 4, None, 8, None, None) == pk.PKV_OK
+
+
+def test_allocator_calls_reject_null_and_bad_sizes(pk):
+    L = pk.LIB
+    assert L.pkv_pool_create(0) is None and L.pkv_pool_create(-5) is None
+    assert L.pkv_pool_create((1 << 23) + 1) is None
+    out = (ctypes.c_int32 * 4)()
+    assert L.pkv_pool_admit(None, None, 0, out, 1, out, out) == pk.PKV_ERR_NULL
+    assert L.pkv_pool_alloc(None, 1, out) == pk.PKV_ERR_NULL
+    assert L.pkv_pool_release(None, out, 1) == pk.PKV_ERR_NULL
+    assert L.pkv_pool_defrag(None, 0, out, out, out, out) == pk.PKV_ERR_NULL
+    pool = pk.pkv_pool_create(4)
+    try:
+        assert L.pkv_pool_alloc(pool, -1, out) == pk.PKV_ERR_SHAPE
+        assert L.pkv_pool_release(pool, out, -1) == pk.PKV_ERR_SHAPE
+        assert pk.pkv_status_string(pk.PKV_ERR_SPACE) and pk.pkv_status_string(pk.PKV_ERR_STATE)
+    finally:
+        pk.pkv_pool_destroy(pool)
