@@ -1,6 +1,8 @@
 """Build libpkv.so in-tree with hipcc for gfx950.
 
-    python -m paged_kv_attention_attn_amd.build
+    python paged_kv_attention_attn_amd/build.py
+
+(run it as a file: importing the package loads the library it builds).
 
 Every HIP translation unit is compiled with packed-FP32 instructions switched
 off; host-side warnings about that target feature are expected.
