@@ -130,6 +130,29 @@ int pkv_attn_fwd(const void* q, const void* k_pool, const void* v_pool,
                  float* out, const pkv_attn_shape* shape,
                  void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Decode / verify (max_q_len * Hq/Hkv <= PKV_MAX_ROWS) over a batch whose
+ * sequences all begin with the same shared_pages pages: a deduplicated prompt
+ * prefix (Dynamic Generator page, "Deduplication": every job references the
+ * same cached pages). Same arguments, layouts and result as pkv_attn_fwd; the
+ * shared keys are attended to once per KV head for all window rows of the
+ * batch (matrix cores, rows of every sequence stacked), the rest of every
+ * sequence as in pkv_attn_fwd, and the two are merged by log-sum-exp.
+ * shared_pages = 0 is pkv_attn_fwd. Workspace: pkv_attn_shared_workspace_bytes
+ * (zero-filled before its first use, like pkv_attn_fwd's; every call leaves
+ * it ready for the next).
+ * Contract, besides pkv_attn_fwd's: block_table[b][j] == block_table[0][j] for
+ * j < shared_pages, and seq_len - q_len >= shared_pages * 256 (every window
+ * row sees the whole shared prefix), for every sequence with q_len > 0;
+ * 1 <= shared_pages < max_pages_per_seq. A sequence breaking it gets undefined
+ * rows, and PKV_EFLAG_PAGE / PKV_EFLAG_QLEN is set.
+ */
+size_t pkv_attn_shared_workspace_bytes(const pkv_attn_shape* shape, int32_t shared_pages);
+int pkv_attn_fwd_shared(const void* q, const void* k_pool, const void* v_pool,
+                        const int32_t* block_table, const int32_t* seq_lens, const int32_t* q_lens,
+                        float* out, const pkv_attn_shape* shape, int32_t shared_pages,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
 /* Synchronise `stream`, copy the error word of `workspace` into *flags
  * (PKV_EFLAG_* bits; 0 = every contract held) and clear it. */
 int pkv_attn_check_errors(void* workspace, void* stream, uint32_t* flags);

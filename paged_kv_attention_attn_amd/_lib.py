@@ -28,7 +28,8 @@ EXPORTS = ("pkv_attn_workspace_bytes", "pkv_attn_workspace_init", "pkv_attn_fwd"
            "pkv_window_next", "pkv_status_string", "pkv_version", "pkv_kv_workspace_bytes",
            "pkv_kv_append", "pkv_kv_rollback", "pkv_kv_check_errors", "pkv_pool_create",
            "pkv_pool_destroy", "pkv_pool_stats", "pkv_pool_admit", "pkv_pool_alloc", "pkv_pool_retain",
-           "pkv_pool_release", "pkv_pool_defrag", "pkv_pool_copy_pages", "pkv_table_remap")
+           "pkv_pool_release", "pkv_pool_defrag", "pkv_pool_copy_pages", "pkv_table_remap",
+           "pkv_attn_shared_workspace_bytes", "pkv_attn_fwd_shared")
 
 
 class pkv_attn_shape(ctypes.Structure):
@@ -58,7 +59,7 @@ class PkvError(RuntimeError):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
-                          "`python -m paged_kv_attention_attn_amd.build`")
+                          "`python paged_kv_attention_attn_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     vp, sz, i32p = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p
     lib.pkv_attn_workspace_bytes.argtypes = [ctypes.POINTER(pkv_attn_shape)]
@@ -68,6 +69,11 @@ def _load():
     lib.pkv_attn_fwd.argtypes = [vp, vp, vp, i32p, i32p, i32p, vp, ctypes.POINTER(pkv_attn_shape),
                                  vp, sz, vp]
     lib.pkv_attn_fwd.restype = ctypes.c_int
+    lib.pkv_attn_shared_workspace_bytes.argtypes = [ctypes.POINTER(pkv_attn_shape), ctypes.c_int32]
+    lib.pkv_attn_shared_workspace_bytes.restype = sz
+    lib.pkv_attn_fwd_shared.argtypes = [vp, vp, vp, i32p, i32p, i32p, vp, ctypes.POINTER(pkv_attn_shape),
+                                        ctypes.c_int32, vp, sz, vp]
+    lib.pkv_attn_fwd_shared.restype = ctypes.c_int
     lib.pkv_attn_check_errors.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_uint32)]
     lib.pkv_attn_check_errors.restype = ctypes.c_int
     lib.pkv_accept_workspace_bytes.argtypes = [ctypes.POINTER(pkv_accept_shape)]
@@ -172,6 +178,31 @@ def pkv_attn_fwd(q, k_pool, v_pool, block_table, seq_lens, q_lens, out, shape, w
                           _ptr(q_lens), _ptr(out), ctypes.byref(shape), _ptr(workspace),
                           workspace.numel(), _stream(stream))
     _check(rc, "pkv_attn_fwd")
+
+
+def pkv_attn_shared_workspace_bytes(shape, shared_pages):
+    return int(LIB.pkv_attn_shared_workspace_bytes(ctypes.byref(shape), int(shared_pages)))
+
+
+def new_attn_shared_workspace(shape, shared_pages, device="cuda"):
+    n = pkv_attn_shared_workspace_bytes(shape, shared_pages)
+    if n == 0:
+        raise PkvError("pkv_attn_shared_workspace_bytes: shape rejected")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def pkv_attn_fwd_shared(q, k_pool, v_pool, block_table, seq_lens, q_lens, out, shape, shared_pages, workspace,
+                        stream=None):
+    """pkv_attn_fwd over a batch whose tables all begin with the same shared_pages pages."""
+    for t, dt, n in ((q, torch.bfloat16, "q"), (k_pool, torch.bfloat16, "k_pool"),
+                     (v_pool, torch.bfloat16, "v_pool"), (block_table, torch.int32, "block_table"),
+                     (seq_lens, torch.int32, "seq_lens"), (q_lens, torch.int32, "q_lens"),
+                     (out, torch.float32, "out"), (workspace, torch.uint8, "workspace")):
+        _need(t, dt, n)
+    rc = LIB.pkv_attn_fwd_shared(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(seq_lens),
+                                 _ptr(q_lens), _ptr(out), ctypes.byref(shape), int(shared_pages), _ptr(workspace),
+                                 workspace.numel(), _stream(stream))
+    _check(rc, "pkv_attn_fwd_shared")
 
 
 def pkv_attn_check_errors(workspace, stream=None):

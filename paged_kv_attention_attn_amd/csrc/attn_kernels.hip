@@ -803,17 +803,20 @@ __global__ __launch_bounds__(WAVES * 64) void attn_split_kernel(
 
   // independent loads first, so their latencies overlap: the sequence's
   // lengths, the split's table entries and the window-row prefix sum
+  // p.page_offset leading table entries (and their tokens) are skipped: a
+  // shared prefix attended to elsewhere; 0 otherwise
+  const int po = p.page_offset;
   const int page0 = s * pps;
   int tbl = -1;
-  if ((int)threadIdx.x < pps && page0 + (int)threadIdx.x < W)
-    tbl = block_table[(size_t)b * W + page0 + threadIdx.x];
-  const int seq_len = seq_lens[b];
+  if ((int)threadIdx.x < pps && page0 + (int)threadIdx.x < W - po)
+    tbl = block_table[(size_t)b * W + po + page0 + threadIdx.x];
+  const int seq_len = seq_lens[b] - po * kPage;
   const int q_len = q_lens[b];
   const int q_start = __builtin_amdgcn_readfirstlane(wave_prefix(q_lens, b));
   if (q_len <= 0) return;
   const int n_pages = (seq_len + kPage - 1) / kPage;
   const int n_splits = (n_pages + pps - 1) / pps;
-  if (q_len > p.max_q_len || q_len > seq_len || n_pages > W) {
+  if (q_len > p.max_q_len || q_len > seq_len || n_pages > W - po) {
     if (s == 0 && g == 0 && threadIdx.x == 0) atomicOr(p.err, PKV_EFLAG_QLEN_BIT);
     return;
   }
@@ -954,6 +957,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_split_kernel(
     if (n_splits == 1) {
       const int h = g * p.group + r % p.group;
       *reinterpret_cast<f32x4*>(p.out + ((size_t)(q_start + r / p.group) * p.Hq + h) * D + 4 * dq) = A / L;
+      if (p.out_lse && dq == 0) p.out_lse[(size_t)(q_start + r / p.group) * p.Hq + h] = M + __log2f(L);
     } else {
       // write-through stores: visible to the merging workgroup on any XCD
       __builtin_amdgcn_raw_buffer_store_b128(A, acc_rsrc, ((s * p.rows_max + r) * D + 4 * dq) * 4, 0, kSc1);
@@ -1031,6 +1035,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_split_kernel(
     const int r = e / D4, dq = e % D4;
     const int h = g * p.group + r % p.group;
     *reinterpret_cast<f32x4*>(p.out + ((size_t)(q_start + r / p.group) * p.Hq + h) * D + 4 * dq) = A[u] / L[u];
+    if (p.out_lse && dq == 0) p.out_lse[(size_t)(q_start + r / p.group) * p.Hq + h] = M[u] + __log2f(L[u]);
   }
   if (threadIdx.x == 0) __hip_atomic_store(p.counters + bg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -1068,11 +1073,26 @@ __device__ __forceinline__ void wait_chunks(int ahead) {
   }
 }
 
+// Streams keys key_begin .. key_end - 1 (key_begin a multiple of 32) of KV
+// head g through the workgroup's ring of NBUF K/V chunks into the tile's
+// rows. s_pages[j] is the physical page of keys (key_begin / 256 + j) * 256 ..
+// (a negative entry reads as zeros). Chunks [0, n_split) take P in two bf16
+// terms; chunks [n_split, n_free) are seen in full by every valid row of this
+// wave and go unmasked; the rest are masked by the tile's row limits.
+//
+// The chunk loop is software-pipelined: while the VALU turns chunk c's
+// scores into P, the matrix cores already compute chunk c + 1's scores. Each
+// wave issues a quarter of every chunk's direct buffer->LDS loads. arrive(k):
+// chunk k has landed once at most the chunks issued after it are pending
+// (this wave's share); the barrier then covers the other waves' shares and
+// tells that every wave is done with chunk k - 2 (its V was read in the
+// iteration that ended before it), whose slot takes chunk k + NBUF - 2. It
+// then copies chunk k's K operand out. Every wave of the workgroup must call
+// this with the same key range.
 template <int D, int NBUF>
-__global__ __launch_bounds__(kPrefillRows) void attn_prefill_kernel(
-    const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
-    const int32_t* __restrict__ q_lens, int B, int Hkv, int qtok, int W, AttnParams p) {
-  using Tile = MfmaTile<D, 2>;
+__device__ __forceinline__ void stream_keys(MfmaTile<D, 2>& tile, char* ring, const int* s_pages,
+                                            const AttnParams& p, int Hkv, int g, int key_begin, int key_end,
+                                            int n_split, int n_free, float scale_log2) {
   using G = TileGeom<D, 32>;
   constexpr int TC = 32;
   constexpr int NI = G::NI;   // 1 KiB loads per K (or V) chunk
@@ -1081,6 +1101,135 @@ __global__ __launch_bounds__(kPrefillRows) void attn_prefill_kernel(
   constexpr int LPC = 2 * KPW;             // load instructions per chunk per wave
   static_assert(NI % kPrefillWaves == 0, "chunk loads split evenly over the waves");
   static_assert(NBUF >= 3 && LPC * (NBUF - 3) < 64, "ring depth");
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int n_chunks = (key_end - key_begin + TC - 1) / TC;
+  const int page_base = key_begin / kPage;
+
+  // per-lane byte offsets of this wave's share of a chunk's direct loads
+  u32 voff[KPW];
+#pragma unroll
+  for (int i = 0; i < KPW; ++i) {
+    const int slot = (wave * KPW + i) * 64 + lane;
+    const int t = slot / NC, pos = slot % NC;
+    voff[i] = t * G::RB + ((pos ^ (t & (NC - 1))) * 16);
+  }
+  const u32 ring_lds = lds_addr_of(ring);
+  const size_t head_stride = (size_t)kPage * D;
+  auto issue = [&](int c) {
+    const int t0 = key_begin + c * TC;
+    const int phys = __builtin_amdgcn_readfirstlane(s_pages[t0 / kPage - page_base]);
+    int nvt = min(TC, key_end - t0);
+    if (phys < 0) nvt = 0;
+    const size_t off = ((size_t)(phys < 0 ? 0 : phys) * Hkv + g) * head_stride + (size_t)(t0 % kPage) * D;
+    const u32 bytes = nvt > 0 ? (u32)(nvt * G::RB) : 0u;
+    const u32x4 rk = make_rsrc(p.k_pool + off, bytes);
+    const u32x4 rv = make_rsrc(p.v_pool + off, bytes);
+    const u32 base = uniform(ring_lds + (c % NBUF) * 2 * G::TILE + wave * KPW * 1024);
+#pragma unroll
+    for (int i = 0; i < KPW; ++i) dma16(rk, voff[i], base + i * 1024);
+#pragma unroll
+    for (int i = 0; i < KPW; ++i) dma16(rv, voff[i], base + G::TILE + i * 1024);
+  };
+
+#pragma unroll
+  for (int c = 0; c < NBUF - 2; ++c)
+    if (c < n_chunks) issue(c);
+
+  auto slot = [&](int c) { return ring + (c % NBUF) * 2 * G::TILE; };
+  auto arrive = [&](int k) {
+    wait_chunks<LPC, NBUF - 3>(min(NBUF - 3, n_chunks - 1 - k));
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (k + NBUF - 2 < n_chunks) issue(k + NBUF - 2);
+    tile.fetch_k(slot(k));
+  };
+  // Prologue: chunk 0's scores. Iteration c then runs, in one stretch of
+  // straight-line code: chunk c's exponentials beside chunk c + 1's score
+  // products, and chunk c's P.V products beside chunk c + 1's row maxima;
+  // the rare rescale of chunk c + 1 closes it.
+  f32x16 S[2];
+  arrive(0);
+  tile.qk(S);
+  if (tile.template scores<true>(S, key_begin, min(TC, key_end - key_begin), scale_log2)) tile.rescale();
+  auto step = [&](auto split_p, auto mask_next, int c) {
+    constexpr bool kSplit = decltype(split_p)::value, kMask = decltype(mask_next)::value;
+    const int cn = c + 1;  // past the last chunk its products repeat chunk c's, unused
+    const int t1 = key_begin + cn * TC;
+    if (cn < n_chunks) arrive(cn);
+    tile.fetch_v(slot(c) + G::TILE);
+    tile.template probs<kSplit>(scale_log2);
+    tile.qk(S);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, kSplit ? 7 : 5, 0);
+    }
+    tile.template pv<kSplit>();
+    const bool grow = tile.template scores<kMask>(S, t1, min(TC, key_end - t1), scale_log2);
+#pragma unroll
+    for (int i = 0; i < (kSplit ? 36 : 20); ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, kSplit ? 2 : 4, 0);
+    }
+    if (grow && cn < n_chunks) tile.rescale();
+  };
+  // chunk c's P: two bf16 terms for chunks below n_split and wherever a key
+  // still weighs more than 1/8 of its row; chunk c + 1's mask: the unmasked
+  // stretch ends one chunk early so its next chunk is unmasked too
+  const int c_mask = max(n_split, n_free - 1);
+  int c = 0;
+  for (; c < n_split; ++c) step(std::true_type{}, std::true_type{}, c);
+  while (c < n_chunks) {
+    for (; c < c_mask && !tile.needs_split(); ++c) step(std::false_type{}, std::false_type{}, c);
+    for (; c >= c_mask && c < n_chunks && !tile.needs_split(); ++c) step(std::false_type{}, std::true_type{}, c);
+    if (c < n_chunks) step(std::true_type{}, std::true_type{}, c++);
+  }
+}
+
+// The softmax of stream_keys takes scale_log2 > 0 (it scales row maxima, not
+// every score, and masked scores are -inf): a negative scale becomes a
+// positive one on -q (negating bf16, its sign bits, is exact), and a zero
+// scale is scale 1 on q = 0 (every visible key weighs the same either way).
+struct QSign {
+  u32 sign, keep;
+  float scale_log2;
+  __device__ explicit QSign(float s)
+      : sign(s < 0.f ? 0x80008000u : 0u), keep(s == 0.f ? 0u : 0xFFFFFFFFu), scale_log2(s == 0.f ? 1.f : fabsf(s)) {}
+  __device__ u32x4 apply(u32x4 q) const { return (q & u32x4{keep, keep, keep, keep}) ^ u32x4{sign, sign, sign, sign}; }
+};
+
+// Loads the q rows of one wave's 64 tile rows straight into the MFMA operand
+// registers; row_src(r) is the q row (element offset) of tile row r, or -1 for
+// a padding row.
+template <int D, class RowSrc>
+__device__ __forceinline__ void load_q_rows(MfmaTile<D, 2>& tile, const uint16_t* q, const QSign& qs,
+                                            RowSrc row_src) {
+  using Tile = MfmaTile<D, 2>;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int half = lane >> 5;
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const long off = row_src(wave * 64 + rb * 32 + (lane & 31));
+    const u32x4* src = reinterpret_cast<const u32x4*>(q + (off < 0 ? 0 : off));
+#pragma unroll
+    for (int kk = 0; kk < Tile::KK; ++kk)
+      tile.qb[rb][kk] = qs.apply(off >= 0 ? src[2 * kk + half] : u32x4{0u, 0u, 0u, 0u});
+  }
+  // wait for the q operands here: a load still pending at the chunk loop
+  // would make the compiler wait for every load in flight (the whole K/V
+  // ring, which it does not see) at each chunk
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int kk = 0; kk < Tile::KK; ++kk) asm volatile("" ::"v"(tile.qb[rb][kk]));
+}
+
+template <int D, int NBUF>
+__global__ __launch_bounds__(kPrefillRows) void attn_prefill_kernel(
+    const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
+    const int32_t* __restrict__ q_lens, int B, int Hkv, int qtok, int W, AttnParams p) {
+  using Tile = MfmaTile<D, 2>;
+  using G = TileGeom<D, 32>;
+  constexpr int TC = 32;
   __shared__ __attribute__((aligned(16))) char ring[NBUF * 2 * G::TILE];
   __shared__ int s_pages[kPrefillMaxPages];
 
@@ -1118,86 +1267,17 @@ __global__ __launch_bounds__(kPrefillRows) void attn_prefill_kernel(
     s_pages[j] = e;
   }
 
-  // The softmax below takes scale_log2 > 0 (it scales row maxima, not every
-  // score, and masked scores are -inf): a negative scale becomes a positive
-  // one on -q (negating bf16, its sign bits, is exact), and a zero scale is
-  // scale 1 on q = 0 (every visible key weighs the same either way).
-  const u32 qsign = p.scale_log2 < 0.f ? 0x80008000u : 0u;
-  const u32 qkeep = p.scale_log2 == 0.f ? 0u : 0xFFFFFFFFu;
-  const float scale_log2 = p.scale_log2 == 0.f ? 1.f : fabsf(p.scale_log2);
-  // q rows of this wave straight into the MFMA operand registers: row r of
-  // the tile is window token tq0 + r / group, q head g * group + r % group
+  // row r of the tile is window token tq0 + r / group, q head g * group + r % group
+  const QSign qs(p.scale_log2);
   Tile tile;
   const int r_lo = (tq0 < 0 ? -tq0 : 0) * p.group, r_hi = qtok * p.group;
   tile.init_rows(wave * 64, p.group, seq_len - q_len + tq0, r_lo, r_hi);
-  {
-    const int half = lane >> 5;
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      const int r = wave * 64 + rb * 32 + (lane & 31);
-      const bool ok = r >= r_lo && r < r_hi;
-      const u32x4* src = reinterpret_cast<const u32x4*>(
-          p.q + ((size_t)(q_start + tq0 + (ok ? r / p.group : 0 - tq0)) * p.Hq + g * p.group + r % p.group) * D);
-#pragma unroll
-      for (int kk = 0; kk < Tile::KK; ++kk) {
-        tile.qb[rb][kk] = ok ? src[2 * kk + half] : u32x4{0u, 0u, 0u, 0u};
-        tile.qb[rb][kk] = (tile.qb[rb][kk] & u32x4{qkeep, qkeep, qkeep, qkeep}) ^ u32x4{qsign, qsign, qsign, qsign};
-      }
-    }
-    // wait for the q operands here: a load still pending at the chunk loop
-    // would make the compiler wait for every load in flight (the whole K/V
-    // ring, which it does not see) at each chunk
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-      for (int kk = 0; kk < Tile::KK; ++kk) asm volatile("" ::"v"(tile.qb[rb][kk]));
-  }
+  load_q_rows<D>(tile, p.q, qs, [&](int r) -> long {
+    if (r < r_lo || r >= r_hi) return -1;
+    return ((long)(q_start + tq0 + r / p.group) * p.Hq + g * p.group + r % p.group) * D;
+  });
   __syncthreads();  // table entries staged
 
-  // per-lane byte offsets of this wave's share of a chunk's direct loads
-  u32 voff[KPW];
-#pragma unroll
-  for (int i = 0; i < KPW; ++i) {
-    const int slot = (wave * KPW + i) * 64 + lane;
-    const int t = slot / NC, pos = slot % NC;
-    voff[i] = t * G::RB + ((pos ^ (t & (NC - 1))) * 16);
-  }
-  const u32 ring_lds = lds_addr_of(ring);
-  const size_t head_stride = (size_t)kPage * D;
-  auto issue = [&](int c) {
-    const int t0 = c * TC;
-    const int phys = __builtin_amdgcn_readfirstlane(s_pages[t0 / kPage]);
-    int nvt = min(TC, key_end - t0);
-    if (phys < 0) nvt = 0;
-    const size_t off = ((size_t)(phys < 0 ? 0 : phys) * Hkv + g) * head_stride + (size_t)(t0 % kPage) * D;
-    const u32 bytes = nvt > 0 ? (u32)(nvt * G::RB) : 0u;
-    const u32x4 rk = make_rsrc(p.k_pool + off, bytes);
-    const u32x4 rv = make_rsrc(p.v_pool + off, bytes);
-    const u32 base = uniform(ring_lds + (c % NBUF) * 2 * G::TILE + wave * KPW * 1024);
-#pragma unroll
-    for (int i = 0; i < KPW; ++i) dma16(rk, voff[i], base + i * 1024);
-#pragma unroll
-    for (int i = 0; i < KPW; ++i) dma16(rv, voff[i], base + G::TILE + i * 1024);
-  };
-
-#pragma unroll
-  for (int c = 0; c < NBUF - 2; ++c)
-    if (c < n_chunks) issue(c);
-
-  // The chunk loop is software-pipelined: while the VALU turns chunk c's
-  // scores into P, the matrix cores already compute chunk c + 1's scores.
-  // arrive(k): chunk k has landed once at most the chunks issued after it are
-  // pending (this wave's share); the barrier then covers the other waves'
-  // shares and tells that every wave is done with chunk k - 2 (its V was read
-  // in the iteration that ended before it), whose slot takes chunk
-  // k + NBUF - 2. It then copies chunk k's K operand out.
-  auto slot = [&](int c) { return ring + (c % NBUF) * 2 * G::TILE; };
-  auto arrive = [&](int k) {
-    wait_chunks<LPC, NBUF - 3>(min(NBUF - 3, n_chunks - 1 - k));
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (k + NBUF - 2 < n_chunks) issue(k + NBUF - 2);
-    tile.fetch_k(slot(k));
-  };
   // the first 64 keys with P in two bf16 terms: rows that see fewer than 64
   // keys see nothing else, and their few terms would not average out the
   // rounding of a single bf16 P. Then the chunks every valid row of this
@@ -1206,47 +1286,7 @@ __global__ __launch_bounds__(kPrefillRows) void attn_prefill_kernel(
   const int wrow = max(r_lo, wave * 64);
   const int wave_min_lim = wrow < r_hi ? seq_len - q_len + tq0 + wrow / p.group : key_end;
   const int n_free = max(n_split, min(key_end / TC, (wave_min_lim + 1) / TC));
-  // Prologue: chunk 0's scores. Iteration c then runs, in one stretch of
-  // straight-line code: chunk c's exponentials beside chunk c + 1's score
-  // products, and chunk c's P.V products beside chunk c + 1's row maxima;
-  // the rare rescale of chunk c + 1 closes it.
-  f32x16 S[2];
-  arrive(0);
-  tile.qk(S);
-  if (tile.template scores<true>(S, 0, min(TC, key_end), scale_log2)) tile.rescale();
-  auto step = [&](auto split_p, auto mask_next, int c) {
-    constexpr bool kSplit = decltype(split_p)::value, kMask = decltype(mask_next)::value;
-    const int cn = c + 1;  // past the last chunk its products repeat chunk c's, unused
-    if (cn < n_chunks) arrive(cn);
-    tile.fetch_v(slot(c) + G::TILE);
-    tile.template probs<kSplit>(scale_log2);
-    tile.qk(S);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, kSplit ? 7 : 5, 0);
-    }
-    tile.template pv<kSplit>();
-    const bool grow = tile.template scores<kMask>(S, cn * TC, min(TC, key_end - cn * TC), scale_log2);
-#pragma unroll
-    for (int i = 0; i < (kSplit ? 36 : 20); ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, kSplit ? 2 : 4, 0);
-    }
-    if (grow && cn < n_chunks) tile.rescale();
-  };
-  // chunk c's P: two bf16 terms for the first 64 keys (rows that see fewer
-  // than 64 keys see nothing else) and wherever a key still weighs more than
-  // 1/32 of its row; chunk c + 1's mask: the unmasked stretch ends one chunk
-  // early so its next chunk is unmasked too
-  const int c_mask = max(n_split, n_free - 1);
-  int c = 0;
-  for (; c < n_split; ++c) step(std::true_type{}, std::true_type{}, c);
-  while (c < n_chunks) {
-    for (; c < c_mask && !tile.needs_split(); ++c) step(std::false_type{}, std::false_type{}, c);
-    for (; c >= c_mask && c < n_chunks && !tile.needs_split(); ++c) step(std::false_type{}, std::true_type{}, c);
-    if (c < n_chunks) step(std::true_type{}, std::true_type{}, c++);
-  }
+  stream_keys<D, NBUF>(tile, ring, s_pages, p, Hkv, g, 0, key_end, n_split, n_free, qs.scale_log2);
 
   // rows -> out
   {
@@ -1267,6 +1307,130 @@ __global__ __launch_bounds__(kPrefillRows) void attn_prefill_kernel(
         }
     }
   }
+}
+
+// ------------------------------------------------------ shared-prefix path
+
+// Decode / verify over a batch whose sequences all begin with the same
+// shared_pages pages (a deduplicated prompt prefix, ExLlamaV2 "Dynamic
+// Generator" page, "Deduplication"). The shared keys are attended to once per
+// KV head for every window row of the batch stacked into 256-row MFMA tiles
+// (rows = total_q x group), cut into key splits; each split leaves a partial
+// (reference max, row sum, unnormalised accumulator) per row. The tails run
+// through the split kernel with the shared pages skipped, which also leaves
+// each row's log-sum-exp, and shared_merge_kernel folds the partials in.
+//
+// Work item = (KV head g, row tile, key split), KV head fastest so that every
+// item of one head lands on one XCD when Hkv is a multiple of 8.
+template <int D, int NBUF>
+__global__ __launch_bounds__(kPrefillRows) void attn_shared_kernel(SharedParams sp, AttnParams p) {
+  using Tile = MfmaTile<D, 2>;
+  using G = TileGeom<D, 32>;
+  __shared__ __attribute__((aligned(16))) char ring[NBUF * 2 * G::TILE];
+  __shared__ int s_pages[kPrefillMaxPages];
+
+  const int Hkv = p.Hkv;
+  const int g = blockIdx.x % Hkv;
+  const int rest = blockIdx.x / Hkv;
+  const int rt = rest % sp.row_tiles, split = rest / sp.row_tiles;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int shared_tokens = sp.shared_pages * kPage;
+
+  // the contract, checked once: every table starts with sequence 0's shared
+  // entries and every window row sees the whole shared prefix
+  if (blockIdx.x == 0) {
+    for (int e = threadIdx.x; e < p.B * sp.shared_pages; e += kPrefillRows) {
+      const int b = e / sp.shared_pages, j = e % sp.shared_pages;
+      if (p.block_table[(size_t)b * p.W + j] != p.block_table[j]) atomicOr(p.err, PKV_EFLAG_PAGE_BIT);
+      if (j == 0 && p.q_lens[b] > 0 && p.seq_lens[b] - p.q_lens[b] < shared_tokens)
+        atomicOr(p.err, PKV_EFLAG_QLEN_BIT);
+    }
+  }
+
+  const int key_begin = split * sp.split_keys;
+  const int key_end = min(key_begin + sp.split_keys, shared_tokens);
+  if (key_begin >= key_end) return;
+  const int page_base = key_begin / kPage, n_pg = (key_end - 1) / kPage - page_base + 1;
+  for (int j = threadIdx.x; j < n_pg; j += kPrefillRows) {
+    int e = p.block_table[page_base + j];
+    if (e < 0 || e >= p.P) {
+      atomicOr(p.err, PKV_EFLAG_PAGE_BIT);
+      e = -1;
+    }
+    s_pages[j] = e;
+  }
+
+  // tile row r is batch row R = rt * 256 + r: q row R / group, q head
+  // g * group + R % group; every row sees every shared key
+  const int rows = p.total_q * p.group;
+  const int r_hi = min(kPrefillRows, rows - rt * kPrefillRows);
+  const QSign qs(p.scale_log2);
+  Tile tile;
+  tile.init_rows(wave * 64, 1, 1 << 30, 0, r_hi);
+  load_q_rows<D>(tile, p.q, qs, [&](int r) -> long {
+    if (r >= r_hi) return -1;
+    const int R = rt * kPrefillRows + r;
+    return ((long)(R / p.group) * p.Hq + g * p.group + R % p.group) * D;
+  });
+  __syncthreads();  // table entries staged
+
+  const int n_chunks = (key_end - key_begin) / 32;
+  stream_keys<D, NBUF>(tile, ring, s_pages, p, Hkv, g, key_begin, key_end, 0, n_chunks, qs.scale_log2);
+
+  // partials: (m, l) and the unnormalised accumulator of each valid row
+  {
+    const int half = lane >> 5;
+    const size_t base = ((size_t)g * sp.splits + split) * rows + rt * kPrefillRows;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const int r = wave * 64 + rb * 32 + (lane & 31);
+      if (r >= r_hi) continue;
+      if (half == 0) {
+        sp.part_ml[(base + r) * 2] = tile.m[rb];
+        sp.part_ml[(base + r) * 2 + 1] = tile.lacc[rb][0];
+      }
+      float* dst = sp.part_acc + (base + r) * D;
+#pragma unroll
+      for (int mb = 0; mb < Tile::MB; ++mb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          *reinterpret_cast<f32x4*>(dst + mb * 32 + 8 * j + 4 * half) =
+              f32x4{tile.acc[rb][mb][4 * j], tile.acc[rb][mb][4 * j + 1], tile.acc[rb][mb][4 * j + 2],
+                    tile.acc[rb][mb][4 * j + 3]};
+    }
+  }
+}
+
+// out (the tails' normalised rows, in place) and their log-sum-exp merged
+// with the shared-prefix partials: one thread per (q row, q head, 4 dims),
+// splits in order.
+template <int D>
+__global__ __launch_bounds__(256) void shared_merge_kernel(SharedParams sp, AttnParams p) {
+  constexpr int D4 = D / 4;
+  const long e = (long)blockIdx.x * 256 + threadIdx.x;
+  if (e >= (long)p.total_q * p.Hq * D4) return;
+  const int dq = (int)(e % D4);
+  const long th = e / D4;                        // q row * Hq + q head
+  const int h = (int)(th % p.Hq), t = (int)(th / p.Hq);
+  const int g = h / p.group;
+  const int rows = p.total_q * p.group;
+  const int R = t * p.group + h % p.group;
+  const float lse = p.out_lse[th];
+  float M = lse;
+  for (int s = 0; s < sp.splits; ++s) M = fmaxf(M, sp.part_ml[(((size_t)g * sp.splits + s) * rows + R) * 2]);
+  float* o = p.out + th * D + 4 * dq;
+  const float wt = exp2f_fast(lse - M);
+  f32x4 num = *reinterpret_cast<const f32x4*>(o) * wt;
+  float den = wt;
+  for (int s = 0; s < sp.splits; ++s) {
+    const size_t i = ((size_t)g * sp.splits + s) * rows + R;
+    const float ms = sp.part_ml[i * 2];
+    if (ms == kNegInf) continue;
+    const float w = exp2f_fast(ms - M);
+    den += sp.part_ml[i * 2 + 1] * w;
+    num += *reinterpret_cast<const f32x4*>(sp.part_acc + i * D + 4 * dq) * w;
+  }
+  *reinterpret_cast<f32x4*>(o) = num / den;
 }
 
 template <int D, class Tile, int NBUF, int WAVES>
@@ -1342,6 +1506,43 @@ AttnWorkspace attn_workspace(int B, int Hkv, int W, int max_q_len, int group, in
   ws.acc_off = align_up(ws.ml_off + items * pl.rows * 2 * 4, 256);
   ws.total = align_up(ws.acc_off + items * pl.rows * (size_t)D * 4, 256);
   return ws;
+}
+
+SharedPlan shared_plan(int Hkv, int total_q, int group, int shared_pages) {
+  SharedPlan sp;
+  const int rows = total_q * group;
+  sp.row_tiles = (rows + kPrefillRows - 1) / kPrefillRows;
+  const int chunks = shared_pages * kPage / 32;
+  // about one workgroup per CU (one fits: the ring takes most of the LDS),
+  // at least 4 chunks of 32 keys per split
+  const long tiles = (long)Hkv * sp.row_tiles;
+  long splits = (kNumCu + tiles - 1) / tiles;
+  if (splits > chunks / 4) splits = chunks / 4;
+  if (splits < 1) splits = 1;
+  const int per = (int)((chunks + splits - 1) / splits);
+  sp.split_keys = per * 32;
+  sp.splits = (chunks + per - 1) / per;
+  return sp;
+}
+
+hipError_t launch_attn_shared(const AttnParams& p, const SharedParams& sp, hipStream_t stream) {
+  const unsigned grid = (unsigned)((long)p.Hkv * sp.row_tiles * sp.splits);
+  if (p.D == 64)
+    hipLaunchKernelGGL((attn_shared_kernel<64, PKV_PREFILL_NBUF>), dim3(grid), dim3(kPrefillRows), 0, stream, sp, p);
+  else
+    hipLaunchKernelGGL((attn_shared_kernel<128, PKV_PREFILL_NBUF>), dim3(grid), dim3(kPrefillRows), 0, stream, sp,
+                       p);
+  return hipGetLastError();
+}
+
+hipError_t launch_shared_merge(const AttnParams& p, const SharedParams& sp, hipStream_t stream) {
+  const long n = (long)p.total_q * p.Hq * (p.D / 4);
+  const unsigned grid = (unsigned)((n + 255) / 256);
+  if (p.D == 64)
+    hipLaunchKernelGGL((shared_merge_kernel<64>), dim3(grid), dim3(256), 0, stream, sp, p);
+  else
+    hipLaunchKernelGGL((shared_merge_kernel<128>), dim3(grid), dim3(256), 0, stream, sp, p);
+  return hipGetLastError();
 }
 
 hipError_t launch_attn(const AttnParams& p, const AttnPlan& plan, hipStream_t stream) {

@@ -68,6 +68,81 @@ pkv::KvParams kv_params(const pkv_kv_shape* s, void* workspace) {
   return p;
 }
 
+pkv::AttnParams attn_params(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_table,
+                            const int32_t* seq_lens, const int32_t* q_lens, float* out, const pkv_attn_shape* s,
+                            void* workspace, const pkv::AttnWorkspace& ws, const pkv::AttnPlan& plan,
+                            int32_t page_offset) {
+  char* w = static_cast<char*>(workspace);
+  pkv::AttnParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k_pool = static_cast<const uint16_t*>(k_pool);
+  p.v_pool = static_cast<const uint16_t*>(v_pool);
+  p.block_table = block_table;
+  p.seq_lens = seq_lens;
+  p.q_lens = q_lens;
+  p.out = out;
+  p.err = reinterpret_cast<uint32_t*>(w + ws.err_off);
+  p.counters = reinterpret_cast<uint32_t*>(w + ws.counters_off);
+  p.part_ml = reinterpret_cast<float*>(w + ws.ml_off);
+  p.part_acc = reinterpret_cast<float*>(w + ws.acc_off);
+  p.B = s->num_seqs;
+  p.Hq = s->num_q_heads;
+  p.Hkv = s->num_kv_heads;
+  p.group = s->num_q_heads / s->num_kv_heads;
+  p.D = s->head_dim;
+  p.P = s->num_pages;
+  p.W = s->max_pages_per_seq;
+  p.total_q = s->total_q;
+  p.max_q_len = s->max_q_len;
+  p.rows_max = plan.rows;
+  p.pps = plan.pps;
+  p.max_splits = plan.max_splits;
+  p.num_items = s->num_seqs * s->num_kv_heads * (plan.prefill ? plan.tiles : plan.max_splits);
+  p.scale_log2 = static_cast<float>(static_cast<double>(s->scale) * 1.4426950408889634);
+  p.page_offset = page_offset;
+  p.out_lse = nullptr;
+  return p;
+}
+
+// The shared-prefix call: decode / verify windows only (the tails run the
+// split kernel), and at least one page of every table past the shared ones.
+bool shared_shape_ok(const pkv_attn_shape* s, int32_t shared_pages) {
+  if (!attn_shape_ok(s) || shared_pages < 0) return false;
+  if (shared_pages == 0) return true;
+  const long rows = (long)s->max_q_len * (s->num_q_heads / s->num_kv_heads);
+  if (rows > PKV_MAX_ROWS) return false;
+  if (shared_pages >= s->max_pages_per_seq) return false;
+  if ((long)s->total_q * (s->num_q_heads / s->num_kv_heads) > (1L << 24)) return false;
+  return true;
+}
+
+// Workspace of the shared-prefix call: the tails' attention workspace (planned
+// for the table width past the shared pages), each row's log-sum-exp, and the
+// shared partials.
+struct SharedLayout {
+  pkv::AttnWorkspace tail;
+  pkv::AttnPlan plan;
+  pkv::SharedPlan sp;
+  size_t lse_off, ml_off, acc_off, total;
+};
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+SharedLayout shared_layout(const pkv_attn_shape* s, int32_t shared_pages) {
+  SharedLayout L;
+  const int group = s->num_q_heads / s->num_kv_heads;
+  const int tail_w = s->max_pages_per_seq - shared_pages;
+  L.tail = pkv::attn_workspace(s->num_seqs, s->num_kv_heads, tail_w, s->max_q_len, group, s->head_dim);
+  L.plan = pkv::attn_plan(s->num_seqs, s->num_kv_heads, tail_w, s->max_q_len, group);
+  L.sp = pkv::shared_plan(s->num_kv_heads, s->total_q, group, shared_pages);
+  const size_t rows = (size_t)s->total_q * group;
+  L.lse_off = align256(L.tail.total);
+  L.ml_off = align256(L.lse_off + (size_t)s->total_q * s->num_q_heads * 4);
+  L.acc_off = align256(L.ml_off + (size_t)s->num_kv_heads * L.sp.splits * rows * 2 * 4);
+  L.total = align256(L.acc_off + (size_t)s->num_kv_heads * L.sp.splits * rows * s->head_dim * 4);
+  return L;
+}
+
 }  // namespace
 
 extern "C" {
@@ -100,34 +175,47 @@ int pkv_attn_fwd(const void* q, const void* k_pool, const void* v_pool, const in
   if (!workspace || workspace_bytes < ws.total) return PKV_ERR_WORKSPACE;
   const pkv::AttnPlan plan = pkv::attn_plan(s->num_seqs, s->num_kv_heads, s->max_pages_per_seq,
                                             s->max_q_len, group);
-  char* w = static_cast<char*>(workspace);
-  pkv::AttnParams p;
-  p.q = static_cast<const uint16_t*>(q);
-  p.k_pool = static_cast<const uint16_t*>(k_pool);
-  p.v_pool = static_cast<const uint16_t*>(v_pool);
-  p.block_table = block_table;
-  p.seq_lens = seq_lens;
-  p.q_lens = q_lens;
-  p.out = out;
-  p.err = reinterpret_cast<uint32_t*>(w + ws.err_off);
-  p.counters = reinterpret_cast<uint32_t*>(w + ws.counters_off);
-  p.part_ml = reinterpret_cast<float*>(w + ws.ml_off);
-  p.part_acc = reinterpret_cast<float*>(w + ws.acc_off);
-  p.B = s->num_seqs;
-  p.Hq = s->num_q_heads;
-  p.Hkv = s->num_kv_heads;
-  p.group = group;
-  p.D = s->head_dim;
-  p.P = s->num_pages;
-  p.W = s->max_pages_per_seq;
-  p.total_q = s->total_q;
-  p.max_q_len = s->max_q_len;
-  p.rows_max = plan.rows;
-  p.pps = plan.pps;
-  p.max_splits = plan.max_splits;
-  p.num_items = s->num_seqs * s->num_kv_heads * (plan.prefill ? plan.tiles : plan.max_splits);
-  p.scale_log2 = static_cast<float>(static_cast<double>(s->scale) * 1.4426950408889634);
+  const pkv::AttnParams p =
+      attn_params(q, k_pool, v_pool, block_table, seq_lens, q_lens, out, s, workspace, ws, plan, 0);
   if (pkv::launch_attn(p, plan, static_cast<hipStream_t>(stream)) != hipSuccess) return PKV_ERR_HIP;
+  return PKV_OK;
+}
+
+size_t pkv_attn_shared_workspace_bytes(const pkv_attn_shape* s, int32_t shared_pages) {
+  if (!shared_shape_ok(s, shared_pages)) return 0;
+  if (shared_pages == 0) return pkv_attn_workspace_bytes(s);
+  return shared_layout(s, shared_pages).total;
+}
+
+int pkv_attn_fwd_shared(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_table,
+                        const int32_t* seq_lens, const int32_t* q_lens, float* out, const pkv_attn_shape* s,
+                        int32_t shared_pages, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!s) return PKV_ERR_NULL;
+  if (!shared_shape_ok(s, shared_pages)) return PKV_ERR_SHAPE;
+  if (shared_pages == 0)
+    return pkv_attn_fwd(q, k_pool, v_pool, block_table, seq_lens, q_lens, out, s, workspace, workspace_bytes,
+                        stream);
+  if (s->num_seqs == 0 || s->total_q == 0) return PKV_OK;
+  if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !q_lens || !out) return PKV_ERR_NULL;
+  const SharedLayout L = shared_layout(s, shared_pages);
+  if (!workspace || workspace_bytes < L.total) return PKV_ERR_WORKSPACE;
+  char* w = static_cast<char*>(workspace);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // the tails: the split kernel with the shared pages skipped, leaving each
+  // row's log-sum-exp too
+  pkv::AttnParams p =
+      attn_params(q, k_pool, v_pool, block_table, seq_lens, q_lens, out, s, workspace, L.tail, L.plan, shared_pages);
+  p.out_lse = reinterpret_cast<float*>(w + L.lse_off);
+  pkv::SharedParams sp{};
+  sp.part_ml = reinterpret_cast<float*>(w + L.ml_off);
+  sp.part_acc = reinterpret_cast<float*>(w + L.acc_off);
+  sp.shared_pages = shared_pages;
+  sp.splits = L.sp.splits;
+  sp.split_keys = L.sp.split_keys;
+  sp.row_tiles = L.sp.row_tiles;
+  if (pkv::launch_attn_shared(p, sp, st) != hipSuccess) return PKV_ERR_HIP;
+  if (pkv::launch_attn(p, L.plan, st) != hipSuccess) return PKV_ERR_HIP;
+  if (pkv::launch_shared_merge(p, sp, st) != hipSuccess) return PKV_ERR_HIP;
   return PKV_OK;
 }
 

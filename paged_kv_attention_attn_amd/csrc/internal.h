@@ -27,6 +27,8 @@ struct AttnParams {
   int32_t max_splits;   // ceil(W / pps)
   int32_t num_items;    // B * Hkv * max_splits
   float scale_log2;     // scale * log2(e)
+  int32_t page_offset;  // leading table entries skipped (a shared prefix attended to elsewhere), 0 otherwise
+  float* out_lse;       // nullable: [total_q, Hq] base-2 log-sum-exp of each row's scaled scores
 };
 
 // Workspace layout for a shape (byte offsets from the workspace base).
@@ -45,7 +47,21 @@ struct AttnPlan {
   int tiles;     // prefill: query tiles of the longest window
 };
 
+// Shared-prefix path: key splits of the shared pages and their partials.
+struct SharedParams {
+  float* part_ml;       // [Hkv][splits][total_q * group][2] = (reference max (log2 units), row sum)
+  float* part_acc;      // [Hkv][splits][total_q * group][D] unnormalised
+  int32_t shared_pages, splits, split_keys, row_tiles;
+};
+
+struct SharedPlan {
+  int splits, split_keys, row_tiles;
+};
+
 AttnPlan attn_plan(int B, int Hkv, int W, int max_q_len, int group);
+SharedPlan shared_plan(int Hkv, int total_q, int group, int shared_pages);
+hipError_t launch_attn_shared(const AttnParams& p, const SharedParams& sp, hipStream_t stream);
+hipError_t launch_shared_merge(const AttnParams& p, const SharedParams& sp, hipStream_t stream);
 AttnWorkspace attn_workspace(int B, int Hkv, int W, int max_q_len, int group, int D);
 hipError_t launch_attn(const AttnParams& p, const AttnPlan& plan, hipStream_t stream);
 

@@ -1,0 +1,132 @@
+"""GPU parity of the shared-prefix call (pkv_attn_fwd_shared): a batch whose
+tables all begin with the same pages attends to them once for every window
+row, then to each sequence's own tail, merged by log-sum-exp. Compared with
+the oracle (which knows nothing of the sharing), on the prefix-dedup
+configuration and on small decode / verify shapes; plus its contract flags
+and repeated calls on one workspace."""
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+import oracle
+from workloads import make_config, normal_bf16, AttnCase, BF16_QNAN
+from tests.gpu_util import say, assert_close, dev_bf16, dev_i32
+
+
+@pytest.fixture(scope="module")
+def pk():
+    import torch
+    assert torch.cuda.is_available()
+    import paged_kv_attention_attn_amd as pk
+    return pk
+
+
+def run_shared(pk, case, shared_pages, max_q_len=None):
+    import torch
+    q, k, v = dev_bf16(case.q), dev_bf16(case.k_pool), dev_bf16(case.v_pool)
+    bt, sl, ql = dev_i32(case.block_table), dev_i32(case.seq_lens), dev_i32(case.q_lens)
+    mq = max_q_len if max_q_len is not None else int(case.q_lens.max())
+    shape = pk.attn_shape(q, k, bt, mq, case.scale)
+    ws = pk.new_attn_shared_workspace(shape, shared_pages)
+    out = torch.empty(case.q.shape, dtype=torch.float32, device="cuda")
+    pk.pkv_attn_fwd_shared(q, k, v, bt, sl, ql, out, shape, shared_pages, ws)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    out.fill_(float("nan"))
+    pk.pkv_attn_fwd_shared(q, k, v, bt, sl, ql, out, shape, shared_pages, ws)   # the workspace is reusable
+    torch.cuda.synchronize()
+    again = out.cpu().numpy()
+    return got, again, pk.pkv_attn_check_errors(ws)
+
+
+def shared_case(seed, shared_pages, tails, q_lens, Hq=8, Hkv=2, D=128, spare=3):
+    """Sequences whose tables start with the same shared_pages pages; each has
+    tails[b] more tokens in private pages. Unreferenced pages and tails past
+    the lengths are NaN."""
+    rng = np.random.default_rng(seed)
+    B = len(tails)
+    own = [-(-int(t) // 256) for t in tails]
+    P = shared_pages + sum(own) + spare
+    perm = rng.permutation(P).astype(np.int32)
+    W = shared_pages + max(own) + 1
+    table = np.full((B, W), -1, np.int32)
+    table[:, :shared_pages] = perm[:shared_pages]
+    o = shared_pages
+    for b in range(B):
+        table[b, shared_pages:shared_pages + own[b]] = perm[o:o + own[b]]
+        o += own[b]
+    seq_lens = (shared_pages * 256 + np.asarray(tails)).astype(np.int32)
+    q_lens = np.asarray(q_lens, np.int32)
+    k = normal_bf16(rng, (P, Hkv, 256, D))
+    v = normal_bf16(rng, (P, Hkv, 256, D))
+    used = set(table[table >= 0].tolist())
+    for p in range(P):
+        if p not in used:
+            k[p] = BF16_QNAN
+            v[p] = BF16_QNAN
+    for b in range(B):
+        last, fill = int(table[b, shared_pages + own[b] - 1]), int(tails[b]) % 256
+        if fill:
+            k[last, :, fill:] = BF16_QNAN
+            v[last, :, fill:] = BF16_QNAN
+    q = normal_bf16(rng, (int(q_lens.sum()), Hq, D))
+    return AttnCase("shared", q, k, v, table, seq_lens, q_lens, float(np.float32(1 / np.sqrt(D))))
+
+
+def oracle_attn(case):
+    return oracle.attention(case.q, case.k_pool, case.v_pool, case.block_table, case.seq_lens, case.q_lens,
+                            case.scale)
+
+
+SHAPES = [
+    # shared_pages, tails, q_lens, Hq, Hkv, D
+    (1, [1, 100, 256, 257, 600], [1, 1, 1, 1, 1], 8, 2, 128),     # decode, tails across page ends
+    (3, [6, 40, 300], [6, 3, 6], 32, 8, 128),                    # verify windows (24 rows), 8 KV heads
+    (2, [16, 500, 77, 1000], [16, 2, 9, 1], 8, 2, 64),           # 64 rows, head_dim 64
+    (5, [10] * 70, [1] * 70, 8, 8, 128),                         # one KV head per q head, 70 sequences
+]
+
+
+@pytest.mark.parametrize("i", range(len(SHAPES)))
+def test_shared_prefix_matches_the_oracle(pk, i):
+    sp, tails, q_lens, Hq, Hkv, D = SHAPES[i]
+    say(f"shared prefix {i}: {sp} pages, tails {tails[:6]}, q_lens {q_lens[:6]}, Hq {Hq} Hkv {Hkv} D {D}")
+    case = shared_case(400 + i, sp, tails, q_lens, Hq, Hkv, D)
+    got, again, flags = run_shared(pk, case, sp)
+    assert flags == 0
+    assert_close(got, oracle_attn(case), f"shared {i}")
+    assert np.array_equal(got, again), "repeated call differs"
+
+
+def test_dedup_configuration(pk):
+    """The prefix-dedup configuration: 100 sequences sharing 16 pages."""
+    say("shared prefix: dedup configuration (100 x 16 shared pages)")
+    case, _ = make_config(4)
+    got, again, flags = run_shared(pk, case, 16)
+    assert flags == 0
+    assert_close(got, oracle_attn(case), "dedup shared")
+    assert np.array_equal(got, again)
+
+
+def test_zero_shared_pages_is_the_plain_call(pk):
+    case = shared_case(420, 2, [30, 300], [2, 1])
+    got, _, flags = run_shared(pk, case, 0)
+    assert flags == 0
+    assert_close(got, oracle_attn(case), "shared 0")
+
+
+def test_broken_contract_is_flagged(pk):
+    say("shared prefix: contract checks")
+    case = shared_case(421, 2, [30, 300, 50], [1, 1, 1])
+    bad = AttnCase("bad", case.q, case.k_pool, case.v_pool, case.block_table.copy(), case.seq_lens,
+                   case.q_lens, case.scale)
+    bad.block_table[2, 1] = bad.block_table[2, 2]          # sequence 2 does not share page 1
+    _, _, flags = run_shared(pk, bad, 2)
+    assert flags & pk.PKV_EFLAG_PAGE
+    short = AttnCase("short", case.q[:2], case.k_pool, case.v_pool, case.block_table[:2].copy(),
+                     np.array([2 * 256 + 30, 2 * 256 + 300], np.int32), np.array([1, 1], np.int32), case.scale)
+    short.seq_lens[0] = 2 * 256                              # no tail token: the window row is shared
+    _, _, flags = run_shared(pk, short, 2)
+    assert flags & pk.PKV_EFLAG_QLEN
