@@ -1403,34 +1403,50 @@ __global__ __launch_bounds__(kPrefillRows) void attn_shared_kernel(SharedParams 
 
 // out (the tails' normalised rows, in place) and their log-sum-exp merged
 // with the shared-prefix partials: one thread per (q row, q head, 4 dims),
-// splits in order.
+// splits in order, in batches of 8 whose loads are all issued before any is
+// used (one memory round trip per batch), with the running max rescaled per
+// batch.
 template <int D>
 __global__ __launch_bounds__(256) void shared_merge_kernel(SharedParams sp, AttnParams p) {
   constexpr int D4 = D / 4;
+  constexpr int SB = 8;
   const long e = (long)blockIdx.x * 256 + threadIdx.x;
   if (e >= (long)p.total_q * p.Hq * D4) return;
   const int dq = (int)(e % D4);
   const long th = e / D4;                        // q row * Hq + q head
   const int h = (int)(th % p.Hq), t = (int)(th / p.Hq);
   const int g = h / p.group;
-  const int rows = p.total_q * p.group;
-  const int R = t * p.group + h % p.group;
-  const float lse = p.out_lse[th];
-  float M = lse;
-  for (int s = 0; s < sp.splits; ++s) M = fmaxf(M, sp.part_ml[(((size_t)g * sp.splits + s) * rows + R) * 2]);
+  const size_t rows = (size_t)p.total_q * p.group;
+  const size_t R = (size_t)t * p.group + h % p.group;
   float* o = p.out + th * D + 4 * dq;
-  const float wt = exp2f_fast(lse - M);
-  f32x4 num = *reinterpret_cast<const f32x4*>(o) * wt;
-  float den = wt;
-  for (int s = 0; s < sp.splits; ++s) {
-    const size_t i = ((size_t)g * sp.splits + s) * rows + R;
-    const float ms = sp.part_ml[i * 2];
-    if (ms == kNegInf) continue;
-    const float w = exp2f_fast(ms - M);
-    den += sp.part_ml[i * 2 + 1] * w;
-    num += *reinterpret_cast<const f32x4*>(sp.part_acc + i * D + 4 * dq) * w;
+  // the tail as a partial: reference max lse, row sum 1, accumulator = its row
+  float M = p.out_lse[th], L = 1.f;
+  f32x4 A = *reinterpret_cast<const f32x4*>(o);
+  for (int s0 = 0; s0 < sp.splits; s0 += SB) {
+    f32x2 ml[SB];
+    f32x4 pa[SB];
+#pragma unroll
+    for (int j = 0; j < SB; ++j) {
+      const size_t i = ((size_t)g * sp.splits + min(s0 + j, sp.splits - 1)) * rows + R;
+      ml[j] = *reinterpret_cast<const f32x2*>(sp.part_ml + i * 2);
+      pa[j] = *reinterpret_cast<const f32x4*>(sp.part_acc + i * D + 4 * dq);
+    }
+    float Mn = M;
+#pragma unroll
+    for (int j = 0; j < SB; ++j)
+      if (s0 + j < sp.splits) Mn = fmaxf(Mn, ml[j].x);
+    const float f = exp2f_fast(M - Mn);
+    L *= f;
+    A *= f;
+#pragma unroll
+    for (int j = 0; j < SB; ++j) {
+      const float w = (s0 + j >= sp.splits || ml[j].x == kNegInf) ? 0.f : exp2f_fast(ml[j].x - Mn);
+      L += w * ml[j].y;
+      A += w * pa[j];
+    }
+    M = Mn;
   }
-  *reinterpret_cast<f32x4*>(o) = num / den;
+  *reinterpret_cast<f32x4*>(o) = A / L;
 }
 
 template <int D, class Tile, int NBUF, int WAVES>
