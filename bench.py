@@ -472,6 +472,24 @@ def main():
                                      "decode_tokens_per_s": round(c.num_seqs / (ms * 1e-3), 1)}
             del a
             torch.cuda.empty_cache()
+        log("configuration 4 through the shared-prefix call")
+        c, _ = make_config(4, seed=args.seed)
+        a = Attn(c, pk, torch, R)
+        shared = 16   # every table of the dedup workload starts with the same 16 pages
+        ws = pk.new_attn_shared_workspace(a.shape, shared)
+        f = lambda i: pk.pkv_attn_fwd_shared(a.q, a.k[i % R], a.v[i % R], a.bt, a.sl, a.ql, a.out, a.shape,
+                                              shared, ws)
+        ms = time_ms(torch, f, args.steps, args.warmup)
+        assert pk.pkv_attn_check_errors(ws) == 0, "shared-prefix call flagged its inputs"
+        kb = kv_logical_bytes(c.seq_lens, c.num_kv_heads, c.head_dim)
+        sweep["config4_shared"] = {"attn_us": round(ms * 1e3, 3), "kv_bytes": kb,
+                                   "kv_gbps_logical": round(kb / (ms * 1e-3) / 1e9, 2),
+                                   "shared_pages": shared,
+                                   "decode_tokens_per_s": round(c.num_seqs / (ms * 1e-3), 1),
+                                   "note": "pkv_attn_fwd_shared: the shared prefix is attended once per KV "
+                                           "head for all 400 window rows, the tails by the decode kernel"}
+        del a, ws
+        torch.cuda.empty_cache()
         sweep["config3"] = {"attn_us": result["attn_us"], "kv_bytes": kv_bytes,
                             "kv_gbps": result["attn_kv_gbps"], "hbm_fraction": result["attn_hbm_fraction"]}
         result["configs"] = sweep

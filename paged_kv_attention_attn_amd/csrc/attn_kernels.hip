@@ -69,6 +69,9 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 #ifndef PKV_PREFILL_NBUF
 #define PKV_PREFILL_NBUF 8  // K/V chunks in the ring shared by a prefill workgroup
 #endif
+#ifndef PKV_SHARED_WG
+#define PKV_SHARED_WG kNumCu  // workgroups the shared-prefix kernel aims for
+#endif
 #ifndef PKV_FORCE_PPS
 #define PKV_FORCE_PPS 0  // pages per split; 0 = planned per shape
 #endif
@@ -1336,15 +1339,14 @@ __global__ __launch_bounds__(kPrefillRows) void attn_shared_kernel(SharedParams 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int shared_tokens = sp.shared_pages * kPage;
 
-  // the contract, checked once: every table starts with sequence 0's shared
-  // entries and every window row sees the whole shared prefix
-  if (blockIdx.x == 0) {
-    for (int e = threadIdx.x; e < p.B * sp.shared_pages; e += kPrefillRows) {
-      const int b = e / sp.shared_pages, j = e % sp.shared_pages;
-      if (p.block_table[(size_t)b * p.W + j] != p.block_table[j]) atomicOr(p.err, PKV_EFLAG_PAGE_BIT);
-      if (j == 0 && p.q_lens[b] > 0 && p.seq_lens[b] - p.q_lens[b] < shared_tokens)
-        atomicOr(p.err, PKV_EFLAG_QLEN_BIT);
-    }
+  // the contract, one (sequence, shared entry) pair per thread of the grid:
+  // every table starts with sequence 0's shared entries and every window row
+  // sees the whole shared prefix
+  for (long e = (long)blockIdx.x * kPrefillRows + threadIdx.x; e < (long)p.B * sp.shared_pages;
+       e += (long)gridDim.x * kPrefillRows) {
+    const int b = (int)(e / sp.shared_pages), j = (int)(e % sp.shared_pages);
+    if (p.block_table[(size_t)b * p.W + j] != p.block_table[j]) atomicOr(p.err, PKV_EFLAG_PAGE_BIT);
+    if (j == 0 && p.q_lens[b] > 0 && p.seq_lens[b] - p.q_lens[b] < shared_tokens) atomicOr(p.err, PKV_EFLAG_QLEN_BIT);
   }
 
   const int key_begin = split * sp.split_keys;
@@ -1532,7 +1534,7 @@ SharedPlan shared_plan(int Hkv, int total_q, int group, int shared_pages) {
   // about one workgroup per CU (one fits: the ring takes most of the LDS),
   // at least 4 chunks of 32 keys per split
   const long tiles = (long)Hkv * sp.row_tiles;
-  long splits = (kNumCu + tiles - 1) / tiles;
+  long splits = (PKV_SHARED_WG + tiles - 1) / tiles;
   if (splits > chunks / 4) splits = chunks / 4;
   if (splits < 1) splits = 1;
   const int per = (int)((chunks + splits - 1) / splits);
