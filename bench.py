@@ -49,6 +49,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-configs", action="store_true", help="skip the per-configuration sweep")
     ap.add_argument("--no-prefill", action="store_true", help="skip the long-window (prefill) leg")
+    ap.add_argument("--no-queue", action="store_true", help="skip the mixed job-queue leg")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="time budget of the CPU oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -117,7 +118,9 @@ class Attn:
         self.q = dev(case.q)
         self.bt, self.sl, self.ql = i32(case.block_table), i32(case.seq_lens), i32(case.q_lens)
         self.out = torch.empty(case.q.shape, dtype=torch.float32, device="cuda")
-        self.shape = pk.attn_shape(self.q, k0, self.bt, max(1, case.max_q_len), case.scale)
+        # the host knows the lengths: its page count plans the splits
+        pages = int(sum(-(-int(n) // 256) for n in case.seq_lens))
+        self.shape = pk.attn_shape(self.q, k0, self.bt, max(1, case.max_q_len), case.scale, pages)
         self.ws = pk.new_attn_workspace(self.shape)
         self.R = replicas
 
@@ -264,6 +267,42 @@ def prefill_leg(torch, pk, seed, steps, warmup):
     out["note"] = ("algorithmic flops = 4 * head_dim * q_heads * sum over window rows of visible keys; "
                    "peak = dense bf16 matrix-core rate")
     return out
+
+
+def queue_leg(torch, pk, seed, steps, warmup):
+    """The mixed job queue (48 jobs of 256..16384 tokens with windows of 1, 3,
+    5 or 7 rows, admitted into a churned 256-page pool as pages free up, the
+    oldest retiring each step): every step's attention and accept timed on
+    its own inputs (HIP events, replicated pools not needed: the steps differ).
+    Verified tokens/s = accepted tokens over the summed attention + accept time."""
+    from workloads import Config5Queue, kv_logical_bytes
+    q = Config5Queue(seed=seed)
+    t_attn = t_acc = 0.0
+    accepted = kv = n = rows = 0
+    for st in q.steps():
+        c = st.case
+        a = Attn(c, pk, torch, 1)
+        ac = Accept(st.accept, pk, torch, 1)
+        t_attn += time_ms(torch, a, steps, warmup)
+        t_acc += time_ms(torch, ac, steps, warmup)
+        ac.win.copy_(ac.win0)
+        a(0)
+        ac(0)
+        torch.cuda.synchronize()
+        assert pk.pkv_attn_check_errors(a.ws) == 0, f"queue step {st.index}: attention error flags"
+        got = ac.oa.cpu().numpy()
+        assert np.array_equal(got, st.accept.planted_match + 1), f"queue step {st.index}: accepted counts"
+        accepted += int(got.sum())
+        kv += kv_logical_bytes(c.seq_lens, c.num_kv_heads, c.head_dim)
+        rows += int(c.q_lens.sum())
+        n += 1
+        del a, ac
+    torch.cuda.empty_cache()
+    return {"steps": n, "window_rows": rows, "accepted_tokens": accepted, "kv_bytes": kv,
+            "attn_us_total": round(t_attn * 1e3, 2), "accept_us_total": round(t_acc * 1e3, 2),
+            "kv_gbps": round(kv / (t_attn * 1e-3) / 1e9, 2),
+            "verified_tokens_per_s": round(accepted / ((t_attn + t_acc) * 1e-3), 1),
+            "note": "single layer, no model GEMMs; accepted counts checked against the planted draft matches"}
 
 
 def pool_leg(torch, pk, steps, warmup):
@@ -462,7 +501,7 @@ def main():
         sweep = {}
         for cfg in (1, 2, 4):
             log(f"configuration {cfg}")
-            c, _ = make_config(cfg, seed=args.seed)
+            c, ca = make_config(cfg, seed=args.seed)
             a = Attn(c, pk, torch, R)
             ms = time_ms(torch, a, args.steps, args.warmup)
             kb = kv_logical_bytes(c.seq_lens, c.num_kv_heads, c.head_dim)
@@ -470,7 +509,16 @@ def main():
                                      "kv_gbps": round(kb / (ms * 1e-3) / 1e9, 2),
                                      "hbm_fraction": round(kb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                                      "decode_tokens_per_s": round(c.num_seqs / (ms * 1e-3), 1)}
-            del a
+            if ca is not None:   # a verify step: attention + accept
+                ac = Accept(ca, pk, torch, R)
+                ms_acc = time_ms(torch, ac, args.steps, args.warmup)
+                ac.win.copy_(ac.win0)
+                ac(0)
+                torch.cuda.synchronize()
+                got = int(ac.oa.sum().item())
+                sweep[f"config{cfg}"].update({"accept_us": round(ms_acc * 1e3, 3), "accepted_per_step": got,
+                                              "verified_tokens_per_s": round(got / ((ms + ms_acc) * 1e-3), 1)})
+                del ac
             torch.cuda.empty_cache()
         log("configuration 4 through the shared-prefix call")
         c, _ = make_config(4, seed=args.seed)
@@ -494,6 +542,9 @@ def main():
                             "kv_gbps": result["attn_kv_gbps"], "hbm_fraction": result["attn_hbm_fraction"]}
         result["configs"] = sweep
 
+    if not args.no_queue:
+        log("mixed job queue")
+        result["queue"] = queue_leg(torch, pk, args.seed, max(5, args.steps // 5), max(2, args.warmup // 2))
     if not args.no_prefill:
         result["prefill"] = prefill_leg(torch, pk, args.seed, max(5, args.steps // 5), max(2, args.warmup // 2))
     log("page allocator")

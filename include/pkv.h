@@ -75,6 +75,13 @@ typedef struct {
   int32_t total_q;           /* rows of q and out; must equal sum(q_lens)           */
   int32_t max_q_len;         /* 1 .. W * 256, >= every q_lens[b]; Hq/Hkv <= 64      */
   float scale;               /* softmax scale applied to q.k (e.g. 1/sqrt(D))       */
+  int32_t total_pages;       /* planning hint, >= 0: the pages the batch's sequences
+                                reference, sum of ceil(seq_len / 256), as the host
+                                knows it; 0 = unknown (every row taken as W pages).
+                                The key range is cut into splits from it, so a
+                                ragged batch keeps every CU busy; any value gives
+                                correct results, only the speed and the workspace
+                                size depend on it                                    */
 } pkv_attn_shape;
 
 /* Bytes of device workspace pkv_attn_fwd needs for this shape (0 on a bad
@@ -120,10 +127,11 @@ int pkv_attn_workspace_init(void* workspace, size_t bytes, void* stream);
  * total_q; q_len <= max_q_len; q_len <= seq_len <= W * 256; on the long-window
  * kernel also seq_len <= 2048 * 256 (longer sequences are skipped and flagged
  * PKV_EFLAG_QLEN).
- * Precision: fp32 scores and softmax; on matrix cores (rows >= 13) P enters
- * P.V rounded to bf16, except for the first 64 keys on the long-window kernel,
- * where it enters as two bf16 terms (rows with few keys would not average the
- * rounding out).
+ * Precision: fp32 scores and softmax; P enters P.V rounded to bf16 (rows =
+ * q_len * Hq/Hkv <= 4 run on VALU dot products, more rows on the matrix
+ * cores). On the long-window kernel P enters as two bf16 terms for the first
+ * 64 keys and wherever a key weighs more than 1/8 of its row sum so far (rows
+ * with few keys would not average the rounding out).
  */
 int pkv_attn_fwd(const void* q, const void* k_pool, const void* v_pool,
                  const int32_t* block_table, const int32_t* seq_lens, const int32_t* q_lens,

@@ -37,7 +37,8 @@ class pkv_attn_shape(ctypes.Structure):
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int32),
                 ("max_pages_per_seq", ctypes.c_int32), ("total_q", ctypes.c_int32),
-                ("max_q_len", ctypes.c_int32), ("scale", ctypes.c_float)]
+                ("max_q_len", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("total_pages", ctypes.c_int32)]
 
 
 class pkv_accept_shape(ctypes.Structure):
@@ -140,15 +141,16 @@ def _need(t, dtype, name):
         raise ValueError(f"{name} must live on the GPU")
 
 
-def attn_shape(q, k_pool, block_table, max_q_len, scale):
+def attn_shape(q, k_pool, block_table, max_q_len, scale, total_pages=0):
     """pkv_attn_shape from tensor extents (q [total_q, Hq, D], pool [P, Hkv, 256, D],
-    block_table [B, W])."""
+    block_table [B, W]); total_pages is the host's count of referenced pages
+    (sum of ceil(seq_len / 256)), a planning hint, 0 if unknown."""
     total_q, Hq, D = q.shape
     P, Hkv, page, D2 = k_pool.shape
     B, W = block_table.shape
     if D2 != D:
         raise ValueError("q and pool head_dim differ")
-    return pkv_attn_shape(B, Hq, Hkv, D, page, P, W, total_q, int(max_q_len), float(scale))
+    return pkv_attn_shape(B, Hq, Hkv, D, page, P, W, total_q, int(max_q_len), float(scale), int(total_pages))
 
 
 def pkv_attn_workspace_bytes(shape):

@@ -20,11 +20,12 @@
 //
 // Row tiles. The q rows that share KV head g are the window rows times the
 // head group (rows = q_len * Hq/Hkv):
-//  * rows <= 12: VALU tile. Scores: one lane per (row group, token), bf16
-//    pairs through v_dot2_f32_bf16 against a token row read from the
-//    XOR-swizzled LDS tile; row maxima by DPP within 16-lane rows. P.V: one
-//    lane per (token group, 8-dim chunk) in fp32 FMA, P read back from LDS.
-//  * rows >= 13: MFMA tile (v_mfma_f32_32x32x16_bf16), rows padded to 32 or
+//  * rows <= 4 (decode with a head group of up to 4): VALU tile. Scores: one
+//    lane per (row group, token), bf16 pairs through v_dot2_f32_bf16 against
+//    a token row read from the XOR-swizzled LDS tile; row maxima by DPP
+//    within 16-lane rows. P.V: one lane per (token group, 8-dim chunk) in
+//    fp32 FMA, P read back from LDS.
+//  * rows >= 5: MFMA tile (v_mfma_f32_32x32x16_bf16), rows padded to 32 or
 //    64. S^T = K . Q^T puts one q row in each lane column, so the softmax
 //    state and the rescale of O^T are per lane; O^T += V^T . P^T takes P from
 //    registers (rounded to bf16) and V^T by 16-bit LDS reads.
@@ -78,6 +79,7 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr u32 PKV_EFLAG_PAGE_BIT = 1u, PKV_EFLAG_QLEN_BIT = 2u, PKV_EFLAG_ROWS_BIT = 4u;
 constexpr int kNumCu = 256;           // MI355X compute units
+constexpr int kValuMaxRows = 4;       // q rows per (sequence, KV head) on the VALU tile
 constexpr int kLdsPerCu = 160 * 1024;  // gfx950 LDS per CU
 constexpr float kNegInf = -__builtin_inff();
 
@@ -193,7 +195,9 @@ struct TileGeom {
   static_assert(TC * NC % 64 == 0, "chunk must fill whole load instructions");
 };
 
-// VALU row tile: rows = 4 * RPL (RPL q rows per lane in the score phase).
+// VALU row tile: rows = 4 * RPL (RPL q rows per lane in the score phase);
+// launched with RPL = 1, where it beats the matrix cores (8 and 12 rows run
+// faster on the MFMA tile).
 template <int D, int RPL>
 struct ValuTile {
   static constexpr int TC = 16;
@@ -792,16 +796,20 @@ __global__ __launch_bounds__(WAVES * 64) void attn_split_kernel(
   __shared__ int s_pages[C::MAX_PPS];
   __shared__ int s_last;
 
-  // XCD-aware item order: consecutive logical items (the same split and KV
-  // head over consecutive sequences, which share prefix pages under dedup)
-  // land on the same XCD and its L2.
-  const int per_xcd = (num_items + kNumXcd - 1) / kNumXcd;
-  const int item = (blockIdx.x % kNumXcd) * per_xcd + blockIdx.x / kNumXcd;
-  if (item >= num_items) return;
-  const int b = item % B;
-  const int rest = item / B;
-  const int g = rest % Hkv;
-  const int s = rest / Hkv;
+  // XCD-aware item order. The dispatcher deals workgroup i to XCD i % 8; XCD
+  // x takes the (KV head, split) pairs j = x, x + 8, ... (j = g + Hkv * s) in
+  // turn, each pair's sequences consecutively. So the sequences of one pair,
+  // which share prefix pages under dedup, read them through one L2; every XCD
+  // gets the same mix of early splits (work for every sequence) and late ones
+  // (only long sequences have them); and a ragged batch's empty items come
+  // last in each XCD's queue.
+  const int pairs = num_items / B;
+  const int xcd = blockIdx.x % kNumXcd, k = blockIdx.x / kNumXcd;
+  const int b = k % B;
+  const int j = xcd + kNumXcd * (k / B);
+  if (j >= pairs) return;
+  const int g = j % Hkv;
+  const int s = j / Hkv;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
 
   // independent loads first, so their latencies overlap: the sequence's
@@ -1453,8 +1461,9 @@ __global__ __launch_bounds__(256) void shared_merge_kernel(SharedParams sp, Attn
 
 template <int D, class Tile, int NBUF, int WAVES>
 hipError_t launch_one(const AttnParams& p, hipStream_t stream) {
-  const int per_xcd = (p.num_items + kNumXcd - 1) / kNumXcd;
-  const int grid = per_xcd * kNumXcd;
+  // every XCD gets ceil(pairs / 8) pairs of B items (see the kernel)
+  const int pairs = p.num_items / p.B;
+  const int grid = kNumXcd * ((pairs + kNumXcd - 1) / kNumXcd) * p.B;
   hipLaunchKernelGGL((attn_split_kernel<D, Tile, NBUF, WAVES>), dim3(grid), dim3(WAVES * 64), 0, stream,
                      p.block_table, p.seq_lens, p.q_lens, p.num_items, p.B, p.Hkv, p.pps, p.W, p);
   return hipGetLastError();
@@ -1462,24 +1471,21 @@ hipError_t launch_one(const AttnParams& p, hipStream_t stream) {
 
 template <int D>
 hipError_t launch_d(const AttnParams& p, const AttnPlan& plan, hipStream_t stream) {
-  if (!plan.mfma) {
-    const int rpl = (plan.rows + 3) / 4;
-    switch (rpl) {
-      case 1: return launch_one<D, ValuTile<D, 1>, PKV_VALU_NBUF, PKV_VALU_WAVES>(p, stream);
-      case 2: return launch_one<D, ValuTile<D, 2>, PKV_VALU_NBUF, PKV_VALU_WAVES>(p, stream);
-      default: return launch_one<D, ValuTile<D, 3>, PKV_VALU_NBUF, PKV_VALU_WAVES>(p, stream);
-    }
-  }
+  if (!plan.mfma) return launch_one<D, ValuTile<D, 1>, PKV_VALU_NBUF, PKV_VALU_WAVES>(p, stream);
   if (plan.rows <= 32) return launch_one<D, MfmaTile<D, 1>, PKV_MFMA_NBUF, PKV_MFMA_WAVES>(p, stream);
   return launch_one<D, MfmaTile<D, 2>, PKV_MFMA_NBUF, PKV_MFMA_WAVES>(p, stream);
 }
 
 }  // namespace
 
-AttnPlan attn_plan(int B, int Hkv, int W, int max_q_len, int group) {
+AttnPlan attn_plan(int B, int Hkv, int W, int max_q_len, int group, long total_pages) {
   AttnPlan pl;
   pl.rows = max_q_len * group;
-  pl.mfma = pl.rows > 12;
+  // VALU dot products for up to 4 rows (decode with a group of 4); from 5
+  // rows the matrix cores: measured on 8 x 8192 tokens, 8 rows 70.0 -> 56.1
+  // us and 12 rows 95.7 -> 56.3 us, where the VALU tile's per-row work stops
+  // hiding under the K/V stream
+  pl.mfma = pl.rows > kValuMaxRows;
   pl.prefill = pl.rows > PKV_MAX_ROWS;
   pl.qtok = kPrefillRows / group;
   pl.tiles = (max_q_len + pl.qtok - 1) / pl.qtok;
@@ -1494,13 +1500,15 @@ AttnPlan attn_plan(int B, int Hkv, int W, int max_q_len, int group) {
     smem = pl.rows <= 32 ? KernelCfg<128, MfmaTile<128, 1>, PKV_MFMA_NBUF, PKV_MFMA_WAVES>::SMEM
                          : KernelCfg<128, MfmaTile<128, 2>, PKV_MFMA_NBUF, PKV_MFMA_WAVES>::SMEM;
   else
-    smem = KernelCfg<128, ValuTile<128, 3>, PKV_VALU_NBUF, PKV_VALU_WAVES>::SMEM;
+    smem = KernelCfg<128, ValuTile<128, 1>, PKV_VALU_NBUF, PKV_VALU_WAVES>::SMEM;
   int per_cu = kLdsPerCu / smem;
   if (per_cu < 1) per_cu = 1;
   // Pages per split: as few splits as keep one round of workgroups on every
   // CU. Each extra split costs a partial write and read plus a merge; an
-  // idle CU costs more. The table width bounds every sequence's pages.
-  const long tiles = (long)B * Hkv * W;
+  // idle CU costs more. The pages the batch references (the caller's count,
+  // else the table width for every row) spread over the CUs.
+  const long pages = total_pages > 0 ? total_pages : (long)B * W;
+  const long tiles = pages * Hkv;
   const long slots = (long)kNumCu * per_cu;
   long pps = (tiles + slots - 1) / slots;
   if (PKV_FORCE_PPS > 0) pps = PKV_FORCE_PPS;
@@ -1514,8 +1522,8 @@ AttnPlan attn_plan(int B, int Hkv, int W, int max_q_len, int group) {
 
 static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-AttnWorkspace attn_workspace(int B, int Hkv, int W, int max_q_len, int group, int D) {
-  const AttnPlan pl = attn_plan(B, Hkv, W, max_q_len, group);
+AttnWorkspace attn_workspace(int B, int Hkv, int W, int max_q_len, int group, int D, long total_pages) {
+  const AttnPlan pl = attn_plan(B, Hkv, W, max_q_len, group, total_pages);
   AttnWorkspace ws;
   const size_t items = pl.prefill ? 0 : (size_t)B * Hkv * pl.max_splits;
   ws.err_off = 0;

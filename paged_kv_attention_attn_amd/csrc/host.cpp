@@ -5,6 +5,7 @@
 #include "pkv.h"
 #include "internal.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 
@@ -21,10 +22,12 @@ bool attn_shape_ok(const pkv_attn_shape* s) {
   if (s->max_q_len < 1 || (long)s->max_q_len > (long)s->max_pages_per_seq * PKV_PAGE_SIZE) return false;
   if (s->num_q_heads / s->num_kv_heads > PKV_MAX_ROWS) return false;
   if (!std::isfinite(s->scale)) return false;
+  if (s->total_pages < 0) return false;
   // 32-bit indexing limits inside the kernels
   if ((long)s->num_seqs * s->max_pages_per_seq > (1L << 31) - 1) return false;
   if ((long)s->num_pages * s->num_kv_heads * PKV_PAGE_SIZE * s->head_dim > (1L << 40)) return false;
-  if ((long)s->num_seqs * s->num_kv_heads * s->max_pages_per_seq > (1L << 30)) return false;
+  // work items, with every XCD's share of (KV head, split) pairs padded to a whole pair
+  if ((long)s->num_seqs * ((long)s->num_kv_heads * s->max_pages_per_seq + 8) > (1L << 30)) return false;
   if ((long)s->total_q * s->num_q_heads * s->head_dim * 2 >= (1L << 32)) return false;  // q buffer offsets
   return true;
 }
@@ -132,8 +135,10 @@ SharedLayout shared_layout(const pkv_attn_shape* s, int32_t shared_pages) {
   SharedLayout L;
   const int group = s->num_q_heads / s->num_kv_heads;
   const int tail_w = s->max_pages_per_seq - shared_pages;
-  L.tail = pkv::attn_workspace(s->num_seqs, s->num_kv_heads, tail_w, s->max_q_len, group, s->head_dim);
-  L.plan = pkv::attn_plan(s->num_seqs, s->num_kv_heads, tail_w, s->max_q_len, group);
+  // the tails reference the batch's pages less the shared ones of every row
+  const long tail_pages = s->total_pages > 0 ? std::max(1L, s->total_pages - (long)s->num_seqs * shared_pages) : 0;
+  L.tail = pkv::attn_workspace(s->num_seqs, s->num_kv_heads, tail_w, s->max_q_len, group, s->head_dim, tail_pages);
+  L.plan = pkv::attn_plan(s->num_seqs, s->num_kv_heads, tail_w, s->max_q_len, group, tail_pages);
   L.sp = pkv::shared_plan(s->num_kv_heads, s->total_q, group, shared_pages);
   const size_t rows = (size_t)s->total_q * group;
   L.lse_off = align256(L.tail.total);
@@ -151,7 +156,7 @@ size_t pkv_attn_workspace_bytes(const pkv_attn_shape* s) {
   if (!attn_shape_ok(s)) return 0;
   const int group = s->num_q_heads / s->num_kv_heads;
   return pkv::attn_workspace(s->num_seqs, s->num_kv_heads, s->max_pages_per_seq, s->max_q_len, group,
-                             s->head_dim)
+                             s->head_dim, s->total_pages)
       .total;
 }
 
@@ -171,10 +176,10 @@ int pkv_attn_fwd(const void* q, const void* k_pool, const void* v_pool, const in
   if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !q_lens || !out) return PKV_ERR_NULL;
   const int group = s->num_q_heads / s->num_kv_heads;
   const pkv::AttnWorkspace ws = pkv::attn_workspace(s->num_seqs, s->num_kv_heads, s->max_pages_per_seq,
-                                                    s->max_q_len, group, s->head_dim);
+                                                    s->max_q_len, group, s->head_dim, s->total_pages);
   if (!workspace || workspace_bytes < ws.total) return PKV_ERR_WORKSPACE;
   const pkv::AttnPlan plan = pkv::attn_plan(s->num_seqs, s->num_kv_heads, s->max_pages_per_seq,
-                                            s->max_q_len, group);
+                                            s->max_q_len, group, s->total_pages);
   const pkv::AttnParams p =
       attn_params(q, k_pool, v_pool, block_table, seq_lens, q_lens, out, s, workspace, ws, plan, 0);
   if (pkv::launch_attn(p, plan, static_cast<hipStream_t>(stream)) != hipSuccess) return PKV_ERR_HIP;

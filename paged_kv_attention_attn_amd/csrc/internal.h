@@ -58,11 +58,11 @@ struct SharedPlan {
   int splits, split_keys, row_tiles;
 };
 
-AttnPlan attn_plan(int B, int Hkv, int W, int max_q_len, int group);
+AttnPlan attn_plan(int B, int Hkv, int W, int max_q_len, int group, long total_pages);
 SharedPlan shared_plan(int Hkv, int total_q, int group, int shared_pages);
 hipError_t launch_attn_shared(const AttnParams& p, const SharedParams& sp, hipStream_t stream);
 hipError_t launch_shared_merge(const AttnParams& p, const SharedParams& sp, hipStream_t stream);
-AttnWorkspace attn_workspace(int B, int Hkv, int W, int max_q_len, int group, int D);
+AttnWorkspace attn_workspace(int B, int Hkv, int W, int max_q_len, int group, int D, long total_pages);
 hipError_t launch_attn(const AttnParams& p, const AttnPlan& plan, hipStream_t stream);
 
 struct AcceptParams {

@@ -26,7 +26,7 @@ def dev_i32(a):
 class DeviceCase:
     """A case resident on the GPU plus its workspace."""
 
-    def __init__(self, case, pk, max_q_len=None, table_width=None):
+    def __init__(self, case, pk, max_q_len=None, table_width=None, total_pages=0):
         self.case = case
         self.pk = pk
         bt = case.block_table
@@ -40,7 +40,7 @@ class DeviceCase:
         self.sl = dev_i32(case.seq_lens)
         self.ql = dev_i32(case.q_lens)
         mq = max_q_len if max_q_len is not None else max(1, case.max_q_len)
-        self.shape = pk.attn_shape(self.q, self.k, self.bt, mq, case.scale)
+        self.shape = pk.attn_shape(self.q, self.k, self.bt, mq, case.scale, total_pages)
         self.ws = pk.new_attn_workspace(self.shape)
         self.out = torch.empty(case.q.shape, dtype=torch.float32, device="cuda")
 

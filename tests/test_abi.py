@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(pk):
 
 
 def test_struct_layouts_match_the_header(pk):
-    assert ctypes.sizeof(pk.pkv_attn_shape) == 40
+    assert ctypes.sizeof(pk.pkv_attn_shape) == 44
     assert ctypes.sizeof(pk.pkv_accept_shape) == 16
     assert ctypes.sizeof(pk.pkv_kv_shape) == 28
 
@@ -69,6 +69,7 @@ def good_shape(pk, **kw):
     dict(num_q_heads=8 * 65),             # a head group wider than 64 rows
     dict(num_pages=0), dict(max_pages_per_seq=0), dict(num_seqs=-1),
     dict(scale=float("nan")),
+    dict(total_pages=-1),                 # the planning hint counts pages
 ])
 def test_bad_attention_shapes_are_rejected_before_launch(pk, bad):
     s = good_shape(pk, **bad)
@@ -192,3 +193,16 @@ def test_allocator_calls_reject_null_and_bad_sizes(pk):
         assert pk.pkv_status_string(pk.PKV_ERR_SPACE) and pk.pkv_status_string(pk.PKV_ERR_STATE)
     finally:
         pk.pkv_pool_destroy(pool)
+
+
+def test_page_hint_sizes_the_workspace_for_more_splits(pk):
+    """A batch referencing fewer pages than B x W is cut into shorter splits:
+    more partial slots, so at least as much workspace; no hint plans as if
+    every row were full."""
+    full = pk.pkv_attn_workspace_bytes(good_shape(pk, num_seqs=16, total_q=16, max_pages_per_seq=64))
+    same = pk.pkv_attn_workspace_bytes(good_shape(pk, num_seqs=16, total_q=16, max_pages_per_seq=64,
+                                                  total_pages=16 * 64))
+    ragged = pk.pkv_attn_workspace_bytes(good_shape(pk, num_seqs=16, total_q=16, max_pages_per_seq=64,
+                                                    total_pages=200))
+    assert full == same > 0
+    assert ragged > full

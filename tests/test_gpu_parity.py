@@ -26,19 +26,21 @@ def oracle_attn(case):
                             case.q_lens, case.scale)
 
 
-# shapes chosen to exercise both row tiles (VALU rows 1..12, MFMA 13..64),
+# shapes chosen to exercise both row tiles (VALU rows 1..4, MFMA 5..64),
 # both head dims, page boundaries, ragged tails and several splits
 TINY = [
     # seq_lens, q_lens, Hq, Hkv, D
     ([1], [1], 1, 1, 64),
     ([300], [1], 8, 2, 64),
     ([17, 256, 257, 511], [1, 1, 1, 1], 4, 2, 128),
-    ([700, 33], [3, 2], 8, 2, 128),           # VALU 12 rows
+    ([700, 33], [3, 2], 8, 2, 128),           # MFMA 12 rows (3-row window, group 4)
     ([1030], [2], 8, 4, 64),                  # VALU 4 rows with group 2
     ([600, 256, 1], [6, 5, 1], 8, 2, 128),    # MFMA 24 rows / 20 rows
     ([1500, 40], [7, 4], 8, 2, 64),           # MFMA 28 rows
     ([2100], [16], 16, 4, 128),               # MFMA 64 rows (two row blocks)
-    ([513, 777], [16, 9], 4, 4, 128),         # MHA: 16 rows -> MFMA, 9 rows -> VALU path mixed
+    ([513, 777], [16, 9], 4, 4, 128),         # MHA: 16 rows, the 9-row window padded in the same tile
+    ([900, 50], [2, 1], 8, 2, 128),           # MFMA 8 rows, the smallest window past the VALU tile
+    ([640, 3], [1, 1], 10, 2, 64),            # MFMA 5 rows: a head group of 5 in decode
     ([4096, 100, 2], [1, 1, 1], 32, 8, 128),
     ([258], [6], 32, 8, 128),                 # window straddles a page boundary
     ([3000], [5], 2, 1, 64),
