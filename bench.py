@@ -118,9 +118,9 @@ class Attn:
         self.q = dev(case.q)
         self.bt, self.sl, self.ql = i32(case.block_table), i32(case.seq_lens), i32(case.q_lens)
         self.out = torch.empty(case.q.shape, dtype=torch.float32, device="cuda")
-        # the host knows the lengths: its page count plans the splits
-        pages = int(sum(-(-int(n) // 256) for n in case.seq_lens))
-        self.shape = pk.attn_shape(self.q, k0, self.bt, max(1, case.max_q_len), case.scale, pages)
+        # the host knows the lengths: they plan the splits
+        self.shape = pk.pkv_attn_plan(pk.attn_shape(self.q, k0, self.bt, max(1, case.max_q_len), case.scale),
+                                      case.seq_lens)
         self.ws = pk.new_attn_workspace(self.shape)
         self.R = replicas
 

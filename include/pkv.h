@@ -82,6 +82,9 @@ typedef struct {
                                 ragged batch keeps every CU busy; any value gives
                                 correct results, only the speed and the workspace
                                 size depend on it                                    */
+  int32_t pages_per_split;   /* 0..64: pages of K/V one workgroup streams; 0 = derived
+                                from total_pages (pkv_attn_plan sets both from the
+                                host's lengths). Speed and workspace size only     */
 } pkv_attn_shape;
 
 /* Bytes of device workspace pkv_attn_fwd needs for this shape (0 on a bad
@@ -90,6 +93,16 @@ typedef struct {
  * before its first use and again before it is reused for a different shape
  * (pkv_attn_workspace_init does it); every call leaves the counters at zero. */
 size_t pkv_attn_workspace_bytes(const pkv_attn_shape* shape);
+
+/* Host-side plan for a batch whose lengths the host knows (seq_lens_host:
+ * num_seqs int32 in host memory, read only; values past max_pages_per_seq * 256
+ * count as that). Sets shape->total_pages and shape->pages_per_split to the
+ * split length that models fastest: rounds of workgroups over the chip times
+ * (split pages + a workgroup's fixed cost), so a ragged batch neither leaves
+ * CUs idle behind a few long splits nor spills a second round of workgroups.
+ * Only speed and pkv_attn_workspace_bytes change; results stay correct for any
+ * plan. Returns PKV_OK, PKV_ERR_NULL or PKV_ERR_SHAPE. */
+int pkv_attn_plan(pkv_attn_shape* shape, const int32_t* seq_lens_host);
 
 /* Enqueue a zero fill of `bytes` bytes of workspace on `stream`. */
 int pkv_attn_workspace_init(void* workspace, size_t bytes, void* stream);

@@ -29,7 +29,7 @@ EXPORTS = ("pkv_attn_workspace_bytes", "pkv_attn_workspace_init", "pkv_attn_fwd"
            "pkv_kv_append", "pkv_kv_rollback", "pkv_kv_check_errors", "pkv_pool_create",
            "pkv_pool_destroy", "pkv_pool_stats", "pkv_pool_admit", "pkv_pool_alloc", "pkv_pool_retain",
            "pkv_pool_release", "pkv_pool_defrag", "pkv_pool_copy_pages", "pkv_table_remap",
-           "pkv_attn_shared_workspace_bytes", "pkv_attn_fwd_shared")
+           "pkv_attn_shared_workspace_bytes", "pkv_attn_fwd_shared", "pkv_attn_plan")
 
 
 class pkv_attn_shape(ctypes.Structure):
@@ -38,7 +38,7 @@ class pkv_attn_shape(ctypes.Structure):
                 ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int32),
                 ("max_pages_per_seq", ctypes.c_int32), ("total_q", ctypes.c_int32),
                 ("max_q_len", ctypes.c_int32), ("scale", ctypes.c_float),
-                ("total_pages", ctypes.c_int32)]
+                ("total_pages", ctypes.c_int32), ("pages_per_split", ctypes.c_int32)]
 
 
 class pkv_accept_shape(ctypes.Structure):
@@ -65,6 +65,8 @@ def _load():
     vp, sz, i32p = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p
     lib.pkv_attn_workspace_bytes.argtypes = [ctypes.POINTER(pkv_attn_shape)]
     lib.pkv_attn_workspace_bytes.restype = sz
+    lib.pkv_attn_plan.argtypes = [ctypes.POINTER(pkv_attn_shape), vp]
+    lib.pkv_attn_plan.restype = ctypes.c_int
     lib.pkv_attn_workspace_init.argtypes = [vp, sz, vp]
     lib.pkv_attn_workspace_init.restype = ctypes.c_int
     lib.pkv_attn_fwd.argtypes = [vp, vp, vp, i32p, i32p, i32p, vp, ctypes.POINTER(pkv_attn_shape),
@@ -150,7 +152,17 @@ def attn_shape(q, k_pool, block_table, max_q_len, scale, total_pages=0):
     B, W = block_table.shape
     if D2 != D:
         raise ValueError("q and pool head_dim differ")
-    return pkv_attn_shape(B, Hq, Hkv, D, page, P, W, total_q, int(max_q_len), float(scale), int(total_pages))
+    return pkv_attn_shape(B, Hq, Hkv, D, page, P, W, total_q, int(max_q_len), float(scale), int(total_pages), 0)
+
+
+def pkv_attn_plan(shape, seq_lens_host):
+    """Set shape.total_pages and shape.pages_per_split from host-side lengths
+    (any int sequence or numpy array); returns the shape."""
+    lens = np.ascontiguousarray(seq_lens_host, dtype=np.int32)
+    if lens.size != shape.num_seqs:
+        raise ValueError(f"pkv_attn_plan: {lens.size} lengths for {shape.num_seqs} sequences")
+    _check(LIB.pkv_attn_plan(ctypes.byref(shape), lens.ctypes.data_as(ctypes.c_void_p)), "pkv_attn_plan")
+    return shape
 
 
 def pkv_attn_workspace_bytes(shape):

@@ -1478,7 +1478,26 @@ hipError_t launch_d(const AttnParams& p, const AttnPlan& plan, hipStream_t strea
 
 }  // namespace
 
-AttnPlan attn_plan(int B, int Hkv, int W, int max_q_len, int group, long total_pages) {
+namespace {
+
+// Workgroups of the decode / verify kernel that one round puts on the chip:
+// the CUs times the workgroups one CU holds (its LDS decides).
+long attn_slots(const AttnPlan& pl) {
+  int smem;
+  if (pl.mfma)
+    smem = pl.rows <= 32 ? KernelCfg<128, MfmaTile<128, 1>, PKV_MFMA_NBUF, PKV_MFMA_WAVES>::SMEM
+                         : KernelCfg<128, MfmaTile<128, 2>, PKV_MFMA_NBUF, PKV_MFMA_WAVES>::SMEM;
+  else
+    smem = KernelCfg<128, ValuTile<128, 1>, PKV_VALU_NBUF, PKV_VALU_WAVES>::SMEM;
+  const int per_cu = kLdsPerCu / smem;
+  return (long)kNumCu * (per_cu < 1 ? 1 : per_cu);
+}
+
+constexpr int kMaxPps = 64;  // the kernel stages at most 64 table entries per split
+
+}  // namespace
+
+AttnPlan attn_plan(int B, int Hkv, int W, int max_q_len, int group, long total_pages, int pages_per_split) {
   AttnPlan pl;
   pl.rows = max_q_len * group;
   // VALU dot products for up to 4 rows (decode with a group of 4); from 5
@@ -1494,36 +1513,66 @@ AttnPlan attn_plan(int B, int Hkv, int W, int max_q_len, int group, long total_p
     pl.max_splits = 1;
     return pl;
   }
-  // Workgroups resident per CU, from the LDS each variant claims.
-  int smem;
-  if (pl.mfma)
-    smem = pl.rows <= 32 ? KernelCfg<128, MfmaTile<128, 1>, PKV_MFMA_NBUF, PKV_MFMA_WAVES>::SMEM
-                         : KernelCfg<128, MfmaTile<128, 2>, PKV_MFMA_NBUF, PKV_MFMA_WAVES>::SMEM;
-  else
-    smem = KernelCfg<128, ValuTile<128, 1>, PKV_VALU_NBUF, PKV_VALU_WAVES>::SMEM;
-  int per_cu = kLdsPerCu / smem;
-  if (per_cu < 1) per_cu = 1;
-  // Pages per split: as few splits as keep one round of workgroups on every
-  // CU. Each extra split costs a partial write and read plus a merge; an
-  // idle CU costs more. The pages the batch references (the caller's count,
-  // else the table width for every row) spread over the CUs.
-  const long pages = total_pages > 0 ? total_pages : (long)B * W;
-  const long tiles = pages * Hkv;
-  const long slots = (long)kNumCu * per_cu;
-  long pps = (tiles + slots - 1) / slots;
+  long pps;
+  if (pages_per_split > 0) {
+    pps = pages_per_split;  // the caller's plan (attn_best_pps on its lengths)
+  } else {
+    // As few splits as keep one round of workgroups on every CU. Each extra
+    // split costs a partial write and read plus a merge; an idle CU costs
+    // more. The pages the batch references (the caller's count, else the
+    // table width for every row) spread over the CUs.
+    const long pages = total_pages > 0 ? total_pages : (long)B * W;
+    const long slots = attn_slots(pl);
+    pps = (pages * Hkv + slots - 1) / slots;
+  }
   if (PKV_FORCE_PPS > 0) pps = PKV_FORCE_PPS;
   if (pps < 1) pps = 1;
   if (pps > W) pps = W;
-  if (pps > 64) pps = 64;  // the kernel stages at most 64 table entries per split
+  if (pps > kMaxPps) pps = kMaxPps;
   pl.pps = (int)pps;
   pl.max_splits = (W + pl.pps - 1) / pl.pps;
   return pl;
 }
 
+int attn_best_pps(int B, int Hkv, int W, int max_q_len, int group, int D, const int32_t* seq_lens) {
+  AttnPlan pl = attn_plan(B, Hkv, W, max_q_len, group, 0, 0);
+  if (pl.prefill) return 0;
+  const long slots = attn_slots(pl);
+  // A workgroup's fixed cost (table and q loads before its first page
+  // arrives, the partial stores and merge after its last), in page-stream
+  // times: about 11 us against 5 us per 128 KiB page of K and V (head_dim
+  // 128) at a CU's share of the HBM rate.
+  const long overhead = D >= 128 ? 2 : 4;
+  const int top = W < kMaxPps ? W : kMaxPps;
+  long best_cost = -1;
+  int best = 1;
+  for (int pps = 1; pps <= top; ++pps) {
+    long busy = 0;
+    for (int b = 0; b < B; ++b) {
+      long n = seq_lens[b] > 0 ? seq_lens[b] : 0;
+      if (n > (long)W * kPage) n = (long)W * kPage;
+      const long pages = (n + kPage - 1) / kPage;
+      busy += (pages + pps - 1) / pps;
+    }
+    busy *= Hkv;
+    long rounds = (busy + slots - 1) / slots;
+    if (rounds < 1) rounds = 1;
+    // a split's time ~ its pages plus the fixed cost; ties go to longer
+    // splits (fewer partials to merge)
+    const long cost = rounds * (pps + overhead);
+    if (best_cost < 0 || cost <= best_cost) {
+      best_cost = cost;
+      best = pps;
+    }
+  }
+  return best;
+}
+
 static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-AttnWorkspace attn_workspace(int B, int Hkv, int W, int max_q_len, int group, int D, long total_pages) {
-  const AttnPlan pl = attn_plan(B, Hkv, W, max_q_len, group, total_pages);
+AttnWorkspace attn_workspace(int B, int Hkv, int W, int max_q_len, int group, int D, long total_pages,
+                             int pages_per_split) {
+  const AttnPlan pl = attn_plan(B, Hkv, W, max_q_len, group, total_pages, pages_per_split);
   AttnWorkspace ws;
   const size_t items = pl.prefill ? 0 : (size_t)B * Hkv * pl.max_splits;
   ws.err_off = 0;

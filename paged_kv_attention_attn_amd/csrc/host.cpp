@@ -6,6 +6,7 @@
 #include "internal.h"
 
 #include <algorithm>
+#include <climits>
 #include <cmath>
 #include <cstring>
 
@@ -23,6 +24,7 @@ bool attn_shape_ok(const pkv_attn_shape* s) {
   if (s->num_q_heads / s->num_kv_heads > PKV_MAX_ROWS) return false;
   if (!std::isfinite(s->scale)) return false;
   if (s->total_pages < 0) return false;
+  if (s->pages_per_split < 0 || s->pages_per_split > 64) return false;
   // 32-bit indexing limits inside the kernels
   if ((long)s->num_seqs * s->max_pages_per_seq > (1L << 31) - 1) return false;
   if ((long)s->num_pages * s->num_kv_heads * PKV_PAGE_SIZE * s->head_dim > (1L << 40)) return false;
@@ -137,8 +139,10 @@ SharedLayout shared_layout(const pkv_attn_shape* s, int32_t shared_pages) {
   const int tail_w = s->max_pages_per_seq - shared_pages;
   // the tails reference the batch's pages less the shared ones of every row
   const long tail_pages = s->total_pages > 0 ? std::max(1L, s->total_pages - (long)s->num_seqs * shared_pages) : 0;
-  L.tail = pkv::attn_workspace(s->num_seqs, s->num_kv_heads, tail_w, s->max_q_len, group, s->head_dim, tail_pages);
-  L.plan = pkv::attn_plan(s->num_seqs, s->num_kv_heads, tail_w, s->max_q_len, group, tail_pages);
+  // (a split length the caller planned for whole rows does not carry over)
+  L.tail =
+      pkv::attn_workspace(s->num_seqs, s->num_kv_heads, tail_w, s->max_q_len, group, s->head_dim, tail_pages, 0);
+  L.plan = pkv::attn_plan(s->num_seqs, s->num_kv_heads, tail_w, s->max_q_len, group, tail_pages, 0);
   L.sp = pkv::shared_plan(s->num_kv_heads, s->total_q, group, shared_pages);
   const size_t rows = (size_t)s->total_q * group;
   L.lse_off = align256(L.tail.total);
@@ -156,8 +160,24 @@ size_t pkv_attn_workspace_bytes(const pkv_attn_shape* s) {
   if (!attn_shape_ok(s)) return 0;
   const int group = s->num_q_heads / s->num_kv_heads;
   return pkv::attn_workspace(s->num_seqs, s->num_kv_heads, s->max_pages_per_seq, s->max_q_len, group,
-                             s->head_dim, s->total_pages)
+                             s->head_dim, s->total_pages, s->pages_per_split)
       .total;
+}
+
+int pkv_attn_plan(pkv_attn_shape* s, const int32_t* seq_lens_host) {
+  if (!s) return PKV_ERR_NULL;
+  if (!attn_shape_ok(s)) return PKV_ERR_SHAPE;
+  if (s->num_seqs > 0 && !seq_lens_host) return PKV_ERR_NULL;
+  long pages = 0;
+  for (int b = 0; b < s->num_seqs; ++b) {
+    long n = std::min<long>(std::max<int32_t>(seq_lens_host[b], 0), (long)s->max_pages_per_seq * PKV_PAGE_SIZE);
+    pages += (n + PKV_PAGE_SIZE - 1) / PKV_PAGE_SIZE;
+  }
+  const int group = s->num_q_heads / s->num_kv_heads;
+  s->total_pages = (int32_t)std::min<long>(pages, INT32_MAX);
+  s->pages_per_split = pkv::attn_best_pps(s->num_seqs, s->num_kv_heads, s->max_pages_per_seq, s->max_q_len, group,
+                                          s->head_dim, seq_lens_host);
+  return PKV_OK;
 }
 
 int pkv_attn_workspace_init(void* workspace, size_t bytes, void* stream) {
@@ -176,10 +196,11 @@ int pkv_attn_fwd(const void* q, const void* k_pool, const void* v_pool, const in
   if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !q_lens || !out) return PKV_ERR_NULL;
   const int group = s->num_q_heads / s->num_kv_heads;
   const pkv::AttnWorkspace ws = pkv::attn_workspace(s->num_seqs, s->num_kv_heads, s->max_pages_per_seq,
-                                                    s->max_q_len, group, s->head_dim, s->total_pages);
+                                                    s->max_q_len, group, s->head_dim, s->total_pages,
+                                                    s->pages_per_split);
   if (!workspace || workspace_bytes < ws.total) return PKV_ERR_WORKSPACE;
   const pkv::AttnPlan plan = pkv::attn_plan(s->num_seqs, s->num_kv_heads, s->max_pages_per_seq,
-                                            s->max_q_len, group, s->total_pages);
+                                            s->max_q_len, group, s->total_pages, s->pages_per_split);
   const pkv::AttnParams p =
       attn_params(q, k_pool, v_pool, block_table, seq_lens, q_lens, out, s, workspace, ws, plan, 0);
   if (pkv::launch_attn(p, plan, static_cast<hipStream_t>(stream)) != hipSuccess) return PKV_ERR_HIP;

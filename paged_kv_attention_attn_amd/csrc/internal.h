@@ -41,7 +41,7 @@ struct AttnPlan {
   int pps;
   int max_splits;
   int rows;      // rows_max = max_q_len * group
-  bool mfma;     // row tile on matrix cores (rows >= 16)
+  bool mfma;     // row tile on matrix cores (rows >= 5)
   bool prefill;  // rows > PKV_MAX_ROWS: the long-window kernel
   int qtok;      // prefill: window tokens per query tile
   int tiles;     // prefill: query tiles of the longest window
@@ -58,11 +58,16 @@ struct SharedPlan {
   int splits, split_keys, row_tiles;
 };
 
-AttnPlan attn_plan(int B, int Hkv, int W, int max_q_len, int group, long total_pages);
+AttnPlan attn_plan(int B, int Hkv, int W, int max_q_len, int group, long total_pages, int pages_per_split);
+// Pages per split for these host-side lengths: the least modelled time
+// (rounds of workgroups x (split pages + a workgroup's fixed cost)); 0 for
+// shapes on the long-window kernel.
+int attn_best_pps(int B, int Hkv, int W, int max_q_len, int group, int D, const int32_t* seq_lens);
 SharedPlan shared_plan(int Hkv, int total_q, int group, int shared_pages);
 hipError_t launch_attn_shared(const AttnParams& p, const SharedParams& sp, hipStream_t stream);
 hipError_t launch_shared_merge(const AttnParams& p, const SharedParams& sp, hipStream_t stream);
-AttnWorkspace attn_workspace(int B, int Hkv, int W, int max_q_len, int group, int D, long total_pages);
+AttnWorkspace attn_workspace(int B, int Hkv, int W, int max_q_len, int group, int D, long total_pages,
+                             int pages_per_split);
 hipError_t launch_attn(const AttnParams& p, const AttnPlan& plan, hipStream_t stream);
 
 struct AcceptParams {

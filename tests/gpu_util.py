@@ -26,7 +26,8 @@ def dev_i32(a):
 class DeviceCase:
     """A case resident on the GPU plus its workspace."""
 
-    def __init__(self, case, pk, max_q_len=None, table_width=None, total_pages=0):
+    def __init__(self, case, pk, max_q_len=None, table_width=None, total_pages=0, pages_per_split=0,
+                 plan=False):
         self.case = case
         self.pk = pk
         bt = case.block_table
@@ -41,6 +42,9 @@ class DeviceCase:
         self.ql = dev_i32(case.q_lens)
         mq = max_q_len if max_q_len is not None else max(1, case.max_q_len)
         self.shape = pk.attn_shape(self.q, self.k, self.bt, mq, case.scale, total_pages)
+        self.shape.pages_per_split = pages_per_split
+        if plan:   # the host-side plan from the lengths
+            pk.pkv_attn_plan(self.shape, case.seq_lens)
         self.ws = pk.new_attn_workspace(self.shape)
         self.out = torch.empty(case.q.shape, dtype=torch.float32, device="cuda")
 

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(pk):
 
 
 def test_struct_layouts_match_the_header(pk):
-    assert ctypes.sizeof(pk.pkv_attn_shape) == 44
+    assert ctypes.sizeof(pk.pkv_attn_shape) == 48
     assert ctypes.sizeof(pk.pkv_accept_shape) == 16
     assert ctypes.sizeof(pk.pkv_kv_shape) == 28
 
@@ -70,6 +70,7 @@ def good_shape(pk, **kw):
     dict(num_pages=0), dict(max_pages_per_seq=0), dict(num_seqs=-1),
     dict(scale=float("nan")),
     dict(total_pages=-1),                 # the planning hint counts pages
+    dict(pages_per_split=-1), dict(pages_per_split=65),   # a split stages at most 64 table entries
 ])
 def test_bad_attention_shapes_are_rejected_before_launch(pk, bad):
     s = good_shape(pk, **bad)
@@ -206,3 +207,32 @@ def test_page_hint_sizes_the_workspace_for_more_splits(pk):
                                                     total_pages=200))
     assert full == same > 0
     assert ragged > full
+
+
+def test_host_plan_counts_pages_and_picks_a_split_length(pk):
+    """pkv_attn_plan: total_pages = sum of ceil(seq_len / 256) (lengths past the
+    table clipped to it, negative ones as 0); a uniform batch of full rows
+    keeps the split length that fills one round exactly (8 x 32 pages, 8 KV
+    heads: 8 pages, 256 workgroups); the choice stays within 1..min(W, 64)."""
+    s = good_shape(pk, num_seqs=8, max_pages_per_seq=32, total_q=48, max_q_len=6)
+    pk.pkv_attn_plan(s, [8192] * 8)
+    assert (s.total_pages, s.pages_per_split) == (256, 8)
+    s = good_shape(pk, num_seqs=5, max_pages_per_seq=64, total_q=5)
+    pk.pkv_attn_plan(s, [1, 257, 16384, 99999, -3])
+    assert s.total_pages == 1 + 2 + 64 + 64 + 0
+    assert 1 <= s.pages_per_split <= 64
+    assert pk.pkv_attn_workspace_bytes(s) > 0
+    prefill = good_shape(pk, num_seqs=1, max_pages_per_seq=8, total_q=300, max_q_len=300)
+    pk.pkv_attn_plan(prefill, [600])
+    assert (prefill.total_pages, prefill.pages_per_split) == (3, 0)
+
+
+def test_host_plan_rejects_bad_input(pk):
+    s = good_shape(pk)
+    assert pk.LIB.pkv_attn_plan(None, None) == pk.PKV_ERR_NULL
+    assert pk.LIB.pkv_attn_plan(ctypes.byref(s), None) == pk.PKV_ERR_NULL
+    bad = good_shape(pk, head_dim=96)
+    lens = (ctypes.c_int32 * 4)(1, 2, 3, 4)
+    assert pk.LIB.pkv_attn_plan(ctypes.byref(bad), lens) == pk.PKV_ERR_SHAPE
+    with pytest.raises(ValueError):
+        pk.pkv_attn_plan(s, [1, 2])

@@ -1,8 +1,9 @@
-"""Ragged batches and the planning hint (pkv_attn_shape.total_pages): the
-host's count of referenced pages only decides how the key range is cut into
-splits, so every hint (none, exact, far too small, far too large) must give
-the oracle's result on a batch whose lengths span 2 to 16384 tokens in a
-64-page-wide table; and the mixed job queue's first steps with the hint."""
+"""Ragged batches and the split plan (pkv_attn_shape.total_pages and
+pages_per_split, pkv_attn_plan): the plan only decides how the key range is
+cut into splits, so every hint (none, exact, far too small, far too large),
+every forced split length and the host plan's own choice must give the
+oracle's result on a batch whose lengths span 2 to 16384 tokens in a
+64-page-wide table; and the mixed job queue's first steps with the host plan."""
 
 import numpy as np
 import pytest
@@ -76,15 +77,32 @@ def test_every_page_hint_gives_the_oracle_result(pk, ragged, hint):
     assert_close(got, ref, f"ragged hint {hint}")
 
 
-def test_job_queue_steps_with_the_hint(pk):
+@pytest.mark.parametrize("pps", [1, 3, 64])
+def test_forced_split_lengths_give_the_oracle_result(pk, ragged, pps):
+    case, ref = ragged
+    say(f"ragged batch, pages_per_split {pps}")
+    got, flags = attn_gpu(case, pk, pages_per_split=pps)
+    assert flags == 0
+    assert_close(got, ref, f"ragged pps {pps}")
+
+
+def test_host_plan_gives_the_oracle_result(pk, ragged):
+    case, ref = ragged
+    say("ragged batch, host plan")
+    got, flags = attn_gpu(case, pk, plan=True)
+    assert flags == 0
+    assert_close(got, ref, "ragged host plan")
+
+
+def test_job_queue_steps_with_the_host_plan(pk):
     q = Config5Queue(seed=0)
     ref = {}
     for st in q.steps():
         if st.index >= 3:
             break
         c = st.case
-        say(f"job queue step {st.index} with the page hint: {c.num_seqs} sequences")
-        got, flags = attn_gpu(c, pk, total_pages=pages_of(c.seq_lens))
+        say(f"job queue step {st.index} with the host plan: {c.num_seqs} sequences")
+        got, flags = attn_gpu(c, pk, plan=True)
         assert flags == 0
         r0 = 0
         for b, jid in enumerate(st.job_ids):
