@@ -1067,8 +1067,20 @@ __global__ __launch_bounds__(WAVES * 64) void attn_split_kernel(
 // they share is served from that XCD's L2. No split of the key range: every
 // tile writes its rows of `out` itself.
 
-constexpr int kPrefillWaves = 4;
-constexpr int kPrefillRows = kPrefillWaves * 64;
+constexpr int kPrefillRows = 256;  // rows of a query tile (and of a shared-prefix row tile)
+// Waves of a long-window workgroup: 64-row waves (NRB = 2, one wave per SIMD)
+// or 32-row waves (NRB = 1, two per SIMD, so one wave's exponentials and
+// waits run beside the other's matrix products).
+template <int NRB>
+constexpr int kLongWaves = kPrefillRows / (32 * NRB);
+// 32-row waves measured 446 against 773 TFLOP/s on the whole-prompt prefill:
+// at two waves per SIMD a wave gets 128 VGPRs + 128 accumulation registers and
+// spills about 30 VGPRs in the chunk loop.
+#ifndef PKV_LONG_NRB128
+#define PKV_LONG_NRB128 2  // row blocks per wave on the head_dim-128 long-window kernels
+#endif
+template <int D>
+constexpr int kLongNrb = D == 128 ? PKV_LONG_NRB128 : 2;
 constexpr int kPrefillMaxPages = 2048;  // table entries staged per tile (524288 tokens)
 
 template <int LPC, int A>
@@ -1100,17 +1112,18 @@ __device__ __forceinline__ void wait_chunks(int ahead) {
 // iteration that ended before it), whose slot takes chunk k + NBUF - 2. It
 // then copies chunk k's K operand out. Every wave of the workgroup must call
 // this with the same key range.
-template <int D, int NBUF>
-__device__ __forceinline__ void stream_keys(MfmaTile<D, 2>& tile, char* ring, const int* s_pages,
+template <int D, int NBUF, int NRB>
+__device__ __forceinline__ void stream_keys(MfmaTile<D, NRB>& tile, char* ring, const int* s_pages,
                                             const AttnParams& p, int Hkv, int g, int key_begin, int key_end,
                                             int n_split, int n_free, float scale_log2) {
   using G = TileGeom<D, 32>;
   constexpr int TC = 32;
   constexpr int NI = G::NI;   // 1 KiB loads per K (or V) chunk
   constexpr int NC = G::NC;
-  constexpr int KPW = NI / kPrefillWaves;  // this wave's share of them
+  constexpr int WAVES = kLongWaves<NRB>;
+  constexpr int KPW = NI / WAVES;          // this wave's share of them
   constexpr int LPC = 2 * KPW;             // load instructions per chunk per wave
-  static_assert(NI % kPrefillWaves == 0, "chunk loads split evenly over the waves");
+  static_assert(NI % WAVES == 0, "chunk loads split evenly over the waves");
   static_assert(NBUF >= 3 && LPC * (NBUF - 3) < 64, "ring depth");
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int n_chunks = (key_end - key_begin + TC - 1) / TC;
@@ -1170,14 +1183,14 @@ __device__ __forceinline__ void stream_keys(MfmaTile<D, 2>& tile, char* ring, co
     tile.template probs<kSplit>(scale_log2);
     tile.qk(S);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < 8 * NRB; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, kSplit ? 7 : 5, 0);
     }
     tile.template pv<kSplit>();
     const bool grow = tile.template scores<kMask>(S, t1, min(TC, key_end - t1), scale_log2);
 #pragma unroll
-    for (int i = 0; i < (kSplit ? 36 : 20); ++i) {
+    for (int i = 0; i < (kSplit ? 18 : 10) * NRB; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, kSplit ? 2 : 4, 0);
     }
@@ -1211,15 +1224,15 @@ struct QSign {
 // Loads the q rows of one wave's 64 tile rows straight into the MFMA operand
 // registers; row_src(r) is the q row (element offset) of tile row r, or -1 for
 // a padding row.
-template <int D, class RowSrc>
-__device__ __forceinline__ void load_q_rows(MfmaTile<D, 2>& tile, const uint16_t* q, const QSign& qs,
+template <int D, int NRB, class RowSrc>
+__device__ __forceinline__ void load_q_rows(MfmaTile<D, NRB>& tile, const uint16_t* q, const QSign& qs,
                                             RowSrc row_src) {
-  using Tile = MfmaTile<D, 2>;
+  using Tile = MfmaTile<D, NRB>;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int half = lane >> 5;
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    const long off = row_src(wave * 64 + rb * 32 + (lane & 31));
+  for (int rb = 0; rb < NRB; ++rb) {
+    const long off = row_src(wave * 32 * NRB + rb * 32 + (lane & 31));
     const u32x4* src = reinterpret_cast<const u32x4*>(q + (off < 0 ? 0 : off));
 #pragma unroll
     for (int kk = 0; kk < Tile::KK; ++kk)
@@ -1229,16 +1242,18 @@ __device__ __forceinline__ void load_q_rows(MfmaTile<D, 2>& tile, const uint16_t
   // would make the compiler wait for every load in flight (the whole K/V
   // ring, which it does not see) at each chunk
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
+  for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
     for (int kk = 0; kk < Tile::KK; ++kk) asm volatile("" ::"v"(tile.qb[rb][kk]));
 }
 
-template <int D, int NBUF>
-__global__ __launch_bounds__(kPrefillRows) void attn_prefill_kernel(
+template <int D, int NBUF, int NRB>
+__global__ __launch_bounds__(kLongWaves<NRB> * 64) void attn_prefill_kernel(
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ q_lens, int B, int Hkv, int qtok, int W, AttnParams p) {
-  using Tile = MfmaTile<D, 2>;
+  using Tile = MfmaTile<D, NRB>;
+  constexpr int THREADS = kLongWaves<NRB> * 64;
+  constexpr int WROWS = 32 * NRB;  // rows of one wave
   using G = TileGeom<D, 32>;
   constexpr int TC = 32;
   __shared__ __attribute__((aligned(16))) char ring[NBUF * 2 * G::TILE];
@@ -1269,7 +1284,7 @@ __global__ __launch_bounds__(kPrefillRows) void attn_prefill_kernel(
   const int key_end = seq_len - qr * qtok;
   const int n_chunks = (key_end + TC - 1) / TC;
   const int need_pages = (key_end + kPage - 1) / kPage;
-  for (int j = threadIdx.x; j < need_pages; j += kPrefillRows) {
+  for (int j = threadIdx.x; j < need_pages; j += THREADS) {
     int e = block_table[(size_t)b * W + j];
     if (e < 0 || e >= p.P) {
       atomicOr(p.err, PKV_EFLAG_PAGE_BIT);
@@ -1282,7 +1297,7 @@ __global__ __launch_bounds__(kPrefillRows) void attn_prefill_kernel(
   const QSign qs(p.scale_log2);
   Tile tile;
   const int r_lo = (tq0 < 0 ? -tq0 : 0) * p.group, r_hi = qtok * p.group;
-  tile.init_rows(wave * 64, p.group, seq_len - q_len + tq0, r_lo, r_hi);
+  tile.init_rows(wave * WROWS, p.group, seq_len - q_len + tq0, r_lo, r_hi);
   load_q_rows<D>(tile, p.q, qs, [&](int r) -> long {
     if (r < r_lo || r >= r_hi) return -1;
     return ((long)(q_start + tq0 + r / p.group) * p.Hq + g * p.group + r % p.group) * D;
@@ -1294,17 +1309,17 @@ __global__ __launch_bounds__(kPrefillRows) void attn_prefill_kernel(
   // rounding of a single bf16 P. Then the chunks every valid row of this
   // wave sees in full go unmasked; the rest (the diagonal) are masked.
   const int n_split = min(n_chunks, 64 / TC);
-  const int wrow = max(r_lo, wave * 64);
+  const int wrow = max(r_lo, wave * WROWS);
   const int wave_min_lim = wrow < r_hi ? seq_len - q_len + tq0 + wrow / p.group : key_end;
   const int n_free = max(n_split, min(key_end / TC, (wave_min_lim + 1) / TC));
-  stream_keys<D, NBUF>(tile, ring, s_pages, p, Hkv, g, 0, key_end, n_split, n_free, qs.scale_log2);
+  stream_keys<D, NBUF, NRB>(tile, ring, s_pages, p, Hkv, g, 0, key_end, n_split, n_free, qs.scale_log2);
 
   // rows -> out
   {
     const int half = lane >> 5;
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      const int r = wave * 64 + rb * 32 + (lane & 31);
+    for (int rb = 0; rb < NRB; ++rb) {
+      const int r = wave * WROWS + rb * 32 + (lane & 31);
       const float ls = tile.lacc[rb][0];
       if (r < r_lo || r >= r_hi) continue;
       float* dst = p.out + ((size_t)(q_start + tq0 + r / p.group) * p.Hq + g * p.group + r % p.group) * D;
@@ -1333,9 +1348,11 @@ __global__ __launch_bounds__(kPrefillRows) void attn_prefill_kernel(
 //
 // Work item = (KV head g, row tile, key split), KV head fastest so that every
 // item of one head lands on one XCD when Hkv is a multiple of 8.
-template <int D, int NBUF>
-__global__ __launch_bounds__(kPrefillRows) void attn_shared_kernel(SharedParams sp, AttnParams p) {
-  using Tile = MfmaTile<D, 2>;
+template <int D, int NBUF, int NRB>
+__global__ __launch_bounds__(kLongWaves<NRB> * 64) void attn_shared_kernel(SharedParams sp, AttnParams p) {
+  using Tile = MfmaTile<D, NRB>;
+  constexpr int THREADS = kLongWaves<NRB> * 64;
+  constexpr int WROWS = 32 * NRB;  // rows of one wave
   using G = TileGeom<D, 32>;
   __shared__ __attribute__((aligned(16))) char ring[NBUF * 2 * G::TILE];
   __shared__ int s_pages[kPrefillMaxPages];
@@ -1350,8 +1367,8 @@ __global__ __launch_bounds__(kPrefillRows) void attn_shared_kernel(SharedParams 
   // the contract, one (sequence, shared entry) pair per thread of the grid:
   // every table starts with sequence 0's shared entries and every window row
   // sees the whole shared prefix
-  for (long e = (long)blockIdx.x * kPrefillRows + threadIdx.x; e < (long)p.B * sp.shared_pages;
-       e += (long)gridDim.x * kPrefillRows) {
+  for (long e = (long)blockIdx.x * THREADS + threadIdx.x; e < (long)p.B * sp.shared_pages;
+       e += (long)gridDim.x * THREADS) {
     const int b = (int)(e / sp.shared_pages), j = (int)(e % sp.shared_pages);
     if (p.block_table[(size_t)b * p.W + j] != p.block_table[j]) atomicOr(p.err, PKV_EFLAG_PAGE_BIT);
     if (j == 0 && p.q_lens[b] > 0 && p.seq_lens[b] - p.q_lens[b] < shared_tokens) atomicOr(p.err, PKV_EFLAG_QLEN_BIT);
@@ -1361,7 +1378,7 @@ __global__ __launch_bounds__(kPrefillRows) void attn_shared_kernel(SharedParams 
   const int key_end = min(key_begin + sp.split_keys, shared_tokens);
   if (key_begin >= key_end) return;
   const int page_base = key_begin / kPage, n_pg = (key_end - 1) / kPage - page_base + 1;
-  for (int j = threadIdx.x; j < n_pg; j += kPrefillRows) {
+  for (int j = threadIdx.x; j < n_pg; j += THREADS) {
     int e = p.block_table[page_base + j];
     if (e < 0 || e >= p.P) {
       atomicOr(p.err, PKV_EFLAG_PAGE_BIT);
@@ -1376,7 +1393,7 @@ __global__ __launch_bounds__(kPrefillRows) void attn_shared_kernel(SharedParams 
   const int r_hi = min(kPrefillRows, rows - rt * kPrefillRows);
   const QSign qs(p.scale_log2);
   Tile tile;
-  tile.init_rows(wave * 64, 1, 1 << 30, 0, r_hi);
+  tile.init_rows(wave * WROWS, 1, 1 << 30, 0, r_hi);
   load_q_rows<D>(tile, p.q, qs, [&](int r) -> long {
     if (r >= r_hi) return -1;
     const int R = rt * kPrefillRows + r;
@@ -1385,15 +1402,15 @@ __global__ __launch_bounds__(kPrefillRows) void attn_shared_kernel(SharedParams 
   __syncthreads();  // table entries staged
 
   const int n_chunks = (key_end - key_begin) / 32;
-  stream_keys<D, NBUF>(tile, ring, s_pages, p, Hkv, g, key_begin, key_end, 0, n_chunks, qs.scale_log2);
+  stream_keys<D, NBUF, NRB>(tile, ring, s_pages, p, Hkv, g, key_begin, key_end, 0, n_chunks, qs.scale_log2);
 
   // partials: (m, l) and the unnormalised accumulator of each valid row
   {
     const int half = lane >> 5;
     const size_t base = ((size_t)g * sp.splits + split) * rows + rt * kPrefillRows;
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      const int r = wave * 64 + rb * 32 + (lane & 31);
+    for (int rb = 0; rb < NRB; ++rb) {
+      const int r = wave * WROWS + rb * 32 + (lane & 31);
       if (r >= r_hi) continue;
       if (half == 0) {
         sp.part_ml[(base + r) * 2] = tile.m[rb];
@@ -1603,10 +1620,11 @@ SharedPlan shared_plan(int Hkv, int total_q, int group, int shared_pages) {
 hipError_t launch_attn_shared(const AttnParams& p, const SharedParams& sp, hipStream_t stream) {
   const unsigned grid = (unsigned)((long)p.Hkv * sp.row_tiles * sp.splits);
   if (p.D == 64)
-    hipLaunchKernelGGL((attn_shared_kernel<64, PKV_PREFILL_NBUF>), dim3(grid), dim3(kPrefillRows), 0, stream, sp, p);
+    hipLaunchKernelGGL((attn_shared_kernel<64, PKV_PREFILL_NBUF, kLongNrb<64>>), dim3(grid),
+                       dim3(kLongWaves<kLongNrb<64>> * 64), 0, stream, sp, p);
   else
-    hipLaunchKernelGGL((attn_shared_kernel<128, PKV_PREFILL_NBUF>), dim3(grid), dim3(kPrefillRows), 0, stream, sp,
-                       p);
+    hipLaunchKernelGGL((attn_shared_kernel<128, PKV_PREFILL_NBUF, kLongNrb<128>>), dim3(grid),
+                       dim3(kLongWaves<kLongNrb<128>> * 64), 0, stream, sp, p);
   return hipGetLastError();
 }
 
@@ -1624,11 +1642,13 @@ hipError_t launch_attn(const AttnParams& p, const AttnPlan& plan, hipStream_t st
   if (p.num_items == 0) return hipSuccess;
   if (plan.prefill) {
     if (p.D == 64)
-      hipLaunchKernelGGL((attn_prefill_kernel<64, PKV_PREFILL_NBUF>), dim3(p.num_items), dim3(kPrefillRows), 0,
-                         stream, p.block_table, p.seq_lens, p.q_lens, p.B, p.Hkv, plan.qtok, p.W, p);
+      hipLaunchKernelGGL((attn_prefill_kernel<64, PKV_PREFILL_NBUF, kLongNrb<64>>), dim3(p.num_items),
+                         dim3(kLongWaves<kLongNrb<64>> * 64), 0, stream, p.block_table, p.seq_lens, p.q_lens, p.B,
+                         p.Hkv, plan.qtok, p.W, p);
     else
-      hipLaunchKernelGGL((attn_prefill_kernel<128, PKV_PREFILL_NBUF>), dim3(p.num_items), dim3(kPrefillRows), 0,
-                         stream, p.block_table, p.seq_lens, p.q_lens, p.B, p.Hkv, plan.qtok, p.W, p);
+      hipLaunchKernelGGL((attn_prefill_kernel<128, PKV_PREFILL_NBUF, kLongNrb<128>>), dim3(p.num_items),
+                         dim3(kLongWaves<kLongNrb<128>> * 64), 0, stream, p.block_table, p.seq_lens, p.q_lens, p.B,
+                         p.Hkv, plan.qtok, p.W, p);
     return hipGetLastError();
   }
   if (p.D == 64) return launch_d<64>(p, plan, stream);
