@@ -145,6 +145,19 @@ __device__ __forceinline__ float shfl_xor(float x, int m) {
   return __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ m) << 2, __float_as_int(x)));
 }
 
+// Reductions across the two 32-lane halves in one VALU instruction, without
+// an LDS round trip: v_permlane32_swap exchanges the upper 32 lanes of its
+// first operand with the lower 32 of its second, so with x in both every lane
+// holds {x of this lane, x of lane ^ 32} (lane layout checked on the GPU).
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ float exp2f_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Split partials cross XCDs (each XCD has its own L2). Agent-scope relaxed
@@ -357,7 +370,8 @@ struct ValuTile {
 #pragma unroll
       for (int e = 0; e < 8; ++e)
 #pragma unroll
-        for (int msk = NC; msk < 64; msk <<= 1) acc[r][e] += shfl_xor(acc[r][e], msk);
+        for (int msk = NC; msk < 64; msk <<= 1)
+          acc[r][e] = msk == 32 ? sum_xor32(acc[r][e]) : acc[r][e] + shfl_xor(acc[r][e], msk);
     if (lane < NC) {
 #pragma unroll
       for (int r = 0; r < RP; ++r)
@@ -512,7 +526,7 @@ struct MfmaTile {
         x[i] = (tok0 + tt <= lim[rb] && tt < nv) ? S[rb][i] * scale_log2 : kNegInf;
         cm = fmaxf(cm, x[i]);
       }
-      cm = fmaxf(cm, shfl_xor(cm, 32));
+      cm = max_xor32(cm);
       const float mn = fmaxf(m[rb], cm);
       const float mu = (mn == kNegInf) ? 0.f : mn;
       const float alpha = exp2f_fast(m[rb] - mu);
@@ -605,7 +619,7 @@ struct MfmaTile {
         cm = fmaxf(cm, xs[rb][i]);
       }
       // scale_log2 > 0 here, so scaling commutes with the max
-      cmax[rb] = fmaxf(cm, shfl_xor(cm, 32)) * scale_log2;
+      cmax[rb] = max_xor32(cm) * scale_log2;
       grow |= cmax[rb] > m[rb] + kLazyLog2;
     }
     return __builtin_amdgcn_ballot_w64(grow) != 0;
@@ -722,7 +736,7 @@ struct MfmaTile {
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
       const int r = rb * 32 + row;
-      const float ls = l[rb] + shfl_xor(l[rb], 32);
+      const float ls = sum_xor32(l[rb]);
       if (half == 0) {
         rm[r] = m[rb];
         rl[r] = ls;
