@@ -44,6 +44,11 @@ TINY = [
     ([4096, 100, 2], [1, 1, 1], 32, 8, 128),
     ([258], [6], 32, 8, 128),                 # window straddles a page boundary
     ([3000], [5], 2, 1, 64),
+    ([500, 3], [1, 1], 64, 1, 64),            # the widest head group: 64 rows from one q token
+    ([700], [2], 32, 1, 128),                 # 32 q heads on one KV head, 2-row window: 64 rows
+    ([300, 40, 1000], [1, 1, 1], 3, 1, 128),  # a head group of 3 on the VALU tile
+    ([900, 257], [4, 1], 3, 3, 64),           # MHA, 4-row window: the largest VALU tile
+    ([600, 2], [5, 2], 3, 3, 128),            # MHA, 5 rows: the smallest MFMA tile
 ]
 
 
