@@ -31,6 +31,12 @@ bool attn_shape_ok(const pkv_attn_shape* s) {
   // work items, with every XCD's share of (KV head, split) pairs padded to a whole pair
   if ((long)s->num_seqs * ((long)s->num_kv_heads * s->max_pages_per_seq + 8) > (1L << 30)) return false;
   if ((long)s->total_q * s->num_q_heads * s->head_dim * 2 >= (1L << 32)) return false;  // q buffer offsets
+  // long windows: one work item per (sequence, KV head, 256-row query tile)
+  const int group = s->num_q_heads / s->num_kv_heads;
+  if ((long)s->max_q_len * group > PKV_MAX_ROWS) {
+    const long qtok = 256 / group;
+    if ((long)s->num_seqs * s->num_kv_heads * ((s->max_q_len + qtok - 1) / qtok) > (1L << 30)) return false;
+  }
   return true;
 }
 

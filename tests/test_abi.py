@@ -71,6 +71,8 @@ def good_shape(pk, **kw):
     dict(scale=float("nan")),
     dict(total_pages=-1),                 # the planning hint counts pages
     dict(pages_per_split=-1), dict(pages_per_split=65),   # a split stages at most 64 table entries
+    # long windows of 2^20 rows in a head group of 64: 2^31 query tiles, past the item bound
+    dict(num_seqs=2**13, num_q_heads=64, num_kv_heads=1, max_pages_per_seq=2**16, max_q_len=2**20, total_q=1),
 ])
 def test_bad_attention_shapes_are_rejected_before_launch(pk, bad):
     s = good_shape(pk, **bad)
