@@ -134,6 +134,24 @@ def _check(rc, what):
         raise PkvError(f"{what}: {LIB.pkv_status_string(rc).decode()} ({rc})")
 
 
+def _extents(name_call, *checks):
+    """Each check is (tensor, element count the shape implies, name): the
+    kernels index the buffers by the shape, so a tensor of another size is
+    refused here, before any launch."""
+    for t, n, name in checks:
+        if t is not None and t.numel() != n:
+            raise ValueError(f"{name_call}: {name} has {t.numel()} elements, the shape implies {n}")
+
+
+def _attn_extents(call, shape, q, k_pool, v_pool, block_table, seq_lens, q_lens, out):
+    s = shape
+    qn = s.total_q * s.num_q_heads * s.head_dim
+    pool = s.num_pages * s.num_kv_heads * s.page_size * s.head_dim
+    _extents(call, (q, qn, "q"), (out, qn, "out"), (k_pool, pool, "k_pool"), (v_pool, pool, "v_pool"),
+             (block_table, s.num_seqs * s.max_pages_per_seq, "block_table"), (seq_lens, s.num_seqs, "seq_lens"),
+             (q_lens, s.num_seqs, "q_lens"))
+
+
 def _need(t, dtype, name):
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
@@ -183,6 +201,7 @@ def new_attn_workspace(shape, device="cuda"):
 
 def pkv_attn_fwd(q, k_pool, v_pool, block_table, seq_lens, q_lens, out, shape, workspace, stream=None):
     """q, k_pool, v_pool: bf16; block_table, seq_lens, q_lens: int32; out: fp32."""
+    _attn_extents("pkv_attn_fwd", shape, q, k_pool, v_pool, block_table, seq_lens, q_lens, out)
     for t, dt, n in ((q, torch.bfloat16, "q"), (k_pool, torch.bfloat16, "k_pool"),
                      (v_pool, torch.bfloat16, "v_pool"), (block_table, torch.int32, "block_table"),
                      (seq_lens, torch.int32, "seq_lens"), (q_lens, torch.int32, "q_lens"),
@@ -208,6 +227,7 @@ def new_attn_shared_workspace(shape, shared_pages, device="cuda"):
 def pkv_attn_fwd_shared(q, k_pool, v_pool, block_table, seq_lens, q_lens, out, shape, shared_pages, workspace,
                         stream=None):
     """pkv_attn_fwd over a batch whose tables all begin with the same shared_pages pages."""
+    _attn_extents("pkv_attn_fwd_shared", shape, q, k_pool, v_pool, block_table, seq_lens, q_lens, out)
     for t, dt, n in ((q, torch.bfloat16, "q"), (k_pool, torch.bfloat16, "k_pool"),
                      (v_pool, torch.bfloat16, "v_pool"), (block_table, torch.int32, "block_table"),
                      (seq_lens, torch.int32, "seq_lens"), (q_lens, torch.int32, "q_lens"),
@@ -244,6 +264,12 @@ def new_accept_workspace(shape, device="cuda"):
 
 def pkv_accept(logits, draft_ids, n_draft, out_accept, out_next, window, shape, workspace, stream=None):
     """logits fp32; draft_ids, n_draft, out_accept, out_next, window (or None): int32."""
+    B = shape.num_seqs
+    _extents("pkv_accept", (logits, shape.total_rows * shape.vocab, "logits"), (n_draft, B, "n_draft"),
+             (out_accept, B, "out_accept"), (out_next, B, "out_next"), (window, B, "window"))
+    if draft_ids is not None and draft_ids.numel() and draft_ids.numel() < shape.total_rows - B:
+        raise ValueError(f"pkv_accept: draft_ids has {draft_ids.numel()} elements, fewer than the "
+                         f"{shape.total_rows - B} drafts the rows imply")
     for t, dt, n in ((logits, torch.float32, "logits"), (n_draft, torch.int32, "n_draft"),
                      (out_accept, torch.int32, "out_accept"), (out_next, torch.int32, "out_next"),
                      (workspace, torch.uint8, "workspace")):
@@ -292,6 +318,13 @@ def new_kv_workspace(shape, device="cuda"):
 def pkv_kv_append(k_new, v_new, k_pool, v_pool, block_table, seq_lens, q_lens, free_pages, free_count,
                   shape, workspace, stream=None):
     """k_new, v_new, pools: bf16; block_table, seq_lens, q_lens, free_pages, free_count: int32."""
+    s = shape
+    pool = s.num_pages * s.num_kv_heads * s.page_size * s.head_dim
+    win = s.total_q * s.num_kv_heads * s.head_dim
+    _extents("pkv_kv_append", (k_pool, pool, "k_pool"), (v_pool, pool, "v_pool"),
+             (k_new if win else None, win, "k_new"), (v_new if win else None, win, "v_new"),
+             (block_table, s.num_seqs * s.max_pages_per_seq, "block_table"), (seq_lens, s.num_seqs, "seq_lens"),
+             (q_lens, s.num_seqs, "q_lens"), (free_pages, s.num_pages, "free_pages"), (free_count, 1, "free_count"))
     for t, dt, n in ((k_pool, torch.bfloat16, "k_pool"), (v_pool, torch.bfloat16, "v_pool"),
                      (block_table, torch.int32, "block_table"), (seq_lens, torch.int32, "seq_lens"),
                      (q_lens, torch.int32, "q_lens"), (free_pages, torch.int32, "free_pages"),
@@ -311,6 +344,10 @@ def pkv_kv_append(k_new, v_new, k_pool, v_pool, block_table, seq_lens, q_lens, f
 def pkv_kv_rollback(block_table, seq_lens, q_lens, accepted, free_pages, free_count, shape, workspace,
                     stream=None):
     """All int32 device tensors; accepted is pkv_accept's out_accept."""
+    s = shape
+    _extents("pkv_kv_rollback", (block_table, s.num_seqs * s.max_pages_per_seq, "block_table"),
+             (seq_lens, s.num_seqs, "seq_lens"), (q_lens, s.num_seqs, "q_lens"), (accepted, s.num_seqs, "accepted"),
+             (free_pages, s.num_pages, "free_pages"), (free_count, 1, "free_count"))
     for t, n in ((block_table, "block_table"), (seq_lens, "seq_lens"), (q_lens, "q_lens"),
                  (accepted, "accepted"), (free_pages, "free_pages"), (free_count, "free_count")):
         _need(t, torch.int32, n)
@@ -393,6 +430,9 @@ def pkv_pool_defrag(pool, num_pages, move_referenced=False):
 
 def pkv_pool_copy_pages(k_pool, v_pool, src, dst, err=None, stream=None):
     """k_pool, v_pool: bf16 [P, Hkv, 256, D]; src, dst: int32 device tensors."""
+    _extents("pkv_pool_copy_pages", (v_pool, k_pool.numel(), "v_pool"), (dst, src.numel(), "dst"))
+    if err is not None and err.numel() < 1:
+        raise ValueError("pkv_pool_copy_pages: err needs one int32")
     for t, dt, n in ((k_pool, torch.bfloat16, "k_pool"), (v_pool, torch.bfloat16, "v_pool"),
                      (src, torch.int32, "src"), (dst, torch.int32, "dst")):
         _need(t, dt, n)

@@ -238,3 +238,44 @@ def test_host_plan_rejects_bad_input(pk):
     assert pk.LIB.pkv_attn_plan(ctypes.byref(bad), lens) == pk.PKV_ERR_SHAPE
     with pytest.raises(ValueError):
         pk.pkv_attn_plan(s, [1, 2])
+
+
+def test_binding_refuses_tensors_of_another_size(pk):
+    """The kernels index every buffer by the shape, so the binding checks each
+    tensor's element count against it before anything reaches the device
+    (CPU tensors suffice: the count is checked first)."""
+    import torch
+    bf, i32, f32 = torch.bfloat16, torch.int32, torch.float32
+    s = good_shape(pk, num_seqs=2, num_q_heads=8, num_kv_heads=2, head_dim=64, num_pages=4, max_pages_per_seq=3,
+                   total_q=3, max_q_len=2)
+    args = dict(q=torch.zeros(3, 8, 64, dtype=bf), k_pool=torch.zeros(4, 2, 256, 64, dtype=bf),
+                v_pool=torch.zeros(4, 2, 256, 64, dtype=bf), block_table=torch.zeros(2, 3, dtype=i32),
+                seq_lens=torch.zeros(2, dtype=i32), q_lens=torch.zeros(2, dtype=i32),
+                out=torch.zeros(3, 8, 64, dtype=f32))
+    for name, bad in (("q", torch.zeros(2, 8, 64, dtype=bf)), ("out", torch.zeros(3, 8, 32, dtype=f32)),
+                      ("v_pool", torch.zeros(3, 2, 256, 64, dtype=bf)), ("block_table", torch.zeros(2, 2, dtype=i32)),
+                      ("q_lens", torch.zeros(3, dtype=i32))):
+        a = dict(args, **{name: bad})
+        with pytest.raises(ValueError, match=name):
+            pk.pkv_attn_fwd(a["q"], a["k_pool"], a["v_pool"], a["block_table"], a["seq_lens"], a["q_lens"],
+                            a["out"], s, torch.zeros(16, dtype=torch.uint8))
+        with pytest.raises(ValueError, match=name):
+            pk.pkv_attn_fwd_shared(a["q"], a["k_pool"], a["v_pool"], a["block_table"], a["seq_lens"],
+                                   a["q_lens"], a["out"], s, 1, torch.zeros(16, dtype=torch.uint8))
+    acc = pk.pkv_accept_shape(2, 100, 5, 4)
+    with pytest.raises(ValueError, match="logits"):
+        pk.pkv_accept(torch.zeros(4, 100), torch.zeros(3, dtype=i32), torch.zeros(2, dtype=i32),
+                      torch.zeros(2, dtype=i32), torch.zeros(2, dtype=i32), None, acc, torch.zeros(8, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="draft_ids"):
+        pk.pkv_accept(torch.zeros(5, 100), torch.zeros(2, dtype=i32), torch.zeros(2, dtype=i32),
+                      torch.zeros(2, dtype=i32), torch.zeros(2, dtype=i32), None, acc, torch.zeros(8, dtype=torch.uint8))
+    kv = pk.pkv_kv_shape(2, 2, 64, 256, 4, 3, 3)
+    with pytest.raises(ValueError, match="free_pages"):
+        pk.pkv_kv_append(torch.zeros(3, 2, 64, dtype=bf), torch.zeros(3, 2, 64, dtype=bf), args["k_pool"],
+                         args["v_pool"], args["block_table"], args["seq_lens"], args["q_lens"],
+                         torch.zeros(3, dtype=i32), torch.zeros(1, dtype=i32), kv, torch.zeros(8, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="accepted"):
+        pk.pkv_kv_rollback(args["block_table"], args["seq_lens"], args["q_lens"], torch.zeros(1, dtype=i32),
+                           torch.zeros(4, dtype=i32), torch.zeros(1, dtype=i32), kv, torch.zeros(8, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="dst"):
+        pk.pkv_pool_copy_pages(args["k_pool"], args["v_pool"], torch.zeros(2, dtype=i32), torch.zeros(3, dtype=i32))
