@@ -76,3 +76,51 @@ def test_verify_step_replays_bit_exact(pk):
         torch.cuda.synchronize()
         assert torch.equal(dc.out, ref_out), f"eager after replay {rep}: attention differs"
     assert dc.errors() == 0
+
+
+def test_shared_prefix_and_long_window_replay_bit_exact(pk):
+    """The shared-prefix call (three launches: prefix splits, tails, merge)
+    and a long-window call (prefill tiles) captured together; every replay
+    equals the eager result bit for bit."""
+    import torch
+    from tests.test_gpu_shared import shared_case
+    say("graph: shared-prefix call + long window, 4 replays")
+    sc = shared_case(31, 3, [40, 300, 7, 256], [1, 2, 1, 3])
+    sd = DeviceCase(sc, pk)
+    sws = pk.new_attn_shared_workspace(sd.shape, 3)
+    long_case = make_tiny_case(32, [900, 300], [200, 64], Hq=8, Hkv=2, D=128, num_pages=16)
+    ld = DeviceCase(long_case, pk)
+
+    def step():
+        pk.pkv_attn_fwd_shared(sd.q, sd.k, sd.v, sd.bt, sd.sl, sd.ql, sd.out, sd.shape, 3, sws)
+        ld.run()
+
+    step()
+    torch.cuda.synchronize()
+    ref_s, ref_l = sd.out.clone(), ld.out.clone()
+    assert_close(ref_s.cpu().numpy(), oracle.attention(sc.q, sc.k_pool, sc.v_pool, sc.block_table, sc.seq_lens,
+                                                       sc.q_lens, sc.scale), "graph shared eager")
+    assert_close(ref_l.cpu().numpy(), oracle.attention(long_case.q, long_case.k_pool, long_case.v_pool,
+                                                       long_case.block_table, long_case.seq_lens,
+                                                       long_case.q_lens, long_case.scale), "graph long eager")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        sd.out.fill_(float("nan"))
+        ld.out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(sd.out, ref_s), f"replay {rep}: shared-prefix call differs"
+        assert torch.equal(ld.out, ref_l), f"replay {rep}: long window differs"
+        step()
+        torch.cuda.synchronize()
+        assert torch.equal(sd.out, ref_s) and torch.equal(ld.out, ref_l), f"eager after replay {rep}"
+    assert pk.pkv_attn_check_errors(sws) == 0 and ld.errors() == 0
