@@ -18,9 +18,11 @@
  *    shrinks by 1 otherwise.
  *
  * Conventions for every entry point:
- *  - Device pointers are caller-owned device memory. The library allocates
- *    nothing and keeps no per-call state; every kernel is enqueued on `stream`
- *    (a hipStream_t; NULL means the default stream) and nothing synchronises.
+ *  - Device pointers are caller-owned device memory. The library allocates no
+ *    device memory and keeps no per-call state (the one host object is the
+ *    page allocator's, from pkv_pool_create until pkv_pool_destroy); every
+ *    kernel is enqueued on `stream` (a hipStream_t; NULL means the default
+ *    stream) and only the *_check_errors calls synchronise.
  *  - Shapes are checked on the host before any launch. Contents of device
  *    arrays are a caller contract (listed per call). Kernels never read or
  *    write outside the documented extents even when the contract is broken:
@@ -175,7 +177,8 @@ int pkv_attn_fwd_shared(const void* q, const void* k_pool, const void* v_pool,
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /* Synchronise `stream`, copy the error word of `workspace` into *flags
- * (PKV_EFLAG_* bits; 0 = every contract held) and clear it. */
+ * (PKV_EFLAG_* bits; 0 = every contract held) and clear it. It synchronises,
+ * so it is not for use under stream (graph) capture. */
 int pkv_attn_check_errors(void* workspace, void* stream, uint32_t* flags);
 
 /* -------------------------------------------------------------------- accept */
