@@ -165,12 +165,23 @@ int pkv_attn_fwd(const void* q, const void* k_pool, const void* v_pool,
  * (zero-filled before its first use, like pkv_attn_fwd's; every call leaves
  * it ready for the next).
  * Contract, besides pkv_attn_fwd's: block_table[b][j] == block_table[0][j] for
- * j < shared_pages, and seq_len - q_len >= shared_pages * 256 (every window
- * row sees the whole shared prefix), for every sequence with q_len > 0;
- * 1 <= shared_pages < max_pages_per_seq. A sequence breaking it gets undefined
- * rows, and PKV_EFLAG_PAGE / PKV_EFLAG_QLEN is set.
+ * j < shared_pages and every sequence b; seq_len - q_len >= shared_pages * 256
+ * (every window row sees the whole shared prefix) for every sequence with
+ * q_len > 0; 1 <= shared_pages < max_pages_per_seq. A sequence breaking it
+ * gets undefined rows, and PKV_EFLAG_PAGE / PKV_EFLAG_QLEN is set.
  */
 size_t pkv_attn_shared_workspace_bytes(const pkv_attn_shape* shape, int32_t shared_pages);
+
+/* Host helper for the shared-prefix call: the largest shared_pages its
+ * contract allows for this batch, from host copies of the block table
+ * (block_table_host int32 [num_seqs, max_pages_per_seq]), seq_lens and q_lens
+ * (int32 [num_seqs] each): the length of the table prefix every row shares
+ * with row 0, cut so that every window row sees all of it (seq_len - q_len >=
+ * shared_pages * 256 where q_len > 0) and at least one table entry stays past
+ * it; 0 when nothing is shared or no sequence has a window. Returns that
+ * count, or a negative pkv_status (PKV_ERR_NULL, PKV_ERR_SHAPE). */
+int32_t pkv_shared_prefix_pages(const int32_t* block_table_host, const int32_t* seq_lens_host,
+                                const int32_t* q_lens_host, const pkv_attn_shape* shape);
 int pkv_attn_fwd_shared(const void* q, const void* k_pool, const void* v_pool,
                         const int32_t* block_table, const int32_t* seq_lens, const int32_t* q_lens,
                         float* out, const pkv_attn_shape* shape, int32_t shared_pages,

@@ -29,7 +29,7 @@ EXPORTS = ("pkv_attn_workspace_bytes", "pkv_attn_workspace_init", "pkv_attn_fwd"
            "pkv_kv_append", "pkv_kv_rollback", "pkv_kv_check_errors", "pkv_pool_create",
            "pkv_pool_destroy", "pkv_pool_stats", "pkv_pool_admit", "pkv_pool_alloc", "pkv_pool_retain",
            "pkv_pool_release", "pkv_pool_defrag", "pkv_pool_copy_pages", "pkv_table_remap",
-           "pkv_attn_shared_workspace_bytes", "pkv_attn_fwd_shared", "pkv_attn_plan")
+           "pkv_attn_shared_workspace_bytes", "pkv_attn_fwd_shared", "pkv_attn_plan", "pkv_shared_prefix_pages")
 
 
 class pkv_attn_shape(ctypes.Structure):
@@ -65,6 +65,8 @@ def _load():
     vp, sz, i32p = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p
     lib.pkv_attn_workspace_bytes.argtypes = [ctypes.POINTER(pkv_attn_shape)]
     lib.pkv_attn_workspace_bytes.restype = sz
+    lib.pkv_shared_prefix_pages.argtypes = [vp, vp, vp, ctypes.POINTER(pkv_attn_shape)]
+    lib.pkv_shared_prefix_pages.restype = ctypes.c_int32
     lib.pkv_attn_plan.argtypes = [ctypes.POINTER(pkv_attn_shape), vp]
     lib.pkv_attn_plan.restype = ctypes.c_int
     lib.pkv_attn_workspace_init.argtypes = [vp, sz, vp]
@@ -237,6 +239,21 @@ def pkv_attn_fwd_shared(q, k_pool, v_pool, block_table, seq_lens, q_lens, out, s
                                  _ptr(q_lens), _ptr(out), ctypes.byref(shape), int(shared_pages), _ptr(workspace),
                                  workspace.numel(), _stream(stream))
     _check(rc, "pkv_attn_fwd_shared")
+
+
+def pkv_shared_prefix_pages(block_table_host, seq_lens_host, q_lens_host, shape):
+    """The largest shared_pages pkv_attn_fwd_shared accepts for this batch,
+    from host arrays (numpy or sequences) of the table, lengths and windows."""
+    t = np.ascontiguousarray(block_table_host, dtype=np.int32)
+    sl = np.ascontiguousarray(seq_lens_host, dtype=np.int32)
+    ql = np.ascontiguousarray(q_lens_host, dtype=np.int32)
+    if t.size != shape.num_seqs * shape.max_pages_per_seq or sl.size != shape.num_seqs or ql.size != shape.num_seqs:
+        raise ValueError("pkv_shared_prefix_pages: host arrays do not match the shape")
+    vp = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    n = int(LIB.pkv_shared_prefix_pages(vp(t), vp(sl), vp(ql), ctypes.byref(shape)))
+    if n < 0:
+        _check(n, "pkv_shared_prefix_pages")
+    return n
 
 
 def pkv_attn_check_errors(workspace, stream=None):

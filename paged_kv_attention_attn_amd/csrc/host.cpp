@@ -219,6 +219,27 @@ size_t pkv_attn_shared_workspace_bytes(const pkv_attn_shape* s, int32_t shared_p
   return shared_layout(s, shared_pages).total;
 }
 
+int32_t pkv_shared_prefix_pages(const int32_t* table, const int32_t* seq_lens, const int32_t* q_lens,
+                                const pkv_attn_shape* s) {
+  if (!s) return PKV_ERR_NULL;
+  if (!attn_shape_ok(s)) return PKV_ERR_SHAPE;
+  if (s->num_seqs == 0) return 0;
+  if (!table || !seq_lens || !q_lens) return PKV_ERR_NULL;
+  const long W = s->max_pages_per_seq;
+  bool any_window = false;
+  long n = W - 1;  // at least one entry past the shared ones
+  for (long b = 0; b < s->num_seqs; ++b) {
+    if (q_lens[b] > 0) {  // every window row sees the whole shared prefix
+      any_window = true;
+      n = std::min<long>(n, std::max<long>(0, ((long)seq_lens[b] - q_lens[b]) / PKV_PAGE_SIZE));
+    }
+    long j = 0;  // every table starts with row 0's shared entries
+    while (j < n && table[b * W + j] == table[j]) ++j;
+    n = j;
+  }
+  return any_window ? (int32_t)n : 0;
+}
+
 int pkv_attn_fwd_shared(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_table,
                         const int32_t* seq_lens, const int32_t* q_lens, float* out, const pkv_attn_shape* s,
                         int32_t shared_pages, void* workspace, size_t workspace_bytes, void* stream) {

@@ -6,6 +6,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -279,3 +280,39 @@ def test_binding_refuses_tensors_of_another_size(pk):
                            torch.zeros(4, dtype=i32), torch.zeros(1, dtype=i32), kv, torch.zeros(8, dtype=torch.uint8))
     with pytest.raises(ValueError, match="dst"):
         pk.pkv_pool_copy_pages(args["k_pool"], args["v_pool"], torch.zeros(2, dtype=i32), torch.zeros(3, dtype=i32))
+
+
+def _shared_prefix_reference(table, seq_lens, q_lens):
+    """The shared-prefix contract written out: the largest n < W with every
+    row's first n entries equal to row 0's and seq_len - q_len >= 256 n on
+    every row with a window; 0 without any window."""
+    B, W = table.shape
+    if not (q_lens > 0).any():
+        return 0
+    best = 0
+    for n in range(W):
+        ok = all((table[b, :n] == table[0, :n]).all() for b in range(B))
+        ok = ok and all(seq_lens[b] - q_lens[b] >= 256 * n for b in range(B) if q_lens[b] > 0)
+        if ok:
+            best = n
+    return best
+
+
+def test_shared_prefix_pages_from_host_tables(pk):
+    rng = np.random.default_rng(5)
+    for trial in range(200):
+        B, W = int(rng.integers(1, 6)), int(rng.integers(1, 7))
+        base = rng.integers(0, 50, W)
+        table = np.tile(base, (B, 1)).astype(np.int32)
+        for b in range(B):                       # each row diverges somewhere, or not at all
+            cut = int(rng.integers(0, W + 1))
+            table[b, cut:] = rng.integers(50, 100, W - cut)
+        q_lens = rng.integers(0, 4, B).astype(np.int32)
+        seq_lens = (q_lens + rng.integers(0, W * 256 - 3, B)).astype(np.int32)
+        s = good_shape(pk, num_seqs=B, max_pages_per_seq=W, total_q=int(q_lens.sum()), max_q_len=4)
+        assert pk.pkv_shared_prefix_pages(table, seq_lens, q_lens, s) == \
+            _shared_prefix_reference(table, seq_lens, q_lens), trial
+    with pytest.raises(ValueError):
+        pk.pkv_shared_prefix_pages(np.zeros((2, 3), np.int32), [1], [1], good_shape(pk, num_seqs=2,
+                                                                                      max_pages_per_seq=3))
+    assert pk.LIB.pkv_shared_prefix_pages(None, None, None, None) == pk.PKV_ERR_NULL

@@ -130,3 +130,16 @@ def test_broken_contract_is_flagged(pk):
     short.seq_lens[0] = 2 * 256                              # no tail token: the window row is shared
     _, _, flags = run_shared(pk, short, 2)
     assert flags & pk.PKV_EFLAG_QLEN
+
+
+def test_host_helper_finds_the_shared_prefix(pk):
+    """pkv_shared_prefix_pages on the dedup configuration's host tables gives
+    its 16 shared pages, and the call with that count matches the oracle."""
+    case, _ = make_config(4)
+    import torch
+    shape = pk.attn_shape(dev_bf16(case.q), dev_bf16(case.k_pool), dev_i32(case.block_table), 1, case.scale)
+    n = pk.pkv_shared_prefix_pages(case.block_table, case.seq_lens, case.q_lens, shape)
+    assert n == 16
+    got, _, flags = run_shared(pk, case, n)
+    assert flags == 0
+    assert_close(got, oracle_attn(case), "dedup via the helper")
