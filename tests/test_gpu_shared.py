@@ -143,3 +143,26 @@ def test_host_helper_finds_the_shared_prefix(pk):
     got, _, flags = run_shared(pk, case, n)
     assert flags == 0
     assert_close(got, oracle_attn(case), "dedup via the helper")
+
+
+def test_planned_shape_on_the_shared_call(pk):
+    """A shape carrying a host plan (page count and split length for whole
+    rows) on the shared-prefix call with the count the host helper derives:
+    the tails plan their own splits, and the result matches the oracle."""
+    import torch
+    case = shared_case(430, 4, [10, 900, 3000, 256, 1], [1, 3, 2, 1, 4])
+    q, k, v = dev_bf16(case.q), dev_bf16(case.k_pool), dev_bf16(case.v_pool)
+    bt, sl, ql = dev_i32(case.block_table), dev_i32(case.seq_lens), dev_i32(case.q_lens)
+    shape = pk.pkv_attn_plan(pk.attn_shape(q, k, bt, 4, case.scale), case.seq_lens)
+    assert shape.pages_per_split > 0
+    # the tables share 4 pages, but the last sequence (1025 tokens, a 4-row
+    # window) has a window row that sees only 1021 keys: 3 pages are shared
+    # by every row, the 4th goes with the tails
+    n = pk.pkv_shared_prefix_pages(case.block_table, case.seq_lens, case.q_lens, shape)
+    assert n == 3
+    ws = pk.new_attn_shared_workspace(shape, n)
+    out = torch.empty(case.q.shape, dtype=torch.float32, device="cuda")
+    pk.pkv_attn_fwd_shared(q, k, v, bt, sl, ql, out, shape, n, ws)
+    torch.cuda.synchronize()
+    assert pk.pkv_attn_check_errors(ws) == 0
+    assert_close(out.cpu().numpy(), oracle_attn(case), "shared with a planned shape")
