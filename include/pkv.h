@@ -144,9 +144,10 @@ int pkv_attn_workspace_init(void* workspace, size_t bytes, void* stream);
  * PKV_EFLAG_QLEN).
  * Precision: fp32 scores and softmax; P enters P.V rounded to bf16 (rows =
  * q_len * Hq/Hkv <= 4 run on VALU dot products, more rows on the matrix
- * cores). On the long-window kernel P enters as two bf16 terms for the first
- * 64 keys and wherever a key weighs more than 1/8 of its row sum so far (rows
- * with few keys would not average the rounding out).
+ * cores). On the matrix cores P enters as two bf16 terms (about 16
+ * significant bits) wherever a key weighs more than 1/8 of its row sum so
+ * far, and on the long-window kernel also for the first 64 keys: rows that a
+ * few keys dominate would not average the rounding out.
  */
 int pkv_attn_fwd(const void* q, const void* k_pool, const void* v_pool,
                  const int32_t* block_table, const int32_t* seq_lens, const int32_t* q_lens,

@@ -516,6 +516,8 @@ struct MfmaTile {
     }
     // this lane holds tokens 8*(i/4) + 4*half + i%4 of q row `row`
     u32x4 pb[NRB][2];
+    float p[NRB][16];
+    bool heavy = false;
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
       float x[16];
@@ -531,22 +533,24 @@ struct MfmaTile {
       const float mu = (mn == kNegInf) ? 0.f : mn;
       const float alpha = exp2f_fast(m[rb] - mu);
       float ps = 0.f;
-      float p[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        p[i] = exp2f_fast(x[i] - mu);
-        ps += p[i];
+        p[rb][i] = exp2f_fast(x[i] - mu);
+        ps += p[rb][i];
       }
       l[rb] = l[rb] * alpha + ps;
       m[rb] = mn;
+      // a key of this chunk weighing more than kSplitWeight of its row's sum
+      // so far (both halves of the row): its bf16 P would not average out
+      heavy |= cm != kNegInf && exp2f_fast(cm - mu) > kSplitWeight * sum_xor32(l[rb]);
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) acc[rb][mb] *= alpha;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        pb[rb][ks].x = pack_bf16(p[8 * ks + 0], p[8 * ks + 1]);
-        pb[rb][ks].y = pack_bf16(p[8 * ks + 2], p[8 * ks + 3]);
-        pb[rb][ks].z = pack_bf16(p[8 * ks + 4], p[8 * ks + 5]);
-        pb[rb][ks].w = pack_bf16(p[8 * ks + 6], p[8 * ks + 7]);
+        pb[rb][ks].x = pack_bf16(p[rb][8 * ks + 0], p[rb][8 * ks + 1]);
+        pb[rb][ks].y = pack_bf16(p[rb][8 * ks + 2], p[rb][8 * ks + 3]);
+        pb[rb][ks].z = pack_bf16(p[rb][8 * ks + 4], p[rb][8 * ks + 5]);
+        pb[rb][ks].w = pack_bf16(p[rb][8 * ks + 6], p[rb][8 * ks + 7]);
       }
     }
     // O^T[d][q row] += sum_token V[token][d] * P[q row][token]
@@ -559,6 +563,31 @@ struct MfmaTile {
           acc[rb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va[mb][ks]),
                                                                 __builtin_bit_cast(bf16x8, pb[rb][ks]),
                                                                 acc[rb][mb], 0, 0, 0);
+    // rows dominated by a few keys: P enters as two bf16 terms (the rounding
+    // remainder in a second pass), about 16 significant bits
+    if (__builtin_amdgcn_ballot_w64(heavy)) {
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          u32 lo[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const u32 h = pb[rb][ks][e];
+            lo[e] = pack_bf16(p[rb][8 * ks + 2 * e] - bf16lo(h), p[rb][8 * ks + 2 * e + 1] - bf16hi(h));
+          }
+          pb[rb][ks] = u32x4{lo[0], lo[1], lo[2], lo[3]};
+        }
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int rb = 0; rb < NRB; ++rb)
+            acc[rb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va[mb][ks]),
+                                                                  __builtin_bit_cast(bf16x8, pb[rb][ks]),
+                                                                  acc[rb][mb], 0, 0, 0);
+    }
   }
 
   // Long-window variant of compute (query tiles that see thousands of keys),

@@ -222,3 +222,27 @@ def test_sequences_with_empty_windows_are_skipped(pk):
     got, flags = attn_gpu(case, pk)
     assert flags == 0
     assert_close(got, oracle_attn(case), "empty windows")
+
+
+SCALE_SHAPES = [
+    ([300, 700], [1, 1], 8, 2, 64),            # VALU tile
+    ([900, 70], [1, 1], 32, 8, 128),           # VALU tile, head_dim 128
+    ([700, 33], [3, 2], 8, 2, 128),            # MFMA 12 rows
+    ([600, 256, 9], [6, 5, 1], 8, 2, 128),     # MFMA 24 rows
+    ([1500, 40], [16, 4], 16, 4, 64),          # MFMA 64 rows
+]
+
+
+@pytest.mark.parametrize("scale", [-0.2, 0.0, 0.3, 0.6])
+@pytest.mark.parametrize("i", range(len(SCALE_SHAPES)))
+def test_decode_and_verify_any_finite_scale(pk, i, scale):
+    """The split kernel scales every score before its mask and maximum, so a
+    negative scale, a zero scale (the mean of the visible values) and large
+    scales (3.4x and 6.8x the usual 1/sqrt(128): peaky rows where a few keys
+    carry the weight) all follow the definition, on both row tiles."""
+    seq_lens, q_lens, Hq, Hkv, D = SCALE_SHAPES[i]
+    say(f"decode/verify scale {scale}: shape {i}")
+    case = make_tiny_case(500 + i, seq_lens, q_lens, Hq=Hq, Hkv=Hkv, D=D, scale=scale)
+    got, flags = attn_gpu(case, pk)
+    assert flags == 0
+    assert_close(got, oracle_attn(case), f"scale {scale} shape {i}")

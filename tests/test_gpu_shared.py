@@ -166,3 +166,15 @@ def test_planned_shape_on_the_shared_call(pk):
     torch.cuda.synchronize()
     assert pk.pkv_attn_check_errors(ws) == 0
     assert_close(out.cpu().numpy(), oracle_attn(case), "shared with a planned shape")
+
+
+@pytest.mark.parametrize("scale", [-0.2, 0.0, 0.6])
+def test_shared_prefix_any_finite_scale(pk, scale):
+    """The prefix kernel runs a negative scale on -q and a zero scale on q = 0;
+    the tails and the merge take the scale as given."""
+    case = shared_case(440, 2, [30, 300, 600], [1, 3, 2])
+    case = AttnCase("shared-scale", case.q, case.k_pool, case.v_pool, case.block_table, case.seq_lens,
+                    case.q_lens, float(np.float32(scale)))
+    got, again, flags = run_shared(pk, case, 2)
+    assert flags == 0
+    assert_close(got, oracle_attn(case), f"shared scale {scale}")
