@@ -246,3 +246,19 @@ def test_decode_and_verify_any_finite_scale(pk, i, scale):
     got, flags = attn_gpu(case, pk)
     assert flags == 0
     assert_close(got, oracle_attn(case), f"scale {scale} shape {i}")
+
+
+@pytest.mark.parametrize("max_window", [1, 3])
+def test_large_ragged_batch(pk, max_window):
+    """2500 sequences of 1..512 tokens: about 20 000 workgroups, and every
+    workgroup's window-row prefix sum runs over thousands of sequences; on the
+    decode tile (windows of 1) and the MFMA tile (windows of 1..3)."""
+    rng = np.random.default_rng(40 + max_window)
+    B = 2500
+    seq_lens = rng.integers(1, 513, B)
+    q_lens = np.minimum(rng.integers(1, max_window + 1, B), seq_lens)
+    say(f"large ragged batch: {B} sequences, windows up to {max_window}")
+    case = make_tiny_case(450 + max_window, seq_lens.tolist(), q_lens.tolist(), Hq=4, Hkv=1, D=64)
+    got, flags = attn_gpu(case, pk)
+    assert flags == 0
+    assert_close(got, oracle_attn(case), f"large batch, windows up to {max_window}")
