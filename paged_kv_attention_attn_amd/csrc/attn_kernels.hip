@@ -1100,10 +1100,10 @@ __global__ __launch_bounds__(WAVES * 64) void attn_split_kernel(
 // cached prefix). A workgroup takes a query tile of kPrefillRows rows (rows =
 // window tokens times the head group) of one (sequence, KV head) and streams
 // every key the tile may see, 0 .. the tile's last token, through a ring of
-// K/V chunks shared by its waves. Each wave owns 64 of the rows on the MFMA
-// row tile, so a K/V chunk staged once in LDS feeds 4 x 64 rows; the ring is
-// filled by direct buffer->LDS loads, each wave issuing a quarter of every
-// chunk. Tiles are aligned to the end of the window, so tile 0 of every
+// K/V chunks shared by its waves. Each wave owns 32 * NRB of the rows on the
+// MFMA row tile (64 by default), so a K/V chunk staged once in LDS feeds all
+// 256 rows; the ring is filled by direct buffer->LDS loads, each wave issuing
+// an equal share of every chunk. Tiles are aligned to the end of the window, so tile 0 of every
 // sequence is the one with the most keys, and the launch takes tile 0 of every
 // (sequence, KV head) first (longest work first). All tiles of a (sequence,
 // KV head) land on the same XCD when B * Hkv is a multiple of 8, so the K/V
