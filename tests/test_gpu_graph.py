@@ -124,3 +124,31 @@ def test_shared_prefix_and_long_window_replay_bit_exact(pk):
         torch.cuda.synchronize()
         assert torch.equal(sd.out, ref_s) and torch.equal(ld.out, ref_l), f"eager after replay {rep}"
     assert pk.pkv_attn_check_errors(sws) == 0 and ld.errors() == 0
+
+
+def test_two_streams_with_separate_workspaces(pk):
+    """The library keeps no state outside the workspace: two batches (a verify
+    shape whose splits merge through the workspace counters, and a decode
+    shape) launched alternately on two streams, ten rounds, give the same bits
+    as each alone."""
+    import torch
+    say("two streams, separate workspaces")
+    a = DeviceCase(make_tiny_case(51, [4000, 2600, 900], [6, 4, 2], Hq=8, Hkv=2, D=128, num_pages=64), pk)
+    b = DeviceCase(make_tiny_case(52, [3000, 700, 5000, 64], [1, 1, 1, 1], Hq=32, Hkv=8, D=128, num_pages=64), pk)
+    ref_a = torch.from_numpy(a.result()).cuda()
+    ref_b = torch.from_numpy(b.result()).cuda()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    s1.wait_stream(torch.cuda.current_stream())
+    s2.wait_stream(torch.cuda.current_stream())
+    outs_a, outs_b = [], []
+    for _ in range(10):
+        with torch.cuda.stream(s1):
+            a.run(s1)
+            outs_a.append(a.out.clone())
+        with torch.cuda.stream(s2):
+            b.run(s2)
+            outs_b.append(b.out.clone())
+    torch.cuda.synchronize()
+    assert all(torch.equal(o, ref_a) for o in outs_a), "stream 1 results differ"
+    assert all(torch.equal(o, ref_b) for o in outs_b), "stream 2 results differ"
+    assert a.errors() == 0 and b.errors() == 0
