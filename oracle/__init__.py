@@ -21,6 +21,9 @@ What it computes is the plain definition, in float64:
   reuse at admission, prompt caching with least-recently-released eviction,
   and defragmentation; ``page_pool.copy_pages`` / ``.remap_table`` for the
   data movement a defragmentation plans.
+* ``q8_cache.encode`` / ``.decode`` -- the Q8 cache: 8-bit codes with one
+  fp32 scale per token vector, and the bf16 values they decode to (attention
+  over a Q8 cache is ``attention`` over the decoded pools).
 * ``brute`` -- an independent pure-Python loop version of the attention, per
   token and per element, used to pin ``paged_attention`` on tiny inputs.
 
@@ -35,6 +38,7 @@ from .paged_attention import decode_bf16, gather_sequence, attention, attention_
 from .greedy_accept import argmax_rows, accept, window_next
 from . import kv_cache
 from . import page_pool
+from . import q8_cache
 
 __all__ = ["decode_bf16", "gather_sequence", "attention", "attention_rows",
-           "argmax_rows", "accept", "window_next", "kv_cache", "page_pool"]
+           "argmax_rows", "accept", "window_next", "kv_cache", "page_pool", "q8_cache"]
