@@ -188,6 +188,45 @@ int pkv_attn_fwd_shared(const void* q, const void* k_pool, const void* v_pool,
                         float* out, const pkv_attn_shape* shape, int32_t shared_pages,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------ Q8 cache */
+
+/*
+ * An 8-bit K/V cache. Source: the Dynamic Generator page, "Usage" (a
+ * quantized cache mode takes the place of the plain one; an 8-bit mode is
+ * announced as about as compact as FP8 and more accurate). The page gives no
+ * format; this library's: every vector of head_dim values (one token of one
+ * KV head) is stored as int8 codes with one fp32 scale,
+ *   scale = max|x| / 127,  code = x / scale rounded to nearest (ties to even),
+ * in IEEE binary32, codes in [-127, 127]; a zero vector has scale 0, a vector
+ * holding a non-finite value scale NaN, both with codes 0. The cached value of
+ * an element is bf16(code * scale): the fp32 product rounded to bf16, nearest
+ * even. A token costs head_dim + 4 bytes per KV head (132 at D = 128, against
+ * 256 in bf16).
+ * Pool layouts: codes int8 [P, Hkv, 256, D], scales fp32 [P, Hkv, 256].
+ */
+
+/* Encode `rows` bf16 vectors src[rows, head_dim] into codes[rows, head_dim]
+ * (int8) and scales[rows] (fp32), all device memory owned by the caller; a
+ * whole pool is rows = P * Hkv * 256. rows in 0 .. 2^32, head_dim 64 or 128,
+ * else PKV_ERR_SHAPE. Bit-exact: the same codes and scales for the same
+ * input on any launch. */
+int pkv_q8_encode(const void* src, void* codes, float* scales, int64_t rows, int32_t head_dim, void* stream);
+
+/*
+ * pkv_attn_fwd over a Q8 cache: the same result as pkv_attn_fwd over bf16
+ * pools holding the cached values bf16(code * scale) (each chunk of keys is
+ * decoded into LDS inside the gather, then attended to as bf16 keys are).
+ * Arguments as pkv_attn_fwd's, with k_codes / v_codes int8 [P, Hkv, 256, D]
+ * and k_scales / v_scales fp32 [P, Hkv, 256] in place of the bf16 pools;
+ * workspace: pkv_attn_workspace_bytes. Decode / verify shapes only
+ * (max_q_len * Hq/Hkv <= PKV_MAX_ROWS), else PKV_ERR_SHAPE. Slots past a
+ * sequence's end are never read, codes nor scales.
+ */
+int pkv_attn_fwd_q8(const void* q, const void* k_codes, const float* k_scales, const void* v_codes,
+                    const float* v_scales, const int32_t* block_table, const int32_t* seq_lens,
+                    const int32_t* q_lens, float* out, const pkv_attn_shape* shape, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
 /* Synchronise `stream`, copy the error word of `workspace` into *flags
  * (PKV_EFLAG_* bits; 0 = every contract held) and clear it. It synchronises,
  * so it is not for use under stream (graph) capture. */

@@ -29,7 +29,8 @@ EXPORTS = ("pkv_attn_workspace_bytes", "pkv_attn_workspace_init", "pkv_attn_fwd"
            "pkv_kv_append", "pkv_kv_rollback", "pkv_kv_check_errors", "pkv_pool_create",
            "pkv_pool_destroy", "pkv_pool_stats", "pkv_pool_admit", "pkv_pool_alloc", "pkv_pool_retain",
            "pkv_pool_release", "pkv_pool_defrag", "pkv_pool_copy_pages", "pkv_table_remap",
-           "pkv_attn_shared_workspace_bytes", "pkv_attn_fwd_shared", "pkv_attn_plan", "pkv_shared_prefix_pages")
+           "pkv_attn_shared_workspace_bytes", "pkv_attn_fwd_shared", "pkv_attn_plan", "pkv_shared_prefix_pages",
+           "pkv_q8_encode", "pkv_attn_fwd_q8")
 
 
 class pkv_attn_shape(ctypes.Structure):
@@ -74,6 +75,10 @@ def _load():
     lib.pkv_attn_fwd.argtypes = [vp, vp, vp, i32p, i32p, i32p, vp, ctypes.POINTER(pkv_attn_shape),
                                  vp, sz, vp]
     lib.pkv_attn_fwd.restype = ctypes.c_int
+    lib.pkv_attn_fwd_q8.argtypes = [vp] * 9 + [ctypes.POINTER(pkv_attn_shape), vp, sz, vp]
+    lib.pkv_attn_fwd_q8.restype = ctypes.c_int
+    lib.pkv_q8_encode.argtypes = [vp, vp, vp, ctypes.c_int64, ctypes.c_int32, vp]
+    lib.pkv_q8_encode.restype = ctypes.c_int
     lib.pkv_attn_shared_workspace_bytes.argtypes = [ctypes.POINTER(pkv_attn_shape), ctypes.c_int32]
     lib.pkv_attn_shared_workspace_bytes.restype = sz
     lib.pkv_attn_fwd_shared.argtypes = [vp, vp, vp, i32p, i32p, i32p, vp, ctypes.POINTER(pkv_attn_shape),
@@ -213,6 +218,36 @@ def pkv_attn_fwd(q, k_pool, v_pool, block_table, seq_lens, q_lens, out, shape, w
                           _ptr(q_lens), _ptr(out), ctypes.byref(shape), _ptr(workspace),
                           workspace.numel(), _stream(stream))
     _check(rc, "pkv_attn_fwd")
+
+
+def pkv_q8_encode(src, codes, scales, stream=None):
+    """bf16 vectors src [..., D] -> int8 codes [..., D] and fp32 scales [...] (the Q8 cache format)."""
+    for t, dt, n in ((src, torch.bfloat16, "src"), (codes, torch.int8, "codes"), (scales, torch.float32, "scales")):
+        _need(t, dt, n)
+    D = src.shape[-1] if src.dim() else 0
+    rows = src.numel() // D if D else 0
+    _extents("pkv_q8_encode", (codes, rows * D, "codes"), (scales, rows, "scales"))
+    rc = LIB.pkv_q8_encode(_ptr(src), _ptr(codes), _ptr(scales), rows, D, _stream(stream))
+    _check(rc, "pkv_q8_encode")
+
+
+def pkv_attn_fwd_q8(q, k_codes, k_scales, v_codes, v_scales, block_table, seq_lens, q_lens, out, shape, workspace,
+                    stream=None):
+    """pkv_attn_fwd over a Q8 cache: codes int8 [P, Hkv, 256, D], scales fp32 [P, Hkv, 256]."""
+    s = shape
+    _attn_extents("pkv_attn_fwd_q8", shape, q, k_codes, v_codes, block_table, seq_lens, q_lens, out)
+    ns = s.num_pages * s.num_kv_heads * s.page_size
+    _extents("pkv_attn_fwd_q8", (k_scales, ns, "k_scales"), (v_scales, ns, "v_scales"))
+    for t, dt, n in ((q, torch.bfloat16, "q"), (k_codes, torch.int8, "k_codes"), (k_scales, torch.float32, "k_scales"),
+                     (v_codes, torch.int8, "v_codes"), (v_scales, torch.float32, "v_scales"),
+                     (block_table, torch.int32, "block_table"), (seq_lens, torch.int32, "seq_lens"),
+                     (q_lens, torch.int32, "q_lens"), (out, torch.float32, "out"),
+                     (workspace, torch.uint8, "workspace")):
+        _need(t, dt, n)
+    rc = LIB.pkv_attn_fwd_q8(_ptr(q), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes), _ptr(v_scales),
+                             _ptr(block_table), _ptr(seq_lens), _ptr(q_lens), _ptr(out), ctypes.byref(shape),
+                             _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(rc, "pkv_attn_fwd_q8")
 
 
 def pkv_attn_shared_workspace_bytes(shape, shared_pages):

@@ -111,6 +111,19 @@ __device__ __forceinline__ void dma16(u32x4 rsrc, u32 voff, u32 lds_addr) {
       : "memory");
 }
 
+// One 4-byte-per-lane load straight into LDS: lane i's word lands at
+// lds_addr + 4 * i.
+__device__ __forceinline__ void dma4(u32x4 rsrc, u32 voff, u32 lds_addr) {
+  asm volatile(
+      "s_nop 4\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %0, %1, 0 offen lds"
+      :
+      : "v"(voff), "s"(rsrc), "s"(lds_addr)
+      : "memory");
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -783,13 +796,23 @@ struct MfmaTile {
 
 // ------------------------------------------------------------------- kernel
 
-template <int D, class Tile, int NBUF, int WAVES>
+// Q8 (8-bit) cache: a ring slot holds a chunk's K and V codes (TC x D bytes
+// each, token-major as in the pool) and their per-token scales (a 256-byte
+// area each, filled by one 4-byte load per lane); the wave decodes the slot
+// into a bf16 K/V pair in the layout of a bf16 slot, its staging area, which
+// the row tiles read as they read a bf16 slot.
+template <int D, class Tile, int NBUF, int WAVES, bool Q8 = false>
 struct KernelCfg {
   static constexpr int W = WAVES;
   static constexpr int THREADS = WAVES * 64;
   static constexpr int TC = Tile::TC;
   using G = TileGeom<D, TC>;
-  static constexpr int RING = NBUF * 2 * G::TILE;        // per wave: K and V tiles
+  static constexpr int QTILE = TC * D;                   // Q8: code bytes of one K (or V) chunk
+  static constexpr int NCI = QTILE / 1024;               // Q8: 1 KiB code loads per K (or V) chunk
+  static_assert(!Q8 || QTILE % 1024 == 0, "code chunk must fill whole load instructions");
+  static constexpr int SLOT = Q8 ? 2 * QTILE + 512 : 2 * G::TILE;
+  static constexpr int OPS = Q8 ? 2 * NCI + 2 : 2 * G::NI;  // load instructions per chunk
+  static constexpr int RING = NBUF * SLOT + (Q8 ? 2 * G::TILE : 0);  // per wave (+ Q8 staging)
   static constexpr int QB = (Tile::RP * D * 2 + 1023) / 1024 * 1024;  // whole 1 KiB loads
   static constexpr int NQI = QB / 1024;                  // q load instructions per workgroup
   static constexpr int STAGE = WAVES * (RING + Tile::PBUF) + QB;
@@ -820,13 +843,52 @@ __device__ __forceinline__ void wait_ahead(int ahead) {
   else wait_vmcnt<0>();
 }
 
-template <int D, class Tile, int NBUF, int WAVES>
+// Decode one Q8 ring slot (see KernelCfg) into bf16 K and V tiles at stg, in
+// the swizzled layout of a bf16 slot: value = bf16(code * scale), the fp32
+// product rounded to nearest even. Each lane takes 16-code pieces (one token,
+// 16 dims) and writes them as two 16-byte chunks. Tokens past the sequence
+// end have zero codes and scales (the chunk load zero-fills them), so they
+// decode to zeros as a bf16 slot's do.
+template <int D, int TC>
+__device__ __forceinline__ void q8_decode_slot(const char* slot, char* stg) {
+  constexpr int NC = D / 8;          // 16-byte bf16 chunks per token
+  constexpr int PPT = D / 16;        // 16-code pieces per token
+  constexpr int NP = TC * PPT / 64;  // pieces per lane per tile
+  static_assert(TC * PPT % 64 == 0, "pieces must fill the wave");
+  const int lane = threadIdx.x & 63;
+  const float* sc = reinterpret_cast<const float*>(slot + 2 * TC * D);
+#pragma unroll
+  for (int kv = 0; kv < 2; ++kv) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(slot + kv * TC * D);
+    u32x4* dst = reinterpret_cast<u32x4*>(stg + kv * TC * D * 2);
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int pc = i * 64 + lane;
+      const int t = pc / PPT, h = pc % PPT;
+      const u32x4 w = src[pc];
+      const float s = sc[kv * 64 + t];
+      const u32 ws[4] = {w.x, w.y, w.z, w.w};
+      u32 o[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float c0 = (float)(int8_t)(ws[j] & 0xFFu), c1 = (float)(int8_t)((ws[j] >> 8) & 0xFFu);
+        const float c2 = (float)(int8_t)((ws[j] >> 16) & 0xFFu), c3 = (float)(int8_t)(ws[j] >> 24);
+        o[2 * j] = pack_bf16(c0 * s, c1 * s);
+        o[2 * j + 1] = pack_bf16(c2 * s, c3 * s);
+      }
+      dst[t * NC + ((2 * h) ^ (t & (NC - 1)))] = u32x4{o[0], o[1], o[2], o[3]};
+      dst[t * NC + ((2 * h + 1) ^ (t & (NC - 1)))] = u32x4{o[4], o[5], o[6], o[7]};
+    }
+  }
+}
+
+template <int D, class Tile, int NBUF, int WAVES, bool Q8 = false>
 __global__ __launch_bounds__(WAVES * 64) void attn_split_kernel(
     // leading scalars: what the first loads need, preloaded into SGPRs at
     // wave launch instead of read from the argument buffer
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ q_lens, int num_items, int B, int Hkv, int pps, int W, AttnParams p) {
-  using C = KernelCfg<D, Tile, NBUF, WAVES>;
+  using C = KernelCfg<D, Tile, NBUF, WAVES, Q8>;
   constexpr int kWaves = WAVES;
   constexpr int kThreads = WAVES * 64;
   using G = typename C::G;
@@ -928,7 +990,6 @@ __global__ __launch_bounds__(WAVES * 64) void attn_split_kernel(
     voff[i] = t * G::RB + ((pos ^ (t & (NC - 1))) * 16);
   }
 
-  const size_t head_stride = (size_t)kPage * D;  // elements per (page, head) tile
   auto issue = [&](int k) {
     const int c = wave + k * kWaves;
     const int t0 = tok_begin + c * TC;
@@ -938,16 +999,35 @@ __global__ __launch_bounds__(WAVES * 64) void attn_split_kernel(
     const int page_valid = min(kPage, seq_len - (page0 + jp) * kPage);
     int nvt = min(TC, page_valid - in_page);
     if (phys < 0) nvt = 0;
-    const size_t off = ((size_t)(phys < 0 ? 0 : phys) * Hkv + g) * head_stride + (size_t)in_page * D;
-    const u32 bytes = nvt > 0 ? (u32)(nvt * G::RB) : 0u;
-    const u32x4 rk = make_rsrc(p.k_pool + off, bytes);
-    const u32x4 rv = make_rsrc(p.v_pool + off, bytes);
-    const u32 base = uniform(ring_lds + (k % NBUF) * 2 * G::TILE);
-    wait_lgkm0();
+    const size_t tok = ((size_t)(phys < 0 ? 0 : phys) * Hkv + g) * kPage + in_page;  // token index in the pool
+    const u32 base = uniform(ring_lds + (k % NBUF) * C::SLOT);
+    if constexpr (Q8) {
+      // codes: byte i of the chunk lands at byte i of the slot (no swizzle);
+      // scales: lane i's word at word i of the scale area
+      const u32 cbytes = nvt > 0 ? (u32)(nvt * D) : 0u;
+      const u32 sbytes = nvt > 0 ? (u32)(nvt * 4) : 0u;
+      const auto* kc = reinterpret_cast<const char*>(p.k_pool) + tok * D;
+      const auto* vc = reinterpret_cast<const char*>(p.v_pool) + tok * D;
+      const u32x4 rk = make_rsrc(kc, cbytes), rv = make_rsrc(vc, cbytes);
+      const u32x4 rks = make_rsrc(p.k_scales + tok, sbytes), rvs = make_rsrc(p.v_scales + tok, sbytes);
+      wait_lgkm0();
 #pragma unroll
-    for (int i = 0; i < NI; ++i) dma16(rk, voff[i], base + i * 1024);
+      for (int i = 0; i < C::NCI; ++i) dma16(rk, (u32)(i * 64 + lane) * 16u, base + i * 1024);
 #pragma unroll
-    for (int i = 0; i < NI; ++i) dma16(rv, voff[i], base + G::TILE + i * 1024);
+      for (int i = 0; i < C::NCI; ++i) dma16(rv, (u32)(i * 64 + lane) * 16u, base + C::QTILE + i * 1024);
+      dma4(rks, (u32)lane * 4u, base + 2 * C::QTILE);
+      dma4(rvs, (u32)lane * 4u, base + 2 * C::QTILE + 256);
+    } else {
+      const size_t off = tok * D;
+      const u32 bytes = nvt > 0 ? (u32)(nvt * G::RB) : 0u;
+      const u32x4 rk = make_rsrc(p.k_pool + off, bytes);
+      const u32x4 rv = make_rsrc(p.v_pool + off, bytes);
+      wait_lgkm0();
+#pragma unroll
+      for (int i = 0; i < NI; ++i) dma16(rk, voff[i], base + i * 1024);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) dma16(rv, voff[i], base + G::TILE + i * 1024);
+    }
   };
 
   Tile tile;
@@ -960,17 +1040,22 @@ __global__ __launch_bounds__(WAVES * 64) void attn_split_kernel(
   // this wave's q loads were issued before its prologue chunks: once at most
   // `pro` chunks remain in flight they have landed; the barrier covers the
   // other waves' share
-  wait_ahead<2 * NI, NBUF>(pro);
+  wait_ahead<C::OPS, NBUF>(pro);
   asm volatile("s_barrier" ::: "memory");
   tile.load_q(qlds);
 
   for (int k = 0; k < my_chunks; ++k) {
     // chunk k has landed once at most the chunks issued after it are pending
-    wait_ahead<2 * NI, NBUF - 1>(min(NBUF - 1, my_chunks - 1 - k));
+    wait_ahead<C::OPS, NBUF - 1>(min(NBUF - 1, my_chunks - 1 - k));
     const int c = wave + k * kWaves;
     const int t0 = tok_begin + c * TC;
     const int nv = min(TC, tok_end - t0);
-    const char* kt = ring + (k % NBUF) * 2 * G::TILE;
+    const char* kt = ring + (k % NBUF) * C::SLOT;
+    if constexpr (Q8) {
+      char* stg = ring + NBUF * C::SLOT;
+      q8_decode_slot<D, TC>(kt, stg);
+      kt = stg;
+    }
     tile.fetch(kt, kt + G::TILE, nv);
     // the slot is free once its operands sit in registers: refill it now so
     // NBUF chunks stay in flight while this one is computed
@@ -1519,21 +1604,21 @@ __global__ __launch_bounds__(256) void shared_merge_kernel(SharedParams sp, Attn
   *reinterpret_cast<f32x4*>(o) = A / L;
 }
 
-template <int D, class Tile, int NBUF, int WAVES>
+template <int D, class Tile, int NBUF, int WAVES, bool Q8>
 hipError_t launch_one(const AttnParams& p, hipStream_t stream) {
   // every XCD gets ceil(pairs / 8) pairs of B items (see the kernel)
   const int pairs = p.num_items / p.B;
   const int grid = kNumXcd * ((pairs + kNumXcd - 1) / kNumXcd) * p.B;
-  hipLaunchKernelGGL((attn_split_kernel<D, Tile, NBUF, WAVES>), dim3(grid), dim3(WAVES * 64), 0, stream,
+  hipLaunchKernelGGL((attn_split_kernel<D, Tile, NBUF, WAVES, Q8>), dim3(grid), dim3(WAVES * 64), 0, stream,
                      p.block_table, p.seq_lens, p.q_lens, p.num_items, p.B, p.Hkv, p.pps, p.W, p);
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool Q8>
 hipError_t launch_d(const AttnParams& p, const AttnPlan& plan, hipStream_t stream) {
-  if (!plan.mfma) return launch_one<D, ValuTile<D, 1>, PKV_VALU_NBUF, PKV_VALU_WAVES>(p, stream);
-  if (plan.rows <= 32) return launch_one<D, MfmaTile<D, 1>, PKV_MFMA_NBUF, PKV_MFMA_WAVES>(p, stream);
-  return launch_one<D, MfmaTile<D, 2>, PKV_MFMA_NBUF, PKV_MFMA_WAVES>(p, stream);
+  if (!plan.mfma) return launch_one<D, ValuTile<D, 1>, PKV_VALU_NBUF, PKV_VALU_WAVES, Q8>(p, stream);
+  if (plan.rows <= 32) return launch_one<D, MfmaTile<D, 1>, PKV_MFMA_NBUF, PKV_MFMA_WAVES, Q8>(p, stream);
+  return launch_one<D, MfmaTile<D, 2>, PKV_MFMA_NBUF, PKV_MFMA_WAVES, Q8>(p, stream);
 }
 
 }  // namespace
@@ -1694,8 +1779,15 @@ hipError_t launch_attn(const AttnParams& p, const AttnPlan& plan, hipStream_t st
                          p.Hkv, plan.qtok, p.W, p);
     return hipGetLastError();
   }
-  if (p.D == 64) return launch_d<64>(p, plan, stream);
-  return launch_d<128>(p, plan, stream);
+  if (p.D == 64) return launch_d<64, false>(p, plan, stream);
+  return launch_d<128, false>(p, plan, stream);
+}
+
+hipError_t launch_attn_q8(const AttnParams& p, const AttnPlan& plan, hipStream_t stream) {
+  if (p.num_items == 0) return hipSuccess;
+  if (plan.prefill) return hipErrorInvalidValue;  // decode / verify rows only
+  if (p.D == 64) return launch_d<64, true>(p, plan, stream);
+  return launch_d<128, true>(p, plan, stream);
 }
 
 }  // namespace pkv

@@ -213,6 +213,41 @@ int pkv_attn_fwd(const void* q, const void* k_pool, const void* v_pool, const in
   return PKV_OK;
 }
 
+int pkv_attn_fwd_q8(const void* q, const void* k_codes, const float* k_scales, const void* v_codes,
+                    const float* v_scales, const int32_t* block_table, const int32_t* seq_lens,
+                    const int32_t* q_lens, float* out, const pkv_attn_shape* s, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  if (!s) return PKV_ERR_NULL;
+  if (!attn_shape_ok(s)) return PKV_ERR_SHAPE;
+  if ((long)s->max_q_len * (s->num_q_heads / s->num_kv_heads) > PKV_MAX_ROWS) return PKV_ERR_SHAPE;
+  if (s->num_seqs == 0 || s->total_q == 0) return PKV_OK;
+  if (!q || !k_codes || !k_scales || !v_codes || !v_scales || !block_table || !seq_lens || !q_lens || !out)
+    return PKV_ERR_NULL;
+  const int group = s->num_q_heads / s->num_kv_heads;
+  const pkv::AttnWorkspace ws = pkv::attn_workspace(s->num_seqs, s->num_kv_heads, s->max_pages_per_seq,
+                                                    s->max_q_len, group, s->head_dim, s->total_pages,
+                                                    s->pages_per_split);
+  if (!workspace || workspace_bytes < ws.total) return PKV_ERR_WORKSPACE;
+  const pkv::AttnPlan plan = pkv::attn_plan(s->num_seqs, s->num_kv_heads, s->max_pages_per_seq,
+                                            s->max_q_len, group, s->total_pages, s->pages_per_split);
+  pkv::AttnParams p =
+      attn_params(q, k_codes, v_codes, block_table, seq_lens, q_lens, out, s, workspace, ws, plan, 0);
+  p.k_scales = k_scales;
+  p.v_scales = v_scales;
+  if (pkv::launch_attn_q8(p, plan, static_cast<hipStream_t>(stream)) != hipSuccess) return PKV_ERR_HIP;
+  return PKV_OK;
+}
+
+int pkv_q8_encode(const void* src, void* codes, float* scales, int64_t rows, int32_t head_dim, void* stream) {
+  if (rows < 0 || rows > (int64_t(1) << 32) || (head_dim != 64 && head_dim != 128)) return PKV_ERR_SHAPE;
+  if (rows == 0) return PKV_OK;
+  if (!src || !codes || !scales) return PKV_ERR_NULL;
+  if (pkv::launch_q8_encode(static_cast<const uint16_t*>(src), static_cast<int8_t*>(codes), scales, (long)rows,
+                            head_dim, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return PKV_ERR_HIP;
+  return PKV_OK;
+}
+
 size_t pkv_attn_shared_workspace_bytes(const pkv_attn_shape* s, int32_t shared_pages) {
   if (!shared_shape_ok(s, shared_pages)) return 0;
   if (shared_pages == 0) return pkv_attn_workspace_bytes(s);
