@@ -151,6 +151,42 @@ class Accept:
                            self.shape, self.ws)
 
 
+def q8_leg(torch, pk, seed, R, steps, warmup, bf16_us):
+    """Attention over a Q8 cache (int8 codes + one fp32 scale per token and KV
+    head) on the batched-decode and verify workloads: the pools are encoded
+    on the GPU by pkv_q8_encode, then timed like the bf16 calls."""
+    from workloads import make_config
+    res = {}
+    for cfg in (2, 3):
+        log(f"Q8 cache, configuration {cfg}")
+        c, _ = make_config(cfg, seed=seed)
+        a = Attn(c, pk, torch, 1)
+        D = c.head_dim
+        kc = torch.empty(a.k[0].shape, dtype=torch.int8, device="cuda")
+        vc = torch.empty_like(kc)
+        ks = torch.empty(a.k[0].shape[:-1], dtype=torch.float32, device="cuda")
+        vs = torch.empty_like(ks)
+        pk.pkv_q8_encode(a.k[0], kc, ks)
+        pk.pkv_q8_encode(a.v[0], vc, vs)
+        del a.k, a.v
+        kcs, vcs = [kc] + [kc.clone() for _ in range(R - 1)], [vc] + [vc.clone() for _ in range(R - 1)]
+        kss, vss = [ks] + [ks.clone() for _ in range(R - 1)], [vs] + [vs.clone() for _ in range(R - 1)]
+        f = lambda i: pk.pkv_attn_fwd_q8(a.q, kcs[i % R], kss[i % R], vcs[i % R], vss[i % R], a.bt, a.sl, a.ql,
+                                         a.out, a.shape, a.ws)
+        ms = time_ms(torch, f, steps, warmup)
+        assert pk.pkv_attn_check_errors(a.ws) == 0, "Q8 attention flagged its inputs"
+        tokens = int(np.sum(c.seq_lens, dtype=np.int64))
+        qb = tokens * c.num_kv_heads * 2 * (D + 4)
+        res[f"config{cfg}"] = {"attn_us": round(ms * 1e3, 3), "q8_bytes": qb,
+                               "q8_gbps": round(qb / (ms * 1e-3) / 1e9, 2),
+                               "hbm_fraction": round(qb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                               "speedup_vs_bf16": round(bf16_us[cfg] / (ms * 1e3), 3) if cfg in bf16_us else None,
+                               "decode_tokens_per_s": round(c.num_seqs / (ms * 1e-3), 1)}
+        del a, kcs, vcs, kss, vss, kc, vc, ks, vs
+        torch.cuda.empty_cache()
+    return res
+
+
 def time_ms(torch, fn, steps, warmup):
     """Mean milliseconds per call of fn(i), timed with HIP events on the
     current stream (the stream every launch goes to)."""
@@ -541,6 +577,11 @@ def main():
         sweep["config3"] = {"attn_us": result["attn_us"], "kv_bytes": kv_bytes,
                             "kv_gbps": result["attn_kv_gbps"], "hbm_fraction": result["attn_hbm_fraction"]}
         result["configs"] = sweep
+
+    bf16_us = {3: result["attn_us"]}
+    if "configs" in result:
+        bf16_us[2] = result["configs"]["config2"]["attn_us"]
+    result["q8"] = q8_leg(torch, pk, args.seed, R, args.steps, args.warmup, bf16_us)
 
     if not args.no_queue:
         log("mixed job queue")
