@@ -184,6 +184,39 @@ def q8_leg(torch, pk, seed, R, steps, warmup, bf16_us):
                                "decode_tokens_per_s": round(c.num_seqs / (ms * 1e-3), 1)}
         del a, kcs, vcs, kss, vss, kc, vc, ks, vs
         torch.cuda.empty_cache()
+    # a decode batch long enough that streaming the cache sets the time:
+    # 16 sequences x 32768 tokens (2.1 GB of bf16 K/V, far above the caches),
+    # pools drawn on the GPU, the same call sequence for both formats
+    B, L, Hq, Hkv, D = 16, 32768, 32, 8, 128
+    log("Q8 cache, long decode batch")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    npg, P = L // 256, B * (L // 256) + 8
+    k = torch.randn(P, Hkv, 256, D, device="cuda", generator=g).to(torch.bfloat16)
+    v = torch.randn(P, Hkv, 256, D, device="cuda", generator=g).to(torch.bfloat16)
+    table = torch.randperm(P, device="cuda", generator=g)[:B * npg].to(torch.int32).view(B, npg).contiguous()
+    sl = torch.full((B,), L, dtype=torch.int32, device="cuda")
+    ql = torch.ones(B, dtype=torch.int32, device="cuda")
+    q = torch.randn(B, Hq, D, device="cuda", generator=g).to(torch.bfloat16)
+    out = torch.empty(B, Hq, D, device="cuda")
+    shape = pk.pkv_attn_plan(pk.attn_shape(q, k, table, 1, D ** -0.5), np.full(B, L, np.int32))
+    ws = pk.new_attn_workspace(shape)
+    kc = torch.empty(k.shape, dtype=torch.int8, device="cuda")
+    vc = torch.empty_like(kc)
+    ks = torch.empty(k.shape[:-1], dtype=torch.float32, device="cuda")
+    vs = torch.empty_like(ks)
+    pk.pkv_q8_encode(k, kc, ks)
+    pk.pkv_q8_encode(v, vc, vs)
+    tb = time_ms(torch, lambda i: pk.pkv_attn_fwd(q, k, v, table, sl, ql, out, shape, ws), steps, warmup)
+    tq = time_ms(torch, lambda i: pk.pkv_attn_fwd_q8(q, kc, ks, vc, vs, table, sl, ql, out, shape, ws), steps, warmup)
+    assert pk.pkv_attn_check_errors(ws) == 0
+    kvb, qb = B * L * Hkv * D * 4, B * L * Hkv * (D + 4) * 2
+    res["long_decode_16x32768"] = {"bf16_us": round(tb * 1e3, 2), "bf16_gbps": round(kvb / tb / 1e6, 1),
+                                   "bf16_hbm_fraction": round(kvb / tb / 1e6 / HBM_PEAK_GBPS, 4),
+                                   "q8_us": round(tq * 1e3, 2), "q8_gbps": round(qb / tq / 1e6, 1),
+                                   "speedup_vs_bf16": round(tb / tq, 3)}
+    del k, v, kc, vc, ks, vs
+    torch.cuda.empty_cache()
     return res
 
 
