@@ -154,3 +154,63 @@ def test_q8_attention_is_deterministic_and_rejects_long_windows(pk):
     long = Q8Case(make_tiny_case(151, [900], [300], Hq=8, Hkv=2, D=128), pk, plan=False)
     with pytest.raises(pk.PkvError):
         long.run()
+
+
+def test_q8_encode_and_attention_replay_bit_exact(pk):
+    """pkv_q8_encode of the pools and Q8 attention over a split shape,
+    captured together in a HIP graph: every replay equals the eager result
+    bit for bit (codes, scales and attention), with eager calls in between."""
+    say("q8 graph: encode + attention (split merge), 4 replays")
+    case = make_tiny_case(160, [4000, 2600, 900], [6, 4, 2], Hq=8, Hkv=2, D=128, num_pages=64)
+    qc = Q8Case(case, pk)
+    k, v = dev_bf16(case.k_pool), dev_bf16(case.v_pool)
+
+    def step():
+        pk.pkv_q8_encode(k, qc.kc, qc.ks)
+        pk.pkv_q8_encode(v, qc.vc, qc.vs)
+        pk.pkv_attn_fwd_q8(qc.q, qc.kc, qc.ks, qc.vc, qc.vs, qc.bt, qc.sl, qc.ql, qc.out, qc.shape, qc.ws)
+
+    step()
+    torch.cuda.synchronize()
+    ref_out, ref_kc, ref_ks = qc.out.clone(), qc.kc.clone(), qc.ks.clone()
+    assert_close(ref_out.cpu().numpy(), qc.expected(), "q8 graph eager")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        qc.out.fill_(float("nan"))
+        qc.kc.fill_(99)
+        qc.ks.fill_(-1.0)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(qc.out, ref_out), f"replay {rep}: attention differs"
+        assert torch.equal(qc.kc, ref_kc), f"replay {rep}: codes differ"
+        assert torch.equal(qc.ks.isnan(), ref_ks.isnan())
+        assert torch.equal(torch.nan_to_num(qc.ks), torch.nan_to_num(ref_ks)), f"replay {rep}: scales differ"
+        step()
+        torch.cuda.synchronize()
+        assert torch.equal(qc.out, ref_out), f"eager after replay {rep}: attention differs"
+    assert pk.pkv_attn_check_errors(qc.ws) == 0
+
+
+@pytest.mark.parametrize("i", range(4))
+def test_q8_dominant_keys_with_cancelling_values(pk, i):
+    """The peaky rows of the bf16 suite (three planted keys carrying almost all
+    of a row's weight, values v, -1.1 v, 0.3 v) over a Q8 cache."""
+    from tests.test_gpu_peaky import SHAPES, plant
+    seq_lens, q_lens, Hq, Hkv, D = SHAPES[i]
+    if max(q_lens) * (Hq // Hkv) > pk.PKV_MAX_ROWS:
+        pytest.skip("long windows are not served over a Q8 cache")
+    say(f"q8 peaky rows {i}: seq_lens {seq_lens} q_lens {q_lens} Hq {Hq} Hkv {Hkv} D {D}")
+    case = plant(make_tiny_case(600 + i, seq_lens, q_lens, Hq=Hq, Hkv=Hkv, D=D), 700 + i)
+    qc = Q8Case(case, pk)
+    got, flags = qc.run()
+    assert flags == 0
+    assert_close(got, qc.expected(), f"q8 peaky {i}")
