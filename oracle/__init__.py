@@ -24,6 +24,8 @@ What it computes is the plain definition, in float64:
 * ``q8_cache.encode`` / ``.decode`` -- the Q8 cache: 8-bit codes with one
   fp32 scale per token vector, and the bf16 values they decode to (attention
   over a Q8 cache is ``attention`` over the decoded pools).
+* ``q4_cache.encode`` / ``.decode`` -- the Q4 cache: the same scheme at 4
+  bits (codes in [-7, 7], two nibbles per byte).
 * ``brute`` -- an independent pure-Python loop version of the attention, per
   token and per element, used to pin ``paged_attention`` on tiny inputs.
 
@@ -39,6 +41,7 @@ from .greedy_accept import argmax_rows, accept, window_next
 from . import kv_cache
 from . import page_pool
 from . import q8_cache
+from . import q4_cache
 
 __all__ = ["decode_bf16", "gather_sequence", "attention", "attention_rows",
-           "argmax_rows", "accept", "window_next", "kv_cache", "page_pool", "q8_cache"]
+           "argmax_rows", "accept", "window_next", "kv_cache", "page_pool", "q8_cache", "q4_cache"]
