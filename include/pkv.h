@@ -227,6 +227,29 @@ int pkv_attn_fwd_q8(const void* q, const void* k_codes, const float* k_scales, c
                     const int32_t* q_lens, float* out, const pkv_attn_shape* shape, void* workspace,
                     size_t workspace_bytes, void* stream);
 
+/*
+ * A 4-bit K/V cache: the same scheme at 4 bits (the Dynamic Generator page,
+ * "Usage", names a Q4 cache mode as the generator's quantized cache; it gives
+ * no format): scale = max|x| / 7, code = x / scale rounded to nearest even,
+ * codes in [-7, 7]; zero and non-finite vectors as for Q8. Codes are stored as
+ * the nibble code + 8, two per byte: dim 2i in the low nibble of byte i. The
+ * cached value is bf16(code * scale). A token costs head_dim / 2 + 4 bytes
+ * per KV head (68 at D = 128).
+ * Pool layouts: codes uint8 [P, Hkv, 256, D / 2], scales fp32 [P, Hkv, 256].
+ */
+
+/* Encode `rows` bf16 vectors src[rows, head_dim] into codes[rows, head_dim / 2]
+ * (uint8, packed) and scales[rows] (fp32), as pkv_q8_encode. */
+int pkv_q4_encode(const void* src, void* codes, float* scales, int64_t rows, int32_t head_dim, void* stream);
+
+/* pkv_attn_fwd_q8 over a Q4 cache (k_codes / v_codes uint8 [P, Hkv, 256, D / 2]):
+ * the same result as pkv_attn_fwd over the decoded values; same arguments,
+ * workspace and limits. */
+int pkv_attn_fwd_q4(const void* q, const void* k_codes, const float* k_scales, const void* v_codes,
+                    const float* v_scales, const int32_t* block_table, const int32_t* seq_lens,
+                    const int32_t* q_lens, float* out, const pkv_attn_shape* shape, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
 /* Synchronise `stream`, copy the error word of `workspace` into *flags
  * (PKV_EFLAG_* bits; 0 = every contract held) and clear it. It synchronises,
  * so it is not for use under stream (graph) capture. */

@@ -30,7 +30,7 @@ EXPORTS = ("pkv_attn_workspace_bytes", "pkv_attn_workspace_init", "pkv_attn_fwd"
            "pkv_pool_destroy", "pkv_pool_stats", "pkv_pool_admit", "pkv_pool_alloc", "pkv_pool_retain",
            "pkv_pool_release", "pkv_pool_defrag", "pkv_pool_copy_pages", "pkv_table_remap",
            "pkv_attn_shared_workspace_bytes", "pkv_attn_fwd_shared", "pkv_attn_plan", "pkv_shared_prefix_pages",
-           "pkv_q8_encode", "pkv_attn_fwd_q8")
+           "pkv_q8_encode", "pkv_attn_fwd_q8", "pkv_q4_encode", "pkv_attn_fwd_q4")
 
 
 class pkv_attn_shape(ctypes.Structure):
@@ -79,6 +79,10 @@ def _load():
     lib.pkv_attn_fwd_q8.restype = ctypes.c_int
     lib.pkv_q8_encode.argtypes = [vp, vp, vp, ctypes.c_int64, ctypes.c_int32, vp]
     lib.pkv_q8_encode.restype = ctypes.c_int
+    lib.pkv_attn_fwd_q4.argtypes = [vp] * 9 + [ctypes.POINTER(pkv_attn_shape), vp, sz, vp]
+    lib.pkv_attn_fwd_q4.restype = ctypes.c_int
+    lib.pkv_q4_encode.argtypes = [vp, vp, vp, ctypes.c_int64, ctypes.c_int32, vp]
+    lib.pkv_q4_encode.restype = ctypes.c_int
     lib.pkv_attn_shared_workspace_bytes.argtypes = [ctypes.POINTER(pkv_attn_shape), ctypes.c_int32]
     lib.pkv_attn_shared_workspace_bytes.restype = sz
     lib.pkv_attn_fwd_shared.argtypes = [vp, vp, vp, i32p, i32p, i32p, vp, ctypes.POINTER(pkv_attn_shape),
@@ -175,7 +179,7 @@ def attn_shape(q, k_pool, block_table, max_q_len, scale, total_pages=0):
     total_q, Hq, D = q.shape
     P, Hkv, page, D2 = k_pool.shape
     B, W = block_table.shape
-    if D2 != D:
+    if D2 != D and not (k_pool.dtype == torch.uint8 and 2 * D2 == D):   # Q4 pools hold D / 2 bytes
         raise ValueError("q and pool head_dim differ")
     return pkv_attn_shape(B, Hq, Hkv, D, page, P, W, total_q, int(max_q_len), float(scale), int(total_pages), 0)
 
@@ -248,6 +252,39 @@ def pkv_attn_fwd_q8(q, k_codes, k_scales, v_codes, v_scales, block_table, seq_le
                              _ptr(block_table), _ptr(seq_lens), _ptr(q_lens), _ptr(out), ctypes.byref(shape),
                              _ptr(workspace), workspace.numel(), _stream(stream))
     _check(rc, "pkv_attn_fwd_q8")
+
+
+def pkv_q4_encode(src, codes, scales, stream=None):
+    """bf16 vectors src [..., D] -> packed uint8 codes [..., D / 2] and fp32 scales [...] (the Q4 format)."""
+    for t, dt, n in ((src, torch.bfloat16, "src"), (codes, torch.uint8, "codes"), (scales, torch.float32, "scales")):
+        _need(t, dt, n)
+    D = src.shape[-1] if src.dim() else 0
+    rows = src.numel() // D if D else 0
+    _extents("pkv_q4_encode", (codes, rows * D // 2, "codes"), (scales, rows, "scales"))
+    rc = LIB.pkv_q4_encode(_ptr(src), _ptr(codes), _ptr(scales), rows, D, _stream(stream))
+    _check(rc, "pkv_q4_encode")
+
+
+def pkv_attn_fwd_q4(q, k_codes, k_scales, v_codes, v_scales, block_table, seq_lens, q_lens, out, shape, workspace,
+                    stream=None):
+    """pkv_attn_fwd over a Q4 cache: codes uint8 [P, Hkv, 256, D / 2], scales fp32 [P, Hkv, 256]."""
+    s = shape
+    qn = s.total_q * s.num_q_heads * s.head_dim
+    ns = s.num_pages * s.num_kv_heads * s.page_size
+    _extents("pkv_attn_fwd_q4", (q, qn, "q"), (out, qn, "out"), (k_codes, ns * s.head_dim // 2, "k_codes"),
+             (v_codes, ns * s.head_dim // 2, "v_codes"), (k_scales, ns, "k_scales"), (v_scales, ns, "v_scales"),
+             (block_table, s.num_seqs * s.max_pages_per_seq, "block_table"), (seq_lens, s.num_seqs, "seq_lens"),
+             (q_lens, s.num_seqs, "q_lens"))
+    for t, dt, n in ((q, torch.bfloat16, "q"), (k_codes, torch.uint8, "k_codes"), (k_scales, torch.float32, "k_scales"),
+                     (v_codes, torch.uint8, "v_codes"), (v_scales, torch.float32, "v_scales"),
+                     (block_table, torch.int32, "block_table"), (seq_lens, torch.int32, "seq_lens"),
+                     (q_lens, torch.int32, "q_lens"), (out, torch.float32, "out"),
+                     (workspace, torch.uint8, "workspace")):
+        _need(t, dt, n)
+    rc = LIB.pkv_attn_fwd_q4(_ptr(q), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes), _ptr(v_scales),
+                             _ptr(block_table), _ptr(seq_lens), _ptr(q_lens), _ptr(out), ctypes.byref(shape),
+                             _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(rc, "pkv_attn_fwd_q4")
 
 
 def pkv_attn_shared_workspace_bytes(shape, shared_pages):

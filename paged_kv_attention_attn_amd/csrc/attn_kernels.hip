@@ -796,23 +796,24 @@ struct MfmaTile {
 
 // ------------------------------------------------------------------- kernel
 
-// Q8 (8-bit) cache: a ring slot holds a chunk's K and V codes (TC x D bytes
-// each, token-major as in the pool) and their per-token scales (a 256-byte
-// area each, filled by one 4-byte load per lane); the wave decodes the slot
-// into a bf16 K/V pair in the layout of a bf16 slot, its staging area, which
-// the row tiles read as they read a bf16 slot.
-template <int D, class Tile, int NBUF, int WAVES, bool Q8 = false>
+// Quantized caches (QBITS = 8: int8 codes; 4: two 4-bit codes per byte): a
+// ring slot holds a chunk's K and V codes (TC x D x QBITS / 8 bytes each,
+// token-major as in the pool, in whole 1 KiB load areas) and their per-token
+// scales (a 256-byte area each, filled by one 4-byte load per lane); the wave
+// decodes the slot into a bf16 K/V pair in the layout of a bf16 slot, its
+// staging area, which the row tiles read as they read a bf16 slot.
+template <int D, class Tile, int NBUF, int WAVES, int QBITS = 0>
 struct KernelCfg {
   static constexpr int W = WAVES;
   static constexpr int THREADS = WAVES * 64;
   static constexpr int TC = Tile::TC;
   using G = TileGeom<D, TC>;
-  static constexpr int QTILE = TC * D;                   // Q8: code bytes of one K (or V) chunk
-  static constexpr int NCI = QTILE / 1024;               // Q8: 1 KiB code loads per K (or V) chunk
-  static_assert(!Q8 || QTILE % 1024 == 0, "code chunk must fill whole load instructions");
-  static constexpr int SLOT = Q8 ? 2 * QTILE + 512 : 2 * G::TILE;
-  static constexpr int OPS = Q8 ? 2 * NCI + 2 : 2 * G::NI;  // load instructions per chunk
-  static constexpr int RING = NBUF * SLOT + (Q8 ? 2 * G::TILE : 0);  // per wave (+ Q8 staging)
+  static constexpr int QTILE = TC * D * QBITS / 8;          // code bytes of one K (or V) chunk
+  static constexpr int QAREA = (QTILE + 1023) / 1024 * 1024;  // its load area (tail read as zeros)
+  static constexpr int NCI = QAREA / 1024;               // 1 KiB code loads per K (or V) chunk
+  static constexpr int SLOT = QBITS ? 2 * QAREA + 512 : 2 * G::TILE;
+  static constexpr int OPS = QBITS ? 2 * NCI + 2 : 2 * G::NI;  // load instructions per chunk
+  static constexpr int RING = NBUF * SLOT + (QBITS ? 2 * G::TILE : 0);  // per wave (+ staging)
   static constexpr int QB = (Tile::RP * D * 2 + 1023) / 1024 * 1024;  // whole 1 KiB loads
   static constexpr int NQI = QB / 1024;                  // q load instructions per workgroup
   static constexpr int STAGE = WAVES * (RING + Tile::PBUF) + QB;
@@ -843,38 +844,52 @@ __device__ __forceinline__ void wait_ahead(int ahead) {
   else wait_vmcnt<0>();
 }
 
-// Decode one Q8 ring slot (see KernelCfg) into bf16 K and V tiles at stg, in
-// the swizzled layout of a bf16 slot: value = bf16(code * scale), the fp32
-// product rounded to nearest even. Each lane takes 16-code pieces (one token,
-// 16 dims) and writes them as two 16-byte chunks. Tokens past the sequence
-// end have zero codes and scales (the chunk load zero-fills them), so they
-// decode to zeros as a bf16 slot's do.
-template <int D, int TC>
-__device__ __forceinline__ void q8_decode_slot(const char* slot, char* stg) {
+// Decode one quantized ring slot (see KernelCfg) into bf16 K and V tiles at
+// stg, in the swizzled layout of a bf16 slot: value = bf16(code * scale), the
+// fp32 product rounded to nearest even. Each lane takes 16-code pieces (one
+// token, 16 dims: 16 bytes at QB = 8, 8 bytes of nibbles at QB = 4, dim 2i in
+// the low nibble of byte i) and writes them as two 16-byte chunks. Tokens
+// past the sequence end have zero codes and scales (the chunk load
+// zero-fills them) and decode to zeros as a bf16 slot's do; a zero byte of
+// nibbles is the code pair (-8, -8) times a zero scale.
+__device__ __forceinline__ u32 pack_codes(float a, float b, float s) { return pack_bf16(a * s, b * s); }
+
+template <int D, int TC, int QB, int QAREA>
+__device__ __forceinline__ void q_decode_slot(const char* slot, char* stg) {
   constexpr int NC = D / 8;          // 16-byte bf16 chunks per token
   constexpr int PPT = D / 16;        // 16-code pieces per token
   constexpr int NP = TC * PPT / 64;  // pieces per lane per tile
+  constexpr int PB = 16 * QB / 8;    // bytes per piece
   static_assert(TC * PPT % 64 == 0, "pieces must fill the wave");
   const int lane = threadIdx.x & 63;
-  const float* sc = reinterpret_cast<const float*>(slot + 2 * TC * D);
+  const float* sc = reinterpret_cast<const float*>(slot + 2 * QAREA);
 #pragma unroll
   for (int kv = 0; kv < 2; ++kv) {
-    const u32x4* src = reinterpret_cast<const u32x4*>(slot + kv * TC * D);
+    const char* src = slot + kv * QAREA;
     u32x4* dst = reinterpret_cast<u32x4*>(stg + kv * TC * D * 2);
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
       const int pc = i * 64 + lane;
       const int t = pc / PPT, h = pc % PPT;
-      const u32x4 w = src[pc];
       const float s = sc[kv * 64 + t];
-      const u32 ws[4] = {w.x, w.y, w.z, w.w};
       u32 o[8];
+      if constexpr (QB == 8) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(src + pc * PB);
+        const u32 ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float c0 = (float)(int8_t)(ws[j] & 0xFFu), c1 = (float)(int8_t)((ws[j] >> 8) & 0xFFu);
-        const float c2 = (float)(int8_t)((ws[j] >> 16) & 0xFFu), c3 = (float)(int8_t)(ws[j] >> 24);
-        o[2 * j] = pack_bf16(c0 * s, c1 * s);
-        o[2 * j + 1] = pack_bf16(c2 * s, c3 * s);
+        for (int j = 0; j < 4; ++j) {
+          o[2 * j] = pack_codes((float)(int8_t)(ws[j] & 0xFFu), (float)(int8_t)((ws[j] >> 8) & 0xFFu), s);
+          o[2 * j + 1] = pack_codes((float)(int8_t)((ws[j] >> 16) & 0xFFu), (float)(int8_t)(ws[j] >> 24), s);
+        }
+      } else {
+        const u32x2 w = *reinterpret_cast<const u32x2*>(src + pc * PB);
+        const u32 ws[2] = {w.x, w.y};
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int n = 0; n < 8; n += 2)
+            o[4 * j + n / 2] = pack_codes((float)((int)((ws[j] >> (4 * n)) & 15u) - 8),
+                                          (float)((int)((ws[j] >> (4 * n + 4)) & 15u) - 8), s);
       }
       dst[t * NC + ((2 * h) ^ (t & (NC - 1)))] = u32x4{o[0], o[1], o[2], o[3]};
       dst[t * NC + ((2 * h + 1) ^ (t & (NC - 1)))] = u32x4{o[4], o[5], o[6], o[7]};
@@ -882,13 +897,13 @@ __device__ __forceinline__ void q8_decode_slot(const char* slot, char* stg) {
   }
 }
 
-template <int D, class Tile, int NBUF, int WAVES, bool Q8 = false>
+template <int D, class Tile, int NBUF, int WAVES, int QB = 0>
 __global__ __launch_bounds__(WAVES * 64) void attn_split_kernel(
     // leading scalars: what the first loads need, preloaded into SGPRs at
     // wave launch instead of read from the argument buffer
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ q_lens, int num_items, int B, int Hkv, int pps, int W, AttnParams p) {
-  using C = KernelCfg<D, Tile, NBUF, WAVES, Q8>;
+  using C = KernelCfg<D, Tile, NBUF, WAVES, QB>;
   constexpr int kWaves = WAVES;
   constexpr int kThreads = WAVES * 64;
   using G = typename C::G;
@@ -1001,22 +1016,23 @@ __global__ __launch_bounds__(WAVES * 64) void attn_split_kernel(
     if (phys < 0) nvt = 0;
     const size_t tok = ((size_t)(phys < 0 ? 0 : phys) * Hkv + g) * kPage + in_page;  // token index in the pool
     const u32 base = uniform(ring_lds + (k % NBUF) * C::SLOT);
-    if constexpr (Q8) {
-      // codes: byte i of the chunk lands at byte i of the slot (no swizzle);
+    if constexpr (QB != 0) {
+      // codes: byte i of the chunk lands at byte i of its area (no swizzle);
       // scales: lane i's word at word i of the scale area
-      const u32 cbytes = nvt > 0 ? (u32)(nvt * D) : 0u;
+      constexpr int TB = D * QB / 8;  // code bytes per token
+      const u32 cbytes = nvt > 0 ? (u32)(nvt * TB) : 0u;
       const u32 sbytes = nvt > 0 ? (u32)(nvt * 4) : 0u;
-      const auto* kc = reinterpret_cast<const char*>(p.k_pool) + tok * D;
-      const auto* vc = reinterpret_cast<const char*>(p.v_pool) + tok * D;
+      const auto* kc = reinterpret_cast<const char*>(p.k_pool) + tok * TB;
+      const auto* vc = reinterpret_cast<const char*>(p.v_pool) + tok * TB;
       const u32x4 rk = make_rsrc(kc, cbytes), rv = make_rsrc(vc, cbytes);
       const u32x4 rks = make_rsrc(p.k_scales + tok, sbytes), rvs = make_rsrc(p.v_scales + tok, sbytes);
       wait_lgkm0();
 #pragma unroll
       for (int i = 0; i < C::NCI; ++i) dma16(rk, (u32)(i * 64 + lane) * 16u, base + i * 1024);
 #pragma unroll
-      for (int i = 0; i < C::NCI; ++i) dma16(rv, (u32)(i * 64 + lane) * 16u, base + C::QTILE + i * 1024);
-      dma4(rks, (u32)lane * 4u, base + 2 * C::QTILE);
-      dma4(rvs, (u32)lane * 4u, base + 2 * C::QTILE + 256);
+      for (int i = 0; i < C::NCI; ++i) dma16(rv, (u32)(i * 64 + lane) * 16u, base + C::QAREA + i * 1024);
+      dma4(rks, (u32)lane * 4u, base + 2 * C::QAREA);
+      dma4(rvs, (u32)lane * 4u, base + 2 * C::QAREA + 256);
     } else {
       const size_t off = tok * D;
       const u32 bytes = nvt > 0 ? (u32)(nvt * G::RB) : 0u;
@@ -1051,9 +1067,9 @@ __global__ __launch_bounds__(WAVES * 64) void attn_split_kernel(
     const int t0 = tok_begin + c * TC;
     const int nv = min(TC, tok_end - t0);
     const char* kt = ring + (k % NBUF) * C::SLOT;
-    if constexpr (Q8) {
+    if constexpr (QB != 0) {
       char* stg = ring + NBUF * C::SLOT;
-      q8_decode_slot<D, TC>(kt, stg);
+      q_decode_slot<D, TC, QB, C::QAREA>(kt, stg);
       kt = stg;
     }
     tile.fetch(kt, kt + G::TILE, nv);
@@ -1604,21 +1620,21 @@ __global__ __launch_bounds__(256) void shared_merge_kernel(SharedParams sp, Attn
   *reinterpret_cast<f32x4*>(o) = A / L;
 }
 
-template <int D, class Tile, int NBUF, int WAVES, bool Q8>
+template <int D, class Tile, int NBUF, int WAVES, int QB>
 hipError_t launch_one(const AttnParams& p, hipStream_t stream) {
   // every XCD gets ceil(pairs / 8) pairs of B items (see the kernel)
   const int pairs = p.num_items / p.B;
   const int grid = kNumXcd * ((pairs + kNumXcd - 1) / kNumXcd) * p.B;
-  hipLaunchKernelGGL((attn_split_kernel<D, Tile, NBUF, WAVES, Q8>), dim3(grid), dim3(WAVES * 64), 0, stream,
+  hipLaunchKernelGGL((attn_split_kernel<D, Tile, NBUF, WAVES, QB>), dim3(grid), dim3(WAVES * 64), 0, stream,
                      p.block_table, p.seq_lens, p.q_lens, p.num_items, p.B, p.Hkv, p.pps, p.W, p);
   return hipGetLastError();
 }
 
-template <int D, bool Q8>
+template <int D, int QB>
 hipError_t launch_d(const AttnParams& p, const AttnPlan& plan, hipStream_t stream) {
-  if (!plan.mfma) return launch_one<D, ValuTile<D, 1>, PKV_VALU_NBUF, PKV_VALU_WAVES, Q8>(p, stream);
-  if (plan.rows <= 32) return launch_one<D, MfmaTile<D, 1>, PKV_MFMA_NBUF, PKV_MFMA_WAVES, Q8>(p, stream);
-  return launch_one<D, MfmaTile<D, 2>, PKV_MFMA_NBUF, PKV_MFMA_WAVES, Q8>(p, stream);
+  if (!plan.mfma) return launch_one<D, ValuTile<D, 1>, PKV_VALU_NBUF, PKV_VALU_WAVES, QB>(p, stream);
+  if (plan.rows <= 32) return launch_one<D, MfmaTile<D, 1>, PKV_MFMA_NBUF, PKV_MFMA_WAVES, QB>(p, stream);
+  return launch_one<D, MfmaTile<D, 2>, PKV_MFMA_NBUF, PKV_MFMA_WAVES, QB>(p, stream);
 }
 
 }  // namespace
@@ -1779,15 +1795,15 @@ hipError_t launch_attn(const AttnParams& p, const AttnPlan& plan, hipStream_t st
                          p.Hkv, plan.qtok, p.W, p);
     return hipGetLastError();
   }
-  if (p.D == 64) return launch_d<64, false>(p, plan, stream);
-  return launch_d<128, false>(p, plan, stream);
+  if (p.D == 64) return launch_d<64, 0>(p, plan, stream);
+  return launch_d<128, 0>(p, plan, stream);
 }
 
-hipError_t launch_attn_q8(const AttnParams& p, const AttnPlan& plan, hipStream_t stream) {
+hipError_t launch_attn_quant(const AttnParams& p, const AttnPlan& plan, int qbits, hipStream_t stream) {
   if (p.num_items == 0) return hipSuccess;
-  if (plan.prefill) return hipErrorInvalidValue;  // decode / verify rows only
-  if (p.D == 64) return launch_d<64, true>(p, plan, stream);
-  return launch_d<128, true>(p, plan, stream);
+  if (plan.prefill || (qbits != 8 && qbits != 4)) return hipErrorInvalidValue;  // decode / verify rows only
+  if (qbits == 8) return p.D == 64 ? launch_d<64, 8>(p, plan, stream) : launch_d<128, 8>(p, plan, stream);
+  return p.D == 64 ? launch_d<64, 4>(p, plan, stream) : launch_d<128, 4>(p, plan, stream);
 }
 
 }  // namespace pkv

@@ -213,10 +213,12 @@ int pkv_attn_fwd(const void* q, const void* k_pool, const void* v_pool, const in
   return PKV_OK;
 }
 
-int pkv_attn_fwd_q8(const void* q, const void* k_codes, const float* k_scales, const void* v_codes,
-                    const float* v_scales, const int32_t* block_table, const int32_t* seq_lens,
-                    const int32_t* q_lens, float* out, const pkv_attn_shape* s, void* workspace,
-                    size_t workspace_bytes, void* stream) {
+namespace {
+
+int attn_fwd_quant(int qbits, const void* q, const void* k_codes, const float* k_scales, const void* v_codes,
+                   const float* v_scales, const int32_t* block_table, const int32_t* seq_lens,
+                   const int32_t* q_lens, float* out, const pkv_attn_shape* s, void* workspace,
+                   size_t workspace_bytes, void* stream) {
   if (!s) return PKV_ERR_NULL;
   if (!attn_shape_ok(s)) return PKV_ERR_SHAPE;
   if ((long)s->max_q_len * (s->num_q_heads / s->num_kv_heads) > PKV_MAX_ROWS) return PKV_ERR_SHAPE;
@@ -234,8 +236,26 @@ int pkv_attn_fwd_q8(const void* q, const void* k_codes, const float* k_scales, c
       attn_params(q, k_codes, v_codes, block_table, seq_lens, q_lens, out, s, workspace, ws, plan, 0);
   p.k_scales = k_scales;
   p.v_scales = v_scales;
-  if (pkv::launch_attn_q8(p, plan, static_cast<hipStream_t>(stream)) != hipSuccess) return PKV_ERR_HIP;
+  if (pkv::launch_attn_quant(p, plan, qbits, static_cast<hipStream_t>(stream)) != hipSuccess) return PKV_ERR_HIP;
   return PKV_OK;
+}
+
+}  // namespace
+
+int pkv_attn_fwd_q8(const void* q, const void* k_codes, const float* k_scales, const void* v_codes,
+                    const float* v_scales, const int32_t* block_table, const int32_t* seq_lens,
+                    const int32_t* q_lens, float* out, const pkv_attn_shape* s, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  return attn_fwd_quant(8, q, k_codes, k_scales, v_codes, v_scales, block_table, seq_lens, q_lens, out, s,
+                        workspace, workspace_bytes, stream);
+}
+
+int pkv_attn_fwd_q4(const void* q, const void* k_codes, const float* k_scales, const void* v_codes,
+                    const float* v_scales, const int32_t* block_table, const int32_t* seq_lens,
+                    const int32_t* q_lens, float* out, const pkv_attn_shape* s, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  return attn_fwd_quant(4, q, k_codes, k_scales, v_codes, v_scales, block_table, seq_lens, q_lens, out, s,
+                        workspace, workspace_bytes, stream);
 }
 
 int pkv_q8_encode(const void* src, void* codes, float* scales, int64_t rows, int32_t head_dim, void* stream) {
@@ -243,6 +263,16 @@ int pkv_q8_encode(const void* src, void* codes, float* scales, int64_t rows, int
   if (rows == 0) return PKV_OK;
   if (!src || !codes || !scales) return PKV_ERR_NULL;
   if (pkv::launch_q8_encode(static_cast<const uint16_t*>(src), static_cast<int8_t*>(codes), scales, (long)rows,
+                            head_dim, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return PKV_ERR_HIP;
+  return PKV_OK;
+}
+
+int pkv_q4_encode(const void* src, void* codes, float* scales, int64_t rows, int32_t head_dim, void* stream) {
+  if (rows < 0 || rows > (int64_t(1) << 32) || (head_dim != 64 && head_dim != 128)) return PKV_ERR_SHAPE;
+  if (rows == 0) return PKV_OK;
+  if (!src || !codes || !scales) return PKV_ERR_NULL;
+  if (pkv::launch_q4_encode(static_cast<const uint16_t*>(src), static_cast<uint8_t*>(codes), scales, (long)rows,
                             head_dim, static_cast<hipStream_t>(stream)) != hipSuccess)
     return PKV_ERR_HIP;
   return PKV_OK;

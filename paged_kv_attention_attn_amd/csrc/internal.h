@@ -29,7 +29,7 @@ struct AttnParams {
   float scale_log2;     // scale * log2(e)
   int32_t page_offset;  // leading table entries skipped (a shared prefix attended to elsewhere), 0 otherwise
   float* out_lse;       // nullable: [total_q, Hq] base-2 log-sum-exp of each row's scaled scores
-  const float* k_scales;  // Q8 cache only: [P, Hkv, 256] per-token scales (k_pool / v_pool hold int8 codes)
+  const float* k_scales;  // quantized caches only: [P, Hkv, 256] per-token scales (k_pool / v_pool hold codes)
   const float* v_scales;
 };
 
@@ -71,10 +71,12 @@ hipError_t launch_shared_merge(const AttnParams& p, const SharedParams& sp, hipS
 AttnWorkspace attn_workspace(int B, int Hkv, int W, int max_q_len, int group, int D, long total_pages,
                              int pages_per_split);
 hipError_t launch_attn(const AttnParams& p, const AttnPlan& plan, hipStream_t stream);
-// Same over a Q8 cache (p.k_pool / p.v_pool: int8 codes, p.k_scales / p.v_scales);
-// decode / verify plans only.
-hipError_t launch_attn_q8(const AttnParams& p, const AttnPlan& plan, hipStream_t stream);
+// Same over a quantized cache (p.k_pool / p.v_pool: codes, qbits 8 = int8 or
+// 4 = two nibbles per byte; p.k_scales / p.v_scales); decode / verify plans only.
+hipError_t launch_attn_quant(const AttnParams& p, const AttnPlan& plan, int qbits, hipStream_t stream);
 hipError_t launch_q8_encode(const uint16_t* src, int8_t* codes, float* scales, long rows, int D,
+                            hipStream_t stream);
+hipError_t launch_q4_encode(const uint16_t* src, uint8_t* codes, float* scales, long rows, int D,
                             hipStream_t stream);
 
 struct AcceptParams {

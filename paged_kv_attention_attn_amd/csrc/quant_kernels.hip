@@ -1,5 +1,5 @@
-// Q8 cache encoding for gfx950: bf16 token vectors -> 8-bit codes with one
-// fp32 scale per vector.
+// Quantized cache encoding for gfx950: bf16 token vectors -> 8-bit (Q8) or
+// 4-bit (Q4) codes with one fp32 scale per vector.
 //
 // Source: ExLlamaV2 "Dynamic Generator" page, section "Usage" (preparing the
 // model and the generator): a quantized cache mode replaces the plain one; an
@@ -10,8 +10,13 @@
 // vector with a non-finite value scale NaN, both with codes 0. Decoding (in the
 // attention kernels) is bf16(code * scale).
 //
-// One wave per vector: each lane holds D / 64 values, the largest magnitude
-// and the all-finite test are wave reductions.
+// Q4 is the same scheme at 4 bits: scale = max|x| / 7, codes in [-7, 7],
+// stored as the nibble code + 8, two per byte (dim 2i in the low nibble of
+// byte i).
+//
+// One wave per vector: each lane holds D / 64 values (Q4: a pair of adjacent
+// values, one output byte), the largest magnitude and the all-finite test are
+// wave reductions.
 
 #include "internal.h"
 
@@ -59,7 +64,57 @@ __global__ __launch_bounds__(kEncThreads) void q8_encode_kernel(const uint16_t* 
   if (lane == 0) scales[row] = all_finite ? scale : __builtin_nanf("");
 }
 
+// Q4: lane l holds dims 2l and 2l + 1 (lanes past D / 2 hold nothing) and
+// writes byte l of the vector's codes.
+template <int D>
+__global__ __launch_bounds__(kEncThreads) void q4_encode_kernel(const uint16_t* __restrict__ src,
+                                                                uint8_t* __restrict__ codes,
+                                                                float* __restrict__ scales, long rows) {
+  const int lane = threadIdx.x & 63;
+  const long row = (long)blockIdx.x * kEncWaves + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const bool active = lane < D / 2;
+  float v[2] = {0.f, 0.f};
+  if (active) {
+    const uint32_t w = *reinterpret_cast<const uint32_t*>(src + row * D + 2 * lane);
+    v[0] = bf16_to_f32((uint16_t)(w & 0xFFFFu));
+    v[1] = bf16_to_f32((uint16_t)(w >> 16));
+  }
+  bool finite = true;
+  float amax = 0.f;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    finite &= __builtin_isfinite(v[e]);
+    amax = fmaxf(amax, __builtin_isfinite(v[e]) ? fabsf(v[e]) : 0.f);
+  }
+  for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+  const bool all_finite = __builtin_amdgcn_ballot_w64(!finite) == 0;
+  const float scale = amax / 7.f;  // IEEE division, rounded to nearest
+  uint32_t nib[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    int q = 0;
+    if (all_finite && scale > 0.f) q = (int)fminf(fmaxf(__builtin_rintf(v[e] / scale), -7.f), 7.f);
+    nib[e] = (uint32_t)(q + 8);
+  }
+  if (active) codes[row * (D / 2) + lane] = (uint8_t)(nib[0] | (nib[1] << 4));
+  if (lane == 0) scales[row] = all_finite ? scale : __builtin_nanf("");
+}
+
 }  // namespace
+
+hipError_t launch_q4_encode(const uint16_t* src, uint8_t* codes, float* scales, long rows, int D,
+                            hipStream_t stream) {
+  if (rows <= 0) return hipSuccess;
+  const long blocks = (rows + kEncWaves - 1) / kEncWaves;
+  if (D == 64)
+    hipLaunchKernelGGL(q4_encode_kernel<64>, dim3((unsigned)blocks), dim3(kEncThreads), 0, stream, src, codes,
+                       scales, rows);
+  else
+    hipLaunchKernelGGL(q4_encode_kernel<128>, dim3((unsigned)blocks), dim3(kEncThreads), 0, stream, src, codes,
+                       scales, rows);
+  return hipGetLastError();
+}
 
 hipError_t launch_q8_encode(const uint16_t* src, int8_t* codes, float* scales, long rows, int D,
                             hipStream_t stream) {
