@@ -151,44 +151,60 @@ class Accept:
                            self.shape, self.ws)
 
 
-def q8_leg(torch, pk, seed, R, steps, warmup, bf16_us):
-    """Attention over a Q8 cache (int8 codes + one fp32 scale per token and KV
-    head) on the batched-decode and verify workloads: the pools are encoded
-    on the GPU by pkv_q8_encode, then timed like the bf16 calls."""
+QUANT = {  # format: (encode call, attention call, code dtype, code bytes per value)
+    "q8": ("pkv_q8_encode", "pkv_attn_fwd_q8", "int8", 1.0),
+    "q4": ("pkv_q4_encode", "pkv_attn_fwd_q4", "uint8", 0.5),
+}
+
+
+def quant_codes(torch, pk, fmt, k, v):
+    """Encode bf16 pools k, v into (k codes, k scales, v codes, v scales) on the GPU."""
+    enc, _, dt, per = QUANT[fmt]
+    P, Hkv, page, D = k.shape
+    out = []
+    for x in (k, v):
+        c = torch.empty(P, Hkv, page, int(D * per), dtype=getattr(torch, dt), device="cuda")
+        sc = torch.empty(P, Hkv, page, dtype=torch.float32, device="cuda")
+        getattr(pk, enc)(x, c, sc)
+        out += [c, sc]
+    return out
+
+
+def quant_leg(torch, pk, seed, R, steps, warmup, bf16_us):
+    """Attention over the quantized caches (Q8: int8 codes, Q4: two 4-bit
+    codes per byte, each with one fp32 scale per token and KV head) on the
+    batched-decode and verify workloads: the pools are encoded on the GPU by
+    the library's encoders, then timed like the bf16 calls (R replicas)."""
     from workloads import make_config
-    res = {}
+    res = {"q8": {}, "q4": {}}
     for cfg in (2, 3):
-        log(f"Q8 cache, configuration {cfg}")
         c, _ = make_config(cfg, seed=seed)
         a = Attn(c, pk, torch, 1)
         D = c.head_dim
-        kc = torch.empty(a.k[0].shape, dtype=torch.int8, device="cuda")
-        vc = torch.empty_like(kc)
-        ks = torch.empty(a.k[0].shape[:-1], dtype=torch.float32, device="cuda")
-        vs = torch.empty_like(ks)
-        pk.pkv_q8_encode(a.k[0], kc, ks)
-        pk.pkv_q8_encode(a.v[0], vc, vs)
-        del a.k, a.v
-        kcs, vcs = [kc] + [kc.clone() for _ in range(R - 1)], [vc] + [vc.clone() for _ in range(R - 1)]
-        kss, vss = [ks] + [ks.clone() for _ in range(R - 1)], [vs] + [vs.clone() for _ in range(R - 1)]
-        f = lambda i: pk.pkv_attn_fwd_q8(a.q, kcs[i % R], kss[i % R], vcs[i % R], vss[i % R], a.bt, a.sl, a.ql,
-                                         a.out, a.shape, a.ws)
-        ms = time_ms(torch, f, steps, warmup)
-        assert pk.pkv_attn_check_errors(a.ws) == 0, "Q8 attention flagged its inputs"
         tokens = int(np.sum(c.seq_lens, dtype=np.int64))
-        qb = tokens * c.num_kv_heads * 2 * (D + 4)
-        res[f"config{cfg}"] = {"attn_us": round(ms * 1e3, 3), "q8_bytes": qb,
-                               "q8_gbps": round(qb / (ms * 1e-3) / 1e9, 2),
-                               "hbm_fraction": round(qb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-                               "speedup_vs_bf16": round(bf16_us[cfg] / (ms * 1e3), 3) if cfg in bf16_us else None,
-                               "decode_tokens_per_s": round(c.num_seqs / (ms * 1e-3), 1)}
-        del a, kcs, vcs, kss, vss, kc, vc, ks, vs
+        for fmt in ("q8", "q4"):
+            log(f"{fmt} cache, configuration {cfg}")
+            reps = [quant_codes(torch, pk, fmt, a.k[0], a.v[0])]
+            reps += [[t.clone() for t in reps[0]] for _ in range(R - 1)]
+            call = getattr(pk, QUANT[fmt][1])
+            f = lambda i: call(a.q, *reps[i % R], a.bt, a.sl, a.ql, a.out, a.shape, a.ws)
+            ms = time_ms(torch, f, steps, warmup)
+            assert pk.pkv_attn_check_errors(a.ws) == 0, f"{fmt} attention flagged its inputs"
+            qb = int(tokens * c.num_kv_heads * 2 * (D * QUANT[fmt][3] + 4))
+            res[fmt][f"config{cfg}"] = {
+                "attn_us": round(ms * 1e3, 3), "code_bytes": qb, "code_gbps": round(qb / (ms * 1e-3) / 1e9, 2),
+                "hbm_fraction": round(qb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                "speedup_vs_bf16": round(bf16_us[cfg] / (ms * 1e3), 3) if cfg in bf16_us else None,
+                "decode_tokens_per_s": round(c.num_seqs / (ms * 1e-3), 1)}
+            del reps
+            torch.cuda.empty_cache()
+        del a
         torch.cuda.empty_cache()
     # a decode batch long enough that streaming the cache sets the time:
     # 16 sequences x 32768 tokens (2.1 GB of bf16 K/V, far above the caches),
-    # pools drawn on the GPU, the same call sequence for both formats
+    # pools drawn on the GPU, the same call sequence for every format
     B, L, Hq, Hkv, D = 16, 32768, 32, 8, 128
-    log("Q8 cache, long decode batch")
+    log("quantized caches, long decode batch")
     g = torch.Generator(device="cuda")
     g.manual_seed(seed)
     npg, P = L // 256, B * (L // 256) + 8
@@ -201,21 +217,22 @@ def q8_leg(torch, pk, seed, R, steps, warmup, bf16_us):
     out = torch.empty(B, Hq, D, device="cuda")
     shape = pk.pkv_attn_plan(pk.attn_shape(q, k, table, 1, D ** -0.5), np.full(B, L, np.int32))
     ws = pk.new_attn_workspace(shape)
-    kc = torch.empty(k.shape, dtype=torch.int8, device="cuda")
-    vc = torch.empty_like(kc)
-    ks = torch.empty(k.shape[:-1], dtype=torch.float32, device="cuda")
-    vs = torch.empty_like(ks)
-    pk.pkv_q8_encode(k, kc, ks)
-    pk.pkv_q8_encode(v, vc, vs)
     tb = time_ms(torch, lambda i: pk.pkv_attn_fwd(q, k, v, table, sl, ql, out, shape, ws), steps, warmup)
-    tq = time_ms(torch, lambda i: pk.pkv_attn_fwd_q8(q, kc, ks, vc, vs, table, sl, ql, out, shape, ws), steps, warmup)
-    assert pk.pkv_attn_check_errors(ws) == 0
-    kvb, qb = B * L * Hkv * D * 4, B * L * Hkv * (D + 4) * 2
-    res["long_decode_16x32768"] = {"bf16_us": round(tb * 1e3, 2), "bf16_gbps": round(kvb / tb / 1e6, 1),
-                                   "bf16_hbm_fraction": round(kvb / tb / 1e6 / HBM_PEAK_GBPS, 4),
-                                   "q8_us": round(tq * 1e3, 2), "q8_gbps": round(qb / tq / 1e6, 1),
-                                   "speedup_vs_bf16": round(tb / tq, 3)}
-    del k, v, kc, vc, ks, vs
+    kvb = B * L * Hkv * D * 4
+    long = {"bf16_us": round(tb * 1e3, 2), "bf16_gbps": round(kvb / tb / 1e6, 1),
+            "bf16_hbm_fraction": round(kvb / tb / 1e6 / HBM_PEAK_GBPS, 4)}
+    for fmt in ("q8", "q4"):
+        codes = quant_codes(torch, pk, fmt, k, v)
+        call = getattr(pk, QUANT[fmt][1])
+        tq = time_ms(torch, lambda i: call(q, *codes, table, sl, ql, out, shape, ws), steps, warmup)
+        assert pk.pkv_attn_check_errors(ws) == 0
+        qb = int(B * L * Hkv * 2 * (D * QUANT[fmt][3] + 4))
+        long.update({f"{fmt}_us": round(tq * 1e3, 2), f"{fmt}_code_gbps": round(qb / tq / 1e6, 1),
+                     f"{fmt}_speedup_vs_bf16": round(tb / tq, 3)})
+        del codes
+        torch.cuda.empty_cache()
+    res["long_decode_16x32768"] = long
+    del k, v
     torch.cuda.empty_cache()
     return res
 
@@ -614,7 +631,7 @@ def main():
     bf16_us = {3: result["attn_us"]}
     if "configs" in result:
         bf16_us[2] = result["configs"]["config2"]["attn_us"]
-    result["q8"] = q8_leg(torch, pk, args.seed, R, args.steps, args.warmup, bf16_us)
+    result["quantized"] = quant_leg(torch, pk, args.seed, R, args.steps, args.warmup, bf16_us)
 
     if not args.no_queue:
         log("mixed job queue")
