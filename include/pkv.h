@@ -365,6 +365,21 @@ int pkv_kv_append(const void* k_new, const void* v_new, void* k_pool, void* v_po
  * Contract: 0 <= accepted <= q_len <= seq_len; ceil(seq_len / 256) <= W; the
  * stack stays within num_pages.
  */
+/* pkv_kv_append into quantized pools (the Q8 and Q4 formats of pkv_q8_encode /
+ * pkv_q4_encode): the same pages, table and length updates, with every window
+ * row's vector encoded into its slot's codes and scale (codes int8
+ * [P, Hkv, 256, D] for Q8, uint8 [P, Hkv, 256, D / 2] for Q4; scales fp32
+ * [P, Hkv, 256]); the same contract and error behaviour. pkv_kv_rollback
+ * serves every format (it touches no pool). */
+int pkv_kv_append_q8(const void* k_new, const void* v_new, void* k_codes, float* k_scales, void* v_codes,
+                     float* v_scales, int32_t* block_table, int32_t* seq_lens, const int32_t* q_lens,
+                     int32_t* free_pages, int32_t* free_count, const pkv_kv_shape* shape, void* workspace,
+                     size_t workspace_bytes, void* stream);
+int pkv_kv_append_q4(const void* k_new, const void* v_new, void* k_codes, float* k_scales, void* v_codes,
+                     float* v_scales, int32_t* block_table, int32_t* seq_lens, const int32_t* q_lens,
+                     int32_t* free_pages, int32_t* free_count, const pkv_kv_shape* shape, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
 int pkv_kv_rollback(int32_t* block_table, int32_t* seq_lens, const int32_t* q_lens, const int32_t* accepted,
                     int32_t* free_pages, int32_t* free_count, const pkv_kv_shape* shape, void* workspace,
                     size_t workspace_bytes, void* stream);

@@ -30,7 +30,8 @@ EXPORTS = ("pkv_attn_workspace_bytes", "pkv_attn_workspace_init", "pkv_attn_fwd"
            "pkv_pool_destroy", "pkv_pool_stats", "pkv_pool_admit", "pkv_pool_alloc", "pkv_pool_retain",
            "pkv_pool_release", "pkv_pool_defrag", "pkv_pool_copy_pages", "pkv_table_remap",
            "pkv_attn_shared_workspace_bytes", "pkv_attn_fwd_shared", "pkv_attn_plan", "pkv_shared_prefix_pages",
-           "pkv_q8_encode", "pkv_attn_fwd_q8", "pkv_q4_encode", "pkv_attn_fwd_q4")
+           "pkv_q8_encode", "pkv_attn_fwd_q8", "pkv_q4_encode", "pkv_attn_fwd_q4", "pkv_kv_append_q8",
+           "pkv_kv_append_q4")
 
 
 class pkv_attn_shape(ctypes.Structure):
@@ -79,6 +80,9 @@ def _load():
     lib.pkv_attn_fwd_q8.restype = ctypes.c_int
     lib.pkv_q8_encode.argtypes = [vp, vp, vp, ctypes.c_int64, ctypes.c_int32, vp]
     lib.pkv_q8_encode.restype = ctypes.c_int
+    for name in ("pkv_kv_append_q8", "pkv_kv_append_q4"):
+        getattr(lib, name).argtypes = [vp] * 11 + [ctypes.POINTER(pkv_kv_shape), vp, sz, vp]
+        getattr(lib, name).restype = ctypes.c_int
     lib.pkv_attn_fwd_q4.argtypes = [vp] * 9 + [ctypes.POINTER(pkv_attn_shape), vp, sz, vp]
     lib.pkv_attn_fwd_q4.restype = ctypes.c_int
     lib.pkv_q4_encode.argtypes = [vp, vp, vp, ctypes.c_int64, ctypes.c_int32, vp]
@@ -386,9 +390,11 @@ def pkv_version():
     return int(LIB.pkv_version())
 
 
-def kv_shape(k_pool, block_table, total_q):
-    """pkv_kv_shape from tensor extents (pool [P, Hkv, 256, D], block_table [B, W])."""
+def kv_shape(k_pool, block_table, total_q, head_dim=None):
+    """pkv_kv_shape from tensor extents (pool [P, Hkv, 256, D], block_table [B, W]);
+    head_dim for packed Q4 code pools, whose last extent is D / 2."""
     P, Hkv, page, D = k_pool.shape
+    D = int(head_dim) if head_dim is not None else D
     B, W = block_table.shape
     return pkv_kv_shape(B, Hkv, D, page, P, W, int(total_q))
 
@@ -402,6 +408,50 @@ def new_kv_workspace(shape, device="cuda"):
     if n == 0:
         raise PkvError("pkv_kv_workspace_bytes: shape rejected")
     return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def _kv_append_quant(qbits, k_new, v_new, k_codes, k_scales, v_codes, v_scales, block_table, seq_lens, q_lens,
+                     free_pages, free_count, shape, workspace, stream):
+    call = f"pkv_kv_append_q{qbits}"
+    s = shape
+    vecs = s.num_pages * s.num_kv_heads * s.page_size
+    code_dt = torch.int8 if qbits == 8 else torch.uint8
+    win = s.total_q * s.num_kv_heads * s.head_dim
+    _extents(call, (k_codes, vecs * s.head_dim * qbits // 8, "k_codes"),
+             (v_codes, vecs * s.head_dim * qbits // 8, "v_codes"), (k_scales, vecs, "k_scales"),
+             (v_scales, vecs, "v_scales"), (k_new if win else None, win, "k_new"),
+             (v_new if win else None, win, "v_new"), (block_table, s.num_seqs * s.max_pages_per_seq, "block_table"),
+             (seq_lens, s.num_seqs, "seq_lens"), (q_lens, s.num_seqs, "q_lens"),
+             (free_pages, s.num_pages, "free_pages"), (free_count, 1, "free_count"))
+    for t, dt, n in ((k_codes, code_dt, "k_codes"), (v_codes, code_dt, "v_codes"),
+                     (k_scales, torch.float32, "k_scales"), (v_scales, torch.float32, "v_scales"),
+                     (block_table, torch.int32, "block_table"), (seq_lens, torch.int32, "seq_lens"),
+                     (q_lens, torch.int32, "q_lens"), (free_pages, torch.int32, "free_pages"),
+                     (free_count, torch.int32, "free_count"), (workspace, torch.uint8, "workspace")):
+        _need(t, dt, n)
+    if k_new.numel():
+        _need(k_new, torch.bfloat16, "k_new")
+        _need(v_new, torch.bfloat16, "v_new")
+    kn = k_new if k_new.numel() else None
+    vn = v_new if v_new.numel() else None
+    rc = getattr(LIB, call)(_ptr(kn), _ptr(vn), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes), _ptr(v_scales),
+                            _ptr(block_table), _ptr(seq_lens), _ptr(q_lens), _ptr(free_pages), _ptr(free_count),
+                            ctypes.byref(shape), _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(rc, call)
+
+
+def pkv_kv_append_q8(k_new, v_new, k_codes, k_scales, v_codes, v_scales, block_table, seq_lens, q_lens,
+                     free_pages, free_count, shape, workspace, stream=None):
+    """pkv_kv_append into Q8 pools (codes int8 [P, Hkv, 256, D], scales fp32 [P, Hkv, 256])."""
+    _kv_append_quant(8, k_new, v_new, k_codes, k_scales, v_codes, v_scales, block_table, seq_lens, q_lens,
+                     free_pages, free_count, shape, workspace, stream)
+
+
+def pkv_kv_append_q4(k_new, v_new, k_codes, k_scales, v_codes, v_scales, block_table, seq_lens, q_lens,
+                     free_pages, free_count, shape, workspace, stream=None):
+    """pkv_kv_append into Q4 pools (codes uint8 [P, Hkv, 256, D / 2], scales fp32 [P, Hkv, 256])."""
+    _kv_append_quant(4, k_new, v_new, k_codes, k_scales, v_codes, v_scales, block_table, seq_lens, q_lens,
+                     free_pages, free_count, shape, workspace, stream)
 
 
 def pkv_kv_append(k_new, v_new, k_pool, v_pool, block_table, seq_lens, q_lens, free_pages, free_count,

@@ -411,6 +411,55 @@ int pkv_kv_append(const void* k_new, const void* v_new, void* k_pool, void* v_po
   return PKV_OK;
 }
 
+namespace {
+
+int kv_append_quant(int qbits, const void* k_new, const void* v_new, void* k_codes, float* k_scales, void* v_codes,
+                    float* v_scales, int32_t* block_table, int32_t* seq_lens, const int32_t* q_lens,
+                    int32_t* free_pages, int32_t* free_count, const pkv_kv_shape* s, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  if (!s) return PKV_ERR_NULL;
+  if (!kv_shape_ok(s)) return PKV_ERR_SHAPE;
+  if (s->num_seqs == 0) return PKV_OK;
+  if (!k_codes || !v_codes || !k_scales || !v_scales || !block_table || !seq_lens || !q_lens || !free_pages ||
+      !free_count)
+    return PKV_ERR_NULL;
+  if (s->total_q > 0 && (!k_new || !v_new)) return PKV_ERR_NULL;
+  if (!workspace || workspace_bytes < pkv::kv_workspace(s->total_q).total) return PKV_ERR_WORKSPACE;
+  pkv::KvParams p = kv_params(s, workspace);
+  p.k_new = static_cast<const uint16_t*>(k_new);
+  p.v_new = static_cast<const uint16_t*>(v_new);
+  p.k_pool = static_cast<uint16_t*>(k_codes);
+  p.v_pool = static_cast<uint16_t*>(v_codes);
+  p.k_scales = k_scales;
+  p.v_scales = v_scales;
+  p.qbits = qbits;
+  p.block_table = block_table;
+  p.seq_lens = seq_lens;
+  p.q_lens = q_lens;
+  p.free_pages = free_pages;
+  p.free_count = free_count;
+  if (pkv::launch_kv_append(p, static_cast<hipStream_t>(stream)) != hipSuccess) return PKV_ERR_HIP;
+  return PKV_OK;
+}
+
+}  // namespace
+
+int pkv_kv_append_q8(const void* k_new, const void* v_new, void* k_codes, float* k_scales, void* v_codes,
+                     float* v_scales, int32_t* block_table, int32_t* seq_lens, const int32_t* q_lens,
+                     int32_t* free_pages, int32_t* free_count, const pkv_kv_shape* s, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  return kv_append_quant(8, k_new, v_new, k_codes, k_scales, v_codes, v_scales, block_table, seq_lens, q_lens,
+                         free_pages, free_count, s, workspace, workspace_bytes, stream);
+}
+
+int pkv_kv_append_q4(const void* k_new, const void* v_new, void* k_codes, float* k_scales, void* v_codes,
+                     float* v_scales, int32_t* block_table, int32_t* seq_lens, const int32_t* q_lens,
+                     int32_t* free_pages, int32_t* free_count, const pkv_kv_shape* s, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  return kv_append_quant(4, k_new, v_new, k_codes, k_scales, v_codes, v_scales, block_table, seq_lens, q_lens,
+                         free_pages, free_count, s, workspace, workspace_bytes, stream);
+}
+
 int pkv_kv_rollback(int32_t* block_table, int32_t* seq_lens, const int32_t* q_lens, const int32_t* accepted,
                     int32_t* free_pages, int32_t* free_count, const pkv_kv_shape* s, void* workspace,
                     size_t workspace_bytes, void* stream) {

@@ -109,6 +109,9 @@ struct KvParams {
   uint32_t* err;             // workspace error word
   uint32_t* go;              // append: 1 once the plan passed its checks
   int32_t* row_tok;          // append: [total_q] destination page * 256 + slot
+  float* k_scales;           // quantized append: [P, Hkv, 256] (k_pool / v_pool hold codes)
+  float* v_scales;
+  int32_t qbits;             // 0: bf16 pools; 8 or 4: quantized (codes encoded from k_new / v_new)
   int32_t B, Hkv, D, P, W, total_q;
 };
 

@@ -20,12 +20,15 @@
 //
 // append = kv_append_plan_kernel (one workgroup: checks, page allocation,
 // table and length updates, and the destination token of every window row)
-// then kv_append_copy_kernel (16-byte pieces of the rows into the pools).
+// then kv_append_copy_kernel (16-byte pieces of the rows into the pools), or
+// for quantized pools kv_append_quant_kernel (each row vector encoded into
+// its slot's codes and scale).
 // rollback = kv_rollback_kernel (one workgroup).
 
 #include "internal.h"
 
 #include "pkv.h"
+#include "quant_encode.h"
 
 namespace pkv {
 namespace {
@@ -173,6 +176,27 @@ __global__ __launch_bounds__(kCopyThreads) void kv_append_copy_kernel(KvParams p
   *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
 }
 
+// Quantized pools: one wave per vector w = (row r, KV head g, pool K or V),
+// the pool fastest, encodes the row's D values straight into the codes and
+// scale of its destination slot.
+template <int QBITS, int D>
+__global__ __launch_bounds__(kCopyThreads) void kv_append_quant_kernel(KvParams p) {
+  const long w = (long)blockIdx.x * (kCopyThreads / 64) + (threadIdx.x >> 6);
+  if (w >= (long)p.total_q * p.Hkv * 2 || *p.go == 0) return;
+  const int kind = (int)(w % 2);
+  const int g = (int)((w / 2) % p.Hkv);
+  const int r = (int)(w / (2L * p.Hkv));
+  const int tok = p.row_tok[r];
+  const size_t slot = ((size_t)(tok / kPage) * p.Hkv + g) * kPage + tok % kPage;  // vector index in the pool
+  const uint16_t* src = (kind ? p.v_new : p.k_new) + ((size_t)r * p.Hkv + g) * D;
+  char* codes = reinterpret_cast<char*>(kind ? p.v_pool : p.k_pool) + slot * (D * QBITS / 8);
+  float* scale = (kind ? p.v_scales : p.k_scales) + slot;
+  if constexpr (QBITS == 8)
+    q8_encode_wave<D>(src, reinterpret_cast<int8_t*>(codes), scale);
+  else
+    q4_encode_wave<D>(src, reinterpret_cast<uint8_t*>(codes), scale);
+}
+
 // ----------------------------------------------------------------- rollback
 
 __global__ __launch_bounds__(kPlanThreads) void kv_rollback_kernel(KvParams p) {
@@ -243,6 +267,15 @@ hipError_t launch_kv_append(const KvParams& p, hipStream_t stream) {
   hipLaunchKernelGGL(kv_append_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.total_q == 0) return e;
+  if (p.qbits != 0) {
+    const long vecs = (long)p.total_q * p.Hkv * 2;
+    const dim3 grid((unsigned)((vecs + kCopyThreads / 64 - 1) / (kCopyThreads / 64)));
+    if (p.qbits == 8 && p.D == 128) hipLaunchKernelGGL((kv_append_quant_kernel<8, 128>), grid, dim3(kCopyThreads), 0, stream, p);
+    else if (p.qbits == 8) hipLaunchKernelGGL((kv_append_quant_kernel<8, 64>), grid, dim3(kCopyThreads), 0, stream, p);
+    else if (p.D == 128) hipLaunchKernelGGL((kv_append_quant_kernel<4, 128>), grid, dim3(kCopyThreads), 0, stream, p);
+    else hipLaunchKernelGGL((kv_append_quant_kernel<4, 64>), grid, dim3(kCopyThreads), 0, stream, p);
+    return hipGetLastError();
+  }
   const long pieces = (long)p.total_q * p.Hkv * 2 * (p.D / 8);
   const int grid = (int)((pieces + kCopyThreads - 1) / kCopyThreads);
   hipLaunchKernelGGL(kv_append_copy_kernel, dim3(grid), dim3(kCopyThreads), 0, stream, p);

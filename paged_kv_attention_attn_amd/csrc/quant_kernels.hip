@@ -21,6 +21,7 @@
 #include "internal.h"
 
 #include "pkv.h"
+#include "quant_encode.h"
 
 namespace pkv {
 namespace {
@@ -28,77 +29,22 @@ namespace {
 constexpr int kEncThreads = 256;
 constexpr int kEncWaves = kEncThreads / 64;
 
-__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
-
 template <int D>
 __global__ __launch_bounds__(kEncThreads) void q8_encode_kernel(const uint16_t* __restrict__ src,
                                                                 int8_t* __restrict__ codes,
                                                                 float* __restrict__ scales, long rows) {
-  constexpr int EPL = D / 64;  // values per lane
-  const int lane = threadIdx.x & 63;
   const long row = (long)blockIdx.x * kEncWaves + (threadIdx.x >> 6);
   if (row >= rows) return;
-  const uint16_t* x = src + row * D + lane * EPL;
-  float v[EPL];
-  float amax = 0.f;
-  bool finite = true;
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) {
-    v[e] = bf16_to_f32(x[e]);
-    finite &= __builtin_isfinite(v[e]);
-    amax = fmaxf(amax, __builtin_isfinite(v[e]) ? fabsf(v[e]) : 0.f);
-  }
-  for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
-  const bool all_finite = __builtin_amdgcn_ballot_w64(!finite) == 0;
-  const float scale = amax / 127.f;  // IEEE division, rounded to nearest
-  int8_t* c = codes + row * D + lane * EPL;
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) {
-    int q = 0;
-    if (all_finite && scale > 0.f) {
-      const float t = __builtin_rintf(v[e] / scale);
-      q = (int)fminf(fmaxf(t, -127.f), 127.f);
-    }
-    c[e] = (int8_t)q;
-  }
-  if (lane == 0) scales[row] = all_finite ? scale : __builtin_nanf("");
+  q8_encode_wave<D>(src + row * D, codes + row * D, scales + row);
 }
 
-// Q4: lane l holds dims 2l and 2l + 1 (lanes past D / 2 hold nothing) and
-// writes byte l of the vector's codes.
 template <int D>
 __global__ __launch_bounds__(kEncThreads) void q4_encode_kernel(const uint16_t* __restrict__ src,
                                                                 uint8_t* __restrict__ codes,
                                                                 float* __restrict__ scales, long rows) {
-  const int lane = threadIdx.x & 63;
   const long row = (long)blockIdx.x * kEncWaves + (threadIdx.x >> 6);
   if (row >= rows) return;
-  const bool active = lane < D / 2;
-  float v[2] = {0.f, 0.f};
-  if (active) {
-    const uint32_t w = *reinterpret_cast<const uint32_t*>(src + row * D + 2 * lane);
-    v[0] = bf16_to_f32((uint16_t)(w & 0xFFFFu));
-    v[1] = bf16_to_f32((uint16_t)(w >> 16));
-  }
-  bool finite = true;
-  float amax = 0.f;
-#pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    finite &= __builtin_isfinite(v[e]);
-    amax = fmaxf(amax, __builtin_isfinite(v[e]) ? fabsf(v[e]) : 0.f);
-  }
-  for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
-  const bool all_finite = __builtin_amdgcn_ballot_w64(!finite) == 0;
-  const float scale = amax / 7.f;  // IEEE division, rounded to nearest
-  uint32_t nib[2];
-#pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    int q = 0;
-    if (all_finite && scale > 0.f) q = (int)fminf(fmaxf(__builtin_rintf(v[e] / scale), -7.f), 7.f);
-    nib[e] = (uint32_t)(q + 8);
-  }
-  if (active) codes[row * (D / 2) + lane] = (uint8_t)(nib[0] | (nib[1] << 4));
-  if (lane == 0) scales[row] = all_finite ? scale : __builtin_nanf("");
+  q4_encode_wave<D>(src + row * D, codes + row * (D / 2), scales + row);
 }
 
 }  // namespace

@@ -1,0 +1,117 @@
+"""Cache append into quantized pools (pkv_kv_append_q8 / _q4) against the
+oracle: the oracle appends the window's bf16 rows into bf16 pools and encodes
+the result vector by vector, so every slot the append did not write keeps its
+codes and every slot it wrote holds the encoding of its new row. Codes,
+scales (NaN-aware, by bit pattern), tables, lengths and the free stack must
+match bit for bit; attention over the appended quantized pools then matches
+the oracle's attention over the decoded pools; a broken contract changes
+nothing."""
+
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+import oracle
+from oracle import kv_cache as kv, q8_cache, q4_cache
+from tests.gpu_util import say, dev_bf16, dev_i32, assert_close
+from tests.test_oracle_kv import random_state
+
+FMT = {8: (q8_cache, "pkv_kv_append_q8", "pkv_attn_fwd_q8"), 4: (q4_cache, "pkv_kv_append_q4", "pkv_attn_fwd_q4")}
+
+
+@pytest.fixture(scope="module")
+def pk():
+    assert torch.cuda.is_available()
+    import paged_kv_attention_attn_amd as pk
+    return pk
+
+
+def same_scales(got, exp):
+    ok = ~np.isnan(exp)
+    return np.array_equal(np.isnan(got), np.isnan(exp)) and np.array_equal(got.view(np.uint32)[ok],
+                                                                           exp.view(np.uint32)[ok])
+
+
+class QuantCache:
+    def __init__(self, pk, qbits, kp, vp, table, lens, free, cnt, total_q):
+        self.pk, self.qbits = pk, qbits
+        self.mod, self.append_name, self.attn_name = FMT[qbits]
+        kc, ks = self.mod.encode(kp)
+        vc, vs = self.mod.encode(vp)
+        self.kc, self.ks = torch.from_numpy(kc).cuda(), torch.from_numpy(ks).cuda()
+        self.vc, self.vs = torch.from_numpy(vc).cuda(), torch.from_numpy(vs).cuda()
+        self.table, self.lens, self.free = dev_i32(table), dev_i32(lens), dev_i32(free)
+        self.count = dev_i32(np.array([cnt]))
+        self.shape = pk.kv_shape(self.kc, self.table, total_q, head_dim=kp.shape[-1])
+        self.ws = pk.new_kv_workspace(self.shape)
+
+    def append(self, kn, vn, ql):
+        getattr(self.pk, self.append_name)(dev_bf16(kn), dev_bf16(vn), self.kc, self.ks, self.vc, self.vs,
+                                           self.table, self.lens, dev_i32(ql), self.free, self.count, self.shape,
+                                           self.ws)
+        torch.cuda.synchronize()
+
+    def check(self, k2, v2, t2, l2, f2, c2, what):
+        ekc, eks = self.mod.encode(k2)
+        evc, evs = self.mod.encode(v2)
+        np.testing.assert_array_equal(self.kc.cpu().numpy(), ekc, err_msg=f"{what}: K codes")
+        np.testing.assert_array_equal(self.vc.cpu().numpy(), evc, err_msg=f"{what}: V codes")
+        assert same_scales(self.ks.cpu().numpy(), eks), f"{what}: K scales"
+        assert same_scales(self.vs.cpu().numpy(), evs), f"{what}: V scales"
+        np.testing.assert_array_equal(self.table.cpu().numpy(), t2, err_msg=f"{what}: table")
+        np.testing.assert_array_equal(self.lens.cpu().numpy(), l2, err_msg=f"{what}: lengths")
+        c = int(self.count.cpu()[0])
+        assert c == c2
+        np.testing.assert_array_equal(self.free.cpu().numpy()[:c], f2[:c2])
+
+
+@pytest.mark.parametrize("qbits,seed,D", [(8, 0, 128), (8, 2, 64), (4, 1, 128), (4, 3, 64)])
+def test_quantized_append_matches_the_oracle(pk, qbits, seed, D):
+    say(f"quantized append Q{qbits} seed {seed} D {D}")
+    kp, vp, table, lens, ql, kn, vn, free, cnt = random_state(seed, B=6, P=48, W=8, Hkv=8, D=D, max_q=16)
+    qc = QuantCache(pk, qbits, kp, vp, table, lens, free, cnt, int(ql.sum()))
+    qc.append(kn, vn, ql)
+    k2, v2, t2, l2, f2, c2 = kv.append(kp, vp, table, lens, ql, kn, vn, free, cnt)
+    qc.check(k2, v2, t2, l2, f2, c2, f"Q{qbits} append")
+    assert pk.pkv_kv_check_errors(qc.ws) == 0
+
+    # attention over appended pools: the same tables and windows with finite
+    # values (the state above holds arbitrary bit patterns, NaN included)
+    from workloads import normal_bf16
+    rng = np.random.default_rng(100 + seed)
+    kp, vp = normal_bf16(rng, kp.shape), normal_bf16(rng, vp.shape)
+    kn, vn = normal_bf16(rng, kn.shape), normal_bf16(rng, vn.shape)
+    qc = QuantCache(pk, qbits, kp, vp, table, lens, free, cnt, int(ql.sum()))
+    qc.append(kn, vn, ql)
+    k2, v2, t2, l2, f2, c2 = kv.append(kp, vp, table, lens, ql, kn, vn, free, cnt)
+    qc.check(k2, v2, t2, l2, f2, c2, f"Q{qbits} append, finite values")
+    Hq = 16
+    q = normal_bf16(rng, (int(ql.sum()), Hq, D))
+    qd = dev_bf16(q)
+    ashape = pk.attn_shape(qd, qc.kc, qc.table, max(1, int(ql.max())), float(np.float32(D ** -0.5)))
+    aws = pk.new_attn_workspace(ashape)
+    out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    getattr(pk, qc.attn_name)(qd, qc.kc, qc.ks, qc.vc, qc.vs, qc.table, qc.lens, dev_i32(ql), out, ashape, aws)
+    torch.cuda.synchronize()
+    assert pk.pkv_attn_check_errors(aws) == 0
+    ekc, eks = qc.mod.encode(k2)
+    evc, evs = qc.mod.encode(v2)
+    ref = oracle.attention(q, qc.mod.decode(ekc, eks), qc.mod.decode(evc, evs), t2, l2, ql, ashape.scale)
+    assert_close(out.cpu().numpy(), ref, f"Q{qbits} attention after append")
+
+
+@pytest.mark.parametrize("qbits", [8, 4])
+def test_quantized_append_broken_contract_changes_nothing(pk, qbits):
+    say(f"quantized append Q{qbits}: too few free pages")
+    kp, vp, table, lens, ql, kn, vn, free, cnt = random_state(7, B=6, P=48, W=8, Hkv=8, D=128, max_q=16)
+    qc = QuantCache(pk, qbits, kp, vp, table, lens, free, 0, int(ql.sum()))   # an empty free stack
+    before = [t.clone() for t in (qc.kc, qc.ks, qc.vc, qc.vs, qc.table, qc.lens)]
+    needs_pages = any(((l + q + 255) // 256) > ((l + 255) // 256) for l, q in zip(lens, ql))
+    qc.append(kn, vn, ql)
+    flags = pk.pkv_kv_check_errors(qc.ws)
+    if needs_pages:
+        assert flags & pk.PKV_EFLAG_SPACE
+        for a, b in zip(before, (qc.kc, qc.ks, qc.vc, qc.vs, qc.table, qc.lens)):
+            assert torch.equal(torch.nan_to_num(a.float()), torch.nan_to_num(b.float()))
