@@ -316,3 +316,36 @@ def test_shared_prefix_pages_from_host_tables(pk):
         pk.pkv_shared_prefix_pages(np.zeros((2, 3), np.int32), [1], [1], good_shape(pk, num_seqs=2,
                                                                                       max_pages_per_seq=3))
     assert pk.LIB.pkv_shared_prefix_pages(None, None, None, None) == pk.PKV_ERR_NULL
+
+
+def test_quantized_calls_check_shapes_pointers_and_workspace(pk):
+    """The Q8 / Q4 entry points refuse bad input before any launch: unsupported
+    head sizes and row counts in the encoders, long windows, missing scale
+    pools and short workspaces in attention, and the cache appends' pointer
+    and workspace checks."""
+    d = ctypes.c_void_p(0x1000)
+    for enc in (pk.LIB.pkv_q8_encode, pk.LIB.pkv_q4_encode):
+        assert enc(d, d, d, 10, 96, None) == pk.PKV_ERR_SHAPE
+        assert enc(d, d, d, -1, 128, None) == pk.PKV_ERR_SHAPE
+        assert enc(d, d, d, (1 << 32) + 1, 128, None) == pk.PKV_ERR_SHAPE
+        assert enc(None, d, d, 10, 128, None) == pk.PKV_ERR_NULL
+        assert enc(None, None, None, 0, 64, None) == pk.PKV_OK
+    s = good_shape(pk)
+    need = pk.pkv_attn_workspace_bytes(s)
+    for fwd in (pk.LIB.pkv_attn_fwd_q8, pk.LIB.pkv_attn_fwd_q4):
+        assert fwd(*([d] * 9), None, d, need, None) == pk.PKV_ERR_NULL
+        assert fwd(d, d, None, d, d, d, d, d, d, ctypes.byref(s), d, need, None) == pk.PKV_ERR_NULL  # k scales
+        assert fwd(*([d] * 9), ctypes.byref(s), d, need - 1, None) == pk.PKV_ERR_WORKSPACE
+        long = good_shape(pk)
+        long.max_q_len = 64          # 64 window rows x the group: past the decode / verify tile
+        assert fwd(*([d] * 9), ctypes.byref(long), d, 1 << 30, None) == pk.PKV_ERR_SHAPE
+        empty = good_shape(pk, num_seqs=0, total_q=0)
+        assert fwd(*([None] * 9), ctypes.byref(empty), None, 0, None) == pk.PKV_OK
+    ks = pk.pkv_kv_shape(4, 8, 128, 256, 256, 32, 24)
+    kneed = pk.pkv_kv_workspace_bytes(ks)
+    for app in (pk.LIB.pkv_kv_append_q8, pk.LIB.pkv_kv_append_q4):
+        assert app(*([d] * 11), ctypes.byref(ks), d, kneed - 1, None) == pk.PKV_ERR_WORKSPACE
+        assert app(d, d, d, None, d, d, d, d, d, d, d, ctypes.byref(ks), d, kneed, None) == pk.PKV_ERR_NULL
+        assert app(*([d] * 11), None, d, kneed, None) == pk.PKV_ERR_NULL
+        empty = pk.pkv_kv_shape(0, 8, 128, 256, 256, 32, 0)
+        assert app(*([None] * 11), ctypes.byref(empty), None, 0, None) == pk.PKV_OK
