@@ -884,12 +884,33 @@ __device__ __forceinline__ void q_decode_slot(const char* slot, char* stg) {
       } else {
         const u32x2 w = *reinterpret_cast<const u32x2*>(src + pc * PB);
         const u32 ws[2] = {w.x, w.y};
+        // nibble n = code + 8: n * s - 8 s is code * s exactly, so one fma
+        // rounds it as the product would be. -8 s is exact while finite; a
+        // wave holding a scale above 2^124 (a vector near the bf16 maximum)
+        // takes the subtract-then-multiply form instead.
+        const float s8 = -8.f * s;
+        if (__builtin_amdgcn_ballot_w64(!__builtin_isfinite(s8)) == 0) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+          for (int j = 0; j < 2; ++j) {
+            // even / odd dims, one nibble per byte; the masks go through asm so the
+            // byte converts below read them whole (v_cvt_f32_ubyte0..3) instead of
+            // the compiler extracting every nibble on its own
+            u32 lo, hi;
+            asm("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(lo) : "v"(ws[j]));
+            asm("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(hi) : "v"(ws[j] >> 4));
 #pragma unroll
-          for (int n = 0; n < 8; n += 2)
-            o[4 * j + n / 2] = pack_codes((float)((int)((ws[j] >> (4 * n)) & 15u) - 8),
-                                          (float)((int)((ws[j] >> (4 * n + 4)) & 15u) - 8), s);
+            for (int b = 0; b < 4; ++b)
+              o[4 * j + b] = pack_bf16(__builtin_fmaf((float)((lo >> (8 * b)) & 0xFFu), s, s8),
+                                       __builtin_fmaf((float)((hi >> (8 * b)) & 0xFFu), s, s8));
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int n = 0; n < 8; n += 2)
+              o[4 * j + n / 2] = pack_codes((float)((int)((ws[j] >> (4 * n)) & 15u) - 8),
+                                            (float)((int)((ws[j] >> (4 * n + 4)) & 15u) - 8), s);
+        }
       }
       dst[t * NC + ((2 * h) ^ (t & (NC - 1)))] = u32x4{o[0], o[1], o[2], o[3]};
       dst[t * NC + ((2 * h + 1) ^ (t & (NC - 1)))] = u32x4{o[4], o[5], o[6], o[7]};

@@ -122,3 +122,27 @@ def test_q4_attention_is_deterministic_and_rejects_long_windows(pk):
     with pytest.raises(ValueError):   # Q8-sized code pools for a Q4 call
         pk.pkv_attn_fwd_q4(qc.q, torch.zeros(qc.kc.numel() * 2, dtype=torch.uint8, device="cuda"), qc.ks, qc.vc,
                            qc.vs, qc.bt, qc.sl, qc.ql, qc.out, qc.shape, qc.ws)
+
+
+def test_q4_huge_values_take_the_exact_fallback(pk):
+    """A V vector near the bf16 maximum (scale above 2^124, so -8 * scale
+    overflows) makes its wave decode by subtract-then-multiply: the result
+    still matches the oracle. Sequence 0 has 2 tokens, so its outputs (a
+    weighted mean of the values) stay finite."""
+    say("q4: a value vector near the bf16 maximum")
+    case = make_tiny_case(190, [2, 300, 45], [1, 1, 1], Hq=8, Hkv=2, D=128)
+    v = case.v_pool.copy()
+    page = int(case.block_table[0, 0])
+    rng = np.random.default_rng(191)
+    for g in range(v.shape[1]):
+        x = rng.uniform(-1, 1, 128) * 1.0e38
+        x[7] = 1.6e38                                        # scale = 1.6e38 / 7 > 2^124
+        v[page, g, 0] = f32_to_bf16_bits(x.astype(np.float32))
+    from workloads import AttnCase
+    big = AttnCase(case.name + "-huge", case.q, case.k_pool, v, case.block_table, case.seq_lens, case.q_lens,
+                   case.scale)
+    qc = Q4Case(big, pk)
+    assert np.all(qc.vs.cpu().numpy()[page, :, 0] > 2.0 ** 124)
+    got, flags = qc.run()
+    assert flags == 0
+    assert_close(got, qc.expected(), "q4 huge values")
