@@ -122,3 +122,22 @@ def test_scalar_rederivation_on_small_vectors():
             assert hi == int(d[r, j])
         for i in range(8):
             assert int(p[r, i]) == (codes[2 * i] + 8) + 16 * (codes[2 * i + 1] + 8)
+
+
+def test_every_byte_decodes_to_its_nibble_pair():
+    """All 256 bytes, at scale 1 and at an odd scale: byte b holds codes
+    (b & 15) - 8 and (b >> 4) - 8; the decoded bf16 is the float32 product
+    rounded to nearest even, done here by hand."""
+    b = np.arange(256, dtype=np.uint8).reshape(256, 1)
+    for scale in (np.float32(1.0), np.float32(0.3), np.float32(2.0 ** -130)):
+        s = np.full(256, scale, np.float32)
+        d = q4.decode(b, s)
+        for v in range(256):
+            for half, code in ((0, (v & 15) - 8), (1, (v >> 4) - 8)):
+                prod = np.float32(np.float32(code) * scale)
+                u = int(np.array([prod], np.float32).view(np.uint32)[0])
+                hi, low = u >> 16, u & 0xFFFF
+                if low > 0x8000 or (low == 0x8000 and hi & 1):
+                    hi += 1
+                assert int(d[v, half]) == (hi & 0xFFFF), (v, half, scale)
+    assert np.array_equal(q4.pack(q4.unpack(b.reshape(1, 256))), b.reshape(1, 256))

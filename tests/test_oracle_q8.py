@@ -116,3 +116,18 @@ def test_scalar_rederivation_on_small_vectors():
             if low > 0x8000 or (low == 0x8000 and hi & 1):
                 hi += 1
             assert hi == int(d[r, j])
+
+
+def test_every_code_decodes_to_the_rounded_product():
+    """All 256 codes at scales 1, 1/127, an odd value and a subnormal: the
+    decoded bf16 is the float32 product rounded to nearest even, by hand."""
+    c = np.arange(-128, 128, dtype=np.int8).reshape(1, 256)
+    for scale in (np.float32(1.0), np.float32(1.0 / 127), np.float32(0.7071), np.float32(2.0 ** -140)):
+        d = q8.decode(c, np.array([scale], np.float32))
+        for i, code in enumerate(range(-128, 128)):
+            prod = np.float32(np.float32(code) * scale)
+            u = int(np.array([prod], np.float32).view(np.uint32)[0])
+            hi, low = u >> 16, u & 0xFFFF
+            if low > 0x8000 or (low == 0x8000 and hi & 1):
+                hi += 1
+            assert int(d[0, i]) == (hi & 0xFFFF), (code, scale)
