@@ -146,3 +146,22 @@ def test_q4_huge_values_take_the_exact_fallback(pk):
     got, flags = qc.run()
     assert flags == 0
     assert_close(got, qc.expected(), "q4 huge values")
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("qbits,max_window", [(8, 1), (4, 3)])
+def test_quantized_large_ragged_batch(pk, qbits, max_window):
+    """The bf16 suite's large ragged batch (2500 sequences of 1..512 tokens,
+    about 20 000 workgroups) over a Q8 or Q4 cache, on the decode tile
+    (windows of 1) and the MFMA tile (windows of 1..3)."""
+    from tests.test_gpu_q8 import Q8Case
+    rng = np.random.default_rng(40 + max_window)
+    B = 2500
+    seq_lens = rng.integers(1, 513, B)
+    q_lens = np.minimum(rng.integers(1, max_window + 1, B), seq_lens)
+    say(f"Q{qbits} large ragged batch: {B} sequences, windows up to {max_window}")
+    case = make_tiny_case(460 + max_window, seq_lens.tolist(), q_lens.tolist(), Hq=4, Hkv=1, D=64)
+    qc = (Q8Case if qbits == 8 else Q4Case)(case, pk)
+    got, flags = qc.run()
+    assert flags == 0
+    assert_close(got, qc.expected(), f"Q{qbits} large batch, windows up to {max_window}")
