@@ -479,6 +479,15 @@ int pkv_pool_defrag(pkv_pool* pool, int32_t move_referenced, int32_t* remap, int
 int pkv_pool_copy_pages(void* k_pool, void* v_pool, const int32_t* src, const int32_t* dst, int32_t n_moves,
                         int32_t num_pages, int32_t num_kv_heads, int32_t head_dim, uint32_t* err, void* stream);
 
+/* pkv_pool_copy_pages for pools of any page size: copy page src[i] of both
+ * pool_a and pool_b (device buffers of num_pages pages of page_bytes bytes
+ * each) to page dst[i], for i < n_moves; same contract and error word. A
+ * quantized cache moves its code pools (page_bytes = Hkv * 256 * D for Q8,
+ * Hkv * 256 * D / 2 for Q4) and then its scale pools (Hkv * 256 * 4).
+ * page_bytes: a positive multiple of 16, else PKV_ERR_SHAPE. */
+int pkv_pool_copy_page_bytes(void* pool_a, void* pool_b, const int32_t* src, const int32_t* dst, int32_t n_moves,
+                             int32_t num_pages, int64_t page_bytes, uint32_t* err, void* stream);
+
 /* Rewrite block_table[rows, width] in place: every entry t in [0, num_pages)
  * becomes remap[t] (remap: device int32 [num_pages], entries in [0,
  * num_pages)); negative entries stay; entries >= num_pages stay and set

@@ -31,7 +31,7 @@ EXPORTS = ("pkv_attn_workspace_bytes", "pkv_attn_workspace_init", "pkv_attn_fwd"
            "pkv_pool_release", "pkv_pool_defrag", "pkv_pool_copy_pages", "pkv_table_remap",
            "pkv_attn_shared_workspace_bytes", "pkv_attn_fwd_shared", "pkv_attn_plan", "pkv_shared_prefix_pages",
            "pkv_q8_encode", "pkv_attn_fwd_q8", "pkv_q4_encode", "pkv_attn_fwd_q4", "pkv_kv_append_q8",
-           "pkv_kv_append_q4")
+           "pkv_kv_append_q4", "pkv_pool_copy_page_bytes")
 
 
 class pkv_attn_shape(ctypes.Structure):
@@ -125,6 +125,8 @@ def _load():
     lib.pkv_pool_defrag.argtypes = [vp, i32, vp, vp, vp, vp]
     lib.pkv_pool_copy_pages.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, vp, vp]
     lib.pkv_table_remap.argtypes = [vp, i32, i32, vp, i32, vp, vp]
+    lib.pkv_pool_copy_page_bytes.argtypes = [vp, vp, vp, vp, i32, i32, ctypes.c_int64, vp, vp]
+    lib.pkv_pool_copy_page_bytes.restype = ctypes.c_int
     for name in ("pkv_pool_stats", "pkv_pool_admit", "pkv_pool_alloc", "pkv_pool_retain", "pkv_pool_release",
                  "pkv_pool_defrag", "pkv_pool_copy_pages", "pkv_table_remap"):
         getattr(lib, name).restype = ctypes.c_int
@@ -579,6 +581,23 @@ def pkv_pool_copy_pages(k_pool, v_pool, src, dst, err=None, stream=None):
     rc = LIB.pkv_pool_copy_pages(_ptr(k_pool), _ptr(v_pool), _ptr(src), _ptr(dst), src.numel(), P, Hkv, D,
                                  _ptr(err), _stream(stream))
     _check(rc, "pkv_pool_copy_pages")
+
+
+def pkv_pool_copy_page_bytes(pool_a, pool_b, src, dst, err=None, stream=None):
+    """Page moves on two pools of any element type whose first extent is the
+    page (e.g. Q8 / Q4 code pools, or their scale pools); src, dst: int32."""
+    _extents("pkv_pool_copy_page_bytes", (pool_b, pool_a.numel(), "pool_b"), (dst, src.numel(), "dst"))
+    if pool_a.dtype != pool_b.dtype:
+        raise TypeError("pkv_pool_copy_page_bytes: the two pools differ in type")
+    if err is not None and err.numel() < 1:
+        raise ValueError("pkv_pool_copy_page_bytes: err needs one int32")
+    for t, n in ((pool_a, "pool_a"), (pool_b, "pool_b"), (src, "src"), (dst, "dst")):
+        _need(t, t.dtype if n.startswith("pool") else torch.int32, n)
+    P = pool_a.shape[0]
+    page_bytes = pool_a.numel() * pool_a.element_size() // P
+    rc = LIB.pkv_pool_copy_page_bytes(_ptr(pool_a), _ptr(pool_b), _ptr(src), _ptr(dst), src.numel(), P, page_bytes,
+                                      _ptr(err), _stream(stream))
+    _check(rc, "pkv_pool_copy_page_bytes")
 
 
 def pkv_table_remap(block_table, remap, err=None, stream=None):

@@ -508,6 +508,25 @@ int pkv_pool_copy_pages(void* k_pool, void* v_pool, const int32_t* src, const in
   return PKV_OK;
 }
 
+int pkv_pool_copy_page_bytes(void* pool_a, void* pool_b, const int32_t* src, const int32_t* dst, int32_t n_moves,
+                              int32_t num_pages, int64_t page_bytes, uint32_t* err, void* stream) {
+  if (n_moves < 0 || num_pages < 1 || page_bytes < 16 || page_bytes % 16 != 0) return PKV_ERR_SHAPE;
+  if ((long)num_pages * page_bytes > (1L << 40)) return PKV_ERR_SHAPE;
+  if (n_moves == 0) return PKV_OK;
+  if (!pool_a || !pool_b || !src || !dst) return PKV_ERR_NULL;
+  pkv::PageMoveParams p{};
+  p.k_pool = static_cast<uint16_t*>(pool_a);
+  p.v_pool = static_cast<uint16_t*>(pool_b);
+  p.src = src;
+  p.dst = dst;
+  p.err = err;
+  p.n_moves = n_moves;
+  p.P = num_pages;
+  p.page_bytes = static_cast<long>(page_bytes);
+  if (pkv::launch_copy_pages(p, static_cast<hipStream_t>(stream)) != hipSuccess) return PKV_ERR_HIP;
+  return PKV_OK;
+}
+
 int pkv_table_remap(int32_t* block_table, int32_t rows, int32_t width, const int32_t* remap, int32_t num_pages,
                     uint32_t* err, void* stream) {
   if (rows < 0 || width < 1 || num_pages < 1 || (long)rows * width > (1L << 31) - 1) return PKV_ERR_SHAPE;

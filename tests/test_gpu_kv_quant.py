@@ -115,3 +115,48 @@ def test_quantized_append_broken_contract_changes_nothing(pk, qbits):
         assert flags & pk.PKV_EFLAG_SPACE
         for a, b in zip(before, (qc.kc, qc.ks, qc.vc, qc.vs, qc.table, qc.lens)):
             assert torch.equal(torch.nan_to_num(a.float()), torch.nan_to_num(b.float()))
+
+
+@pytest.mark.parametrize("qbits", [8, 4])
+def test_quantized_pools_move_pages_and_attention_follows(pk, qbits):
+    """Defragmentation of quantized pools: pkv_pool_copy_page_bytes moves the
+    code pages and then the scale pages (oracle.page_pool.copy_pages on the
+    same arrays, bit for bit); with the tables remapped, attention over the
+    moved pools equals attention before the move bit for bit."""
+    from oracle import page_pool
+    from workloads import make_tiny_case
+    say(f"Q{qbits} page moves")
+    case = make_tiny_case(200 + qbits, [700, 300, 1030], [1, 3, 2], Hq=8, Hkv=2, D=128, num_pages=16)
+    mod, _, attn_name = FMT[qbits]
+    kc, ks = mod.encode(case.k_pool)
+    vc, vs = mod.encode(case.v_pool)
+    used = sorted(set(int(t) for t in case.block_table.ravel() if t >= 0))
+    free = [p for p in range(16) if p not in used]
+    moves = list(zip(used[-3:], free[:3]))                 # three referenced pages to free slots
+    src, dst = dev_i32([m[0] for m in moves]), dev_i32([m[1] for m in moves])
+    dkc, dks = torch.from_numpy(kc).cuda(), torch.from_numpy(ks).cuda()
+    dvc, dvs = torch.from_numpy(vc).cuda(), torch.from_numpy(vs).cuda()
+    q, bt, sl, ql = dev_bf16(case.q), dev_i32(case.block_table), dev_i32(case.seq_lens), dev_i32(case.q_lens)
+    shape = pk.attn_shape(q, dkc, bt, 3, case.scale)
+    ws = pk.new_attn_workspace(shape)
+    out0 = torch.empty(case.q.shape, dtype=torch.float32, device="cuda")
+    getattr(pk, attn_name)(q, dkc, dks, dvc, dvs, bt, sl, ql, out0, shape, ws)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    pk.pkv_pool_copy_page_bytes(dkc, dvc, src, dst, err)
+    pk.pkv_pool_copy_page_bytes(dks, dvs, src, dst, err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    ekc, evc = page_pool.copy_pages(kc, vc, moves)
+    eks, evs = page_pool.copy_pages(ks, vs, moves)
+    np.testing.assert_array_equal(dkc.cpu().numpy(), ekc)
+    np.testing.assert_array_equal(dvc.cpu().numpy(), evc)
+    assert same_scales(dks.cpu().numpy(), eks) and same_scales(dvs.cpu().numpy(), evs)
+    remap = np.arange(16, dtype=np.int32)
+    for a, b in moves:
+        remap[a] = b
+    bt2 = dev_i32(page_pool.remap_table(case.block_table, remap))
+    out1 = torch.empty_like(out0)
+    getattr(pk, attn_name)(q, dkc, dks, dvc, dvs, bt2, sl, ql, out1, shape, ws)
+    torch.cuda.synchronize()
+    assert pk.pkv_attn_check_errors(ws) == 0
+    assert torch.equal(out0, out1)
