@@ -349,3 +349,14 @@ def test_quantized_calls_check_shapes_pointers_and_workspace(pk):
         assert app(*([d] * 11), None, d, kneed, None) == pk.PKV_ERR_NULL
         empty = pk.pkv_kv_shape(0, 8, 128, 256, 256, 32, 0)
         assert app(*([None] * 11), ctypes.byref(empty), None, 0, None) == pk.PKV_OK
+
+
+def test_byte_page_moves_check_sizes_and_pointers(pk):
+    d = ctypes.c_void_p(0x1000)
+    f = pk.LIB.pkv_pool_copy_page_bytes
+    assert f(d, d, d, d, 1, 16, 24, None, None) == pk.PKV_ERR_SHAPE         # not a multiple of 16
+    assert f(d, d, d, d, 1, 16, 0, None, None) == pk.PKV_ERR_SHAPE
+    assert f(d, d, d, d, -1, 16, 4096, None, None) == pk.PKV_ERR_SHAPE
+    assert f(d, d, d, d, 1, 1 << 20, 1 << 21, None, None) == pk.PKV_ERR_SHAPE   # 2^41 bytes of pool
+    assert f(d, None, d, d, 1, 16, 4096, None, None) == pk.PKV_ERR_NULL
+    assert f(None, None, None, None, 0, 16, 4096, None, None) == pk.PKV_OK
