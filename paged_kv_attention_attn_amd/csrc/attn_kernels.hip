@@ -35,191 +35,14 @@
 // lane hits distinct banks; the swizzle is applied on the global side of the
 // direct loads, which stay fully coalesced per 1 KiB instruction.
 
-#include "internal.h"
-
-#include "pkv.h"
+#include "device.h"
 
 #include <type_traits>
 
 namespace pkv {
 namespace {
 
-using u32 = uint32_t;
-typedef u32 u32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef u32 u32x2 __attribute__((ext_vector_type(2)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-#ifndef PKV_VALU_NBUF
-#define PKV_VALU_NBUF 2  // LDS ring depth (chunks) per wave, VALU row tile
-#endif
-#ifndef PKV_MFMA_NBUF
-#define PKV_MFMA_NBUF 2  // LDS ring depth (chunks) per wave, MFMA row tile
-#endif
-#ifndef PKV_VALU_WAVES
-#define PKV_VALU_WAVES 4  // waves per workgroup, VALU row tile
-#endif
-#ifndef PKV_MFMA_WAVES
-#define PKV_MFMA_WAVES 4  // waves per workgroup, MFMA row tile
-#endif
-#ifndef PKV_PREFILL_NBUF
-#define PKV_PREFILL_NBUF 8  // K/V chunks in the ring shared by a prefill workgroup
-#endif
-#ifndef PKV_SHARED_WG
-#define PKV_SHARED_WG kNumCu  // workgroups the shared-prefix kernel aims for
-#endif
-#ifndef PKV_FORCE_PPS
-#define PKV_FORCE_PPS 0  // pages per split; 0 = planned per shape
-#endif
-
-constexpr u32 PKV_EFLAG_PAGE_BIT = 1u, PKV_EFLAG_QLEN_BIT = 2u, PKV_EFLAG_ROWS_BIT = 4u;
-constexpr int kNumCu = 256;           // MI355X compute units
-constexpr int kValuMaxRows = 4;       // q rows per (sequence, KV head) on the VALU tile
-constexpr int kLdsPerCu = 160 * 1024;  // gfx950 LDS per CU
-constexpr float kNegInf = -__builtin_inff();
-
-__device__ __forceinline__ u32 uniform(u32 x) { return __builtin_amdgcn_readfirstlane(x); }
-
-// Raw buffer descriptor: 48-bit base, stride 0, num_records bytes. Reads at
-// offsets >= num_records return zero and never fault.
-__device__ __forceinline__ u32x4 make_rsrc(const void* base, u32 bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  u32x4 r;
-  r.x = uniform(static_cast<u32>(a));
-  r.y = uniform(static_cast<u32>(a >> 32));
-  r.z = uniform(bytes);
-  r.w = 0x00020000u;
-  return r;
-}
-
-// One 16-byte-per-lane load from the buffer straight into LDS: lane i's 16
-// bytes land at lds_addr + 16 * i. The s_nop covers the wait states a VALU
-// write of an operand SGPR needs before a VMEM read; m0 holds the LDS address.
-__device__ __forceinline__ void dma16(u32x4 rsrc, u32 voff, u32 lds_addr) {
-  asm volatile(
-      "s_nop 4\n\t"
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %0, %1, 0 offen lds"
-      :
-      : "v"(voff), "s"(rsrc), "s"(lds_addr)
-      : "memory");
-}
-
-// One 4-byte-per-lane load straight into LDS: lane i's word lands at
-// lds_addr + 4 * i.
-__device__ __forceinline__ void dma4(u32x4 rsrc, u32 voff, u32 lds_addr) {
-  asm volatile(
-      "s_nop 4\n\t"
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dword %0, %1, 0 offen lds"
-      :
-      : "v"(voff), "s"(rsrc), "s"(lds_addr)
-      : "memory");
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
-}
-
-// Max / sum over the 16 lanes of a DPP row; every lane gets the result.
-__device__ __forceinline__ float row16_max(float x) {
-  x = fmaxf(x, dpp<0xB1>(x));   // quad_perm [1,0,3,2]
-  x = fmaxf(x, dpp<0x4E>(x));   // quad_perm [2,3,0,1]
-  x = fmaxf(x, dpp<0x141>(x));  // row_half_mirror
-  x = fmaxf(x, dpp<0x140>(x));  // row_mirror
-  return x;
-}
-__device__ __forceinline__ float row16_sum(float x) {
-  x += dpp<0xB1>(x);
-  x += dpp<0x4E>(x);
-  x += dpp<0x141>(x);
-  x += dpp<0x140>(x);
-  return x;
-}
-
-__device__ __forceinline__ float shfl_xor(float x, int m) {
-  const int lane = threadIdx.x & 63;
-  return __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ m) << 2, __float_as_int(x)));
-}
-
-// Reductions across the two 32-lane halves in one VALU instruction, without
-// an LDS round trip: v_permlane32_swap exchanges the upper 32 lanes of its
-// first operand with the lower 32 of its second, so with x in both every lane
-// holds {x of this lane, x of lane ^ 32} (lane layout checked on the GPU).
-__device__ __forceinline__ float max_xor32(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float sum_xor32(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-__device__ __forceinline__ float exp2f_fast(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// Split partials cross XCDs (each XCD has its own L2). Agent-scope relaxed
-// atomic stores/loads are write-through / coherent by themselves, so the
-// partials need no L2-wide write-back or invalidate.
-__device__ __forceinline__ void st_coherent(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float ld_coherent(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ float bf16lo(u32 w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16hi(u32 w) { return __uint_as_float(w & 0xFFFF0000u); }
-
-__device__ __forceinline__ float dot2(u32 a, u32 b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c,
-                                         false);
-}
-
-__device__ __forceinline__ u32 pack_bf16(float lo, float hi) {
-  bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
-  return __builtin_bit_cast(u32, v);
-}
-
-__device__ __forceinline__ u32 lds_addr_of(const void* p) {
-  return static_cast<u32>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)(p)));
-}
-
-// Sum of q_lens[0..b) by one wave.
-__device__ __forceinline__ int wave_prefix(const int32_t* q_lens, int b) {
-  const int lane = threadIdx.x & 63;
-  int s = 0;
-  for (int i = lane; i < b; i += 64) s += q_lens[i];
-  for (int m = 32; m >= 1; m >>= 1) s += __builtin_amdgcn_ds_bpermute(((lane ^ m) << 2), s);
-  return s;
-}
-
 // ----------------------------------------------------------------- row tiles
-
-// Geometry shared by both row tiles.
-template <int D, int TC>
-struct TileGeom {
-  static constexpr int NC = D / 8;                 // 16-byte chunks per token row
-  static constexpr int RB = D * 2;                 // bytes per token row
-  static constexpr int NI = TC * NC / 64;          // 1 KiB load instructions per tile
-  static constexpr int TILE = TC * RB;             // bytes of one K (or V) chunk
-  static_assert(TC * NC % 64 == 0, "chunk must fill whole load instructions");
-};
 
 // VALU row tile: rows = 4 * RPL (RPL q rows per lane in the score phase);
 // launched with RPL = 1, where it beats the matrix cores (8 and 12 rows run
@@ -821,28 +644,6 @@ struct KernelCfg {
   static constexpr int SMEM = STAGE > MERGE ? STAGE : MERGE;
   static constexpr int MAX_PPS = 64;
 };
-
-constexpr int kSc1 = 16;  // cache-policy bit: coherent across XCDs (write-through / miss)
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, u32 bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
-}
-
-// Wait until at most `ahead` (0..MAXA) chunks of N load ops each are pending.
-template <int N, int MAXA>
-__device__ __forceinline__ void wait_ahead(int ahead) {
-  if constexpr (MAXA >= 4) {
-    if (ahead >= 4) { wait_vmcnt<4 * N>(); return; }
-  }
-  if constexpr (MAXA >= 3) {
-    if (ahead >= 3) { wait_vmcnt<3 * N>(); return; }
-  }
-  if constexpr (MAXA >= 2) {
-    if (ahead >= 2) { wait_vmcnt<2 * N>(); return; }
-  }
-  if (ahead >= 1) wait_vmcnt<N>();
-  else wait_vmcnt<0>();
-}
 
 // Decode one quantized ring slot (see KernelCfg) into bf16 K and V tiles at
 // stg, in the swizzled layout of a bf16 slot: value = bf16(code * scale), the
@@ -1676,11 +1477,13 @@ long attn_slots(const AttnPlan& pl) {
 }
 
 constexpr int kMaxPps = 64;  // the kernel stages at most 64 table entries per split
+constexpr int kUnitsPerWg = 4;  // persistent kernel: work units per workgroup the plan aims for
 
 }  // namespace
 
-AttnPlan attn_plan(int B, int Hkv, int W, int max_q_len, int group, long total_pages, int pages_per_split) {
-  AttnPlan pl;
+AttnPlan attn_plan(int B, int Hkv, int W, int max_q_len, int group, int D, long total_pages, int pages_per_split,
+                   bool allow_persist) {
+  AttnPlan pl{};
   pl.rows = max_q_len * group;
   // VALU dot products for up to 4 rows (decode with a group of 4); from 5
   // rows the matrix cores: measured on 8 x 8192 tokens, 8 rows 70.0 -> 56.1
@@ -1695,15 +1498,21 @@ AttnPlan attn_plan(int B, int Hkv, int W, int max_q_len, int group, long total_p
     pl.max_splits = 1;
     return pl;
   }
+  pl.persist = PKV_PERSIST && allow_persist && persist_layout(B, W, pl.rows, D, &pl.layout, &pl.nb);
+  const long pages = total_pages > 0 ? total_pages : (long)B * W;
   long pps;
   if (pages_per_split > 0) {
     pps = pages_per_split;  // the caller's plan (attn_best_pps on its lengths)
+  } else if (pl.persist) {
+    // Work units of the persistent kernel: about kUnitsPerWg units per
+    // workgroup, so the ticket queue can even out the compute units' rates;
+    // each unit leaves a partial of (D + 2) floats per row to merge.
+    pps = (pages * Hkv + (long)kNumCu * kUnitsPerWg - 1) / ((long)kNumCu * kUnitsPerWg);
   } else {
     // As few splits as keep one round of workgroups on every CU. Each extra
     // split costs a partial write and read plus a merge; an idle CU costs
     // more. The pages the batch references (the caller's count, else the
     // table width for every row) spread over the CUs.
-    const long pages = total_pages > 0 ? total_pages : (long)B * W;
     const long slots = attn_slots(pl);
     pps = (pages * Hkv + slots - 1) / slots;
   }
@@ -1717,8 +1526,17 @@ AttnPlan attn_plan(int B, int Hkv, int W, int max_q_len, int group, long total_p
 }
 
 int attn_best_pps(int B, int Hkv, int W, int max_q_len, int group, int D, const int32_t* seq_lens) {
-  AttnPlan pl = attn_plan(B, Hkv, W, max_q_len, group, 0, 0);
+  AttnPlan pl = attn_plan(B, Hkv, W, max_q_len, group, D, 0, 0);
   if (pl.prefill) return 0;
+  if (pl.persist) {  // the persistent kernel's unit length for the pages the batch holds
+    long pages = 0;
+    for (int b = 0; b < B; ++b) {
+      long n = seq_lens[b] > 0 ? seq_lens[b] : 0;
+      if (n > (long)W * kPage) n = (long)W * kPage;
+      pages += (n + kPage - 1) / kPage;
+    }
+    return attn_plan(B, Hkv, W, max_q_len, group, D, pages > 0 ? pages : 1, 0).pps;
+  }
   const long slots = attn_slots(pl);
   // A workgroup's fixed cost (table and q loads before its first page
   // arrives, the partial stores and merge after its last), in page-stream
@@ -1753,8 +1571,8 @@ int attn_best_pps(int B, int Hkv, int W, int max_q_len, int group, int D, const 
 static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 AttnWorkspace attn_workspace(int B, int Hkv, int W, int max_q_len, int group, int D, long total_pages,
-                             int pages_per_split) {
-  const AttnPlan pl = attn_plan(B, Hkv, W, max_q_len, group, total_pages, pages_per_split);
+                             int pages_per_split, bool allow_persist) {
+  const AttnPlan pl = attn_plan(B, Hkv, W, max_q_len, group, D, total_pages, pages_per_split, allow_persist);
   AttnWorkspace ws;
   const size_t items = pl.prefill ? 0 : (size_t)B * Hkv * pl.max_splits;
   ws.err_off = 0;
@@ -1805,6 +1623,7 @@ hipError_t launch_shared_merge(const AttnParams& p, const SharedParams& sp, hipS
 
 hipError_t launch_attn(const AttnParams& p, const AttnPlan& plan, hipStream_t stream) {
   if (p.num_items == 0) return hipSuccess;
+  if (plan.persist) return launch_attn_persist(p, plan, stream);
   if (plan.prefill) {
     if (p.D == 64)
       hipLaunchKernelGGL((attn_prefill_kernel<64, PKV_PREFILL_NBUF, kLongNrb<64>>), dim3(p.num_items),
