@@ -8,13 +8,22 @@
 // dropped; the window grows by 2 after a full match and shrinks by 1
 // otherwise.
 //
-// Two kernels. argmax_kernel scans row chunks (an HBM-bound fp32 stream; one
-// row alone is far too small to fill the chip) and folds each chunk's
-// (value, index) into its row's 64-bit key with one atomic max, issued and
-// never waited on. accept_rule_kernel, one workgroup launched behind it on
-// the same stream, reads the row keys, applies the accept rule and the
-// window update, and clears the keys for the next call. The kernel boundary
-// is the only synchronisation between the two.
+// One kernel. Its workgroups scan row chunks (an HBM-bound fp32 stream; one
+// row alone is far too small to fill the chip) and store each chunk's best
+// (value, index) as a 64-bit key. Each then counts itself finished; the
+// workgroup that counts last takes the largest chunk key of every row,
+// applies the accept rule and the window update, and clears the keys and
+// counters for the next call.
+//
+// Ordering. Chunk keys and counters are only touched by agent-scope atomic
+// read-modify-writes (exchanges, adds, and maxima with 0 to read a key that
+// is read twice), and the hardware performs the atomics on one address at one place for
+// every XCD, one after another. A workgroup counts only once its key
+// exchange has returned (so has been performed), and the last workgroup
+// reads the keys only once its own count has returned; so every key read
+// comes after every key write. This is the release / acquire order of the
+// language's model without its L2-wide write-back and invalidate, which only
+// non-atomic data would need.
 //
 // argmax order: larger value first; NaN above every number; lower index on
 // equal values (and between NaNs); -0 equals +0. The key encodes exactly this
@@ -41,7 +50,7 @@ constexpr int kArgUnroll = 8;                 // float4 loads in flight per thre
 #define PKV_ARG_TARGET_WGS 768
 #endif
 constexpr int kArgTargetWgs = PKV_ARG_TARGET_WGS;  // about three workgroups per CU
-constexpr int kRuleThreads = 1024;
+constexpr int kCountStride = 32;  // u32 words between row counters: one 128-byte line each
 
 // (a, ia) ranks before (b, ib): the larger value, a NaN above every number,
 // the lower index on equal values (and between NaNs). Branch-free.
@@ -93,17 +102,162 @@ __device__ __forceinline__ u64 argmax_key(float v, int i) {
 
 __device__ __forceinline__ int key_index(u64 k) { return (int)(0xFFFFFFFFu - (u32)(k & 0xFFFFFFFFull)); }
 
+// Workgroup barrier for LDS traffic only. __syncthreads also waits for the
+// wave's global stores to be acknowledged, a memory round trip that nothing
+// here needs: every global access of these kernels that another wave reads
+// is an atomic.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_scan(int x) {
+  const int lane = threadIdx.x & 63;
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __builtin_amdgcn_ds_bpermute(((lane - d) & 63) << 2, x);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+
+// Chunk key of (row, chunk), read by the last workgroup.
+__device__ __forceinline__ u64 read_slot(const AcceptParams& p, int r, int c) {
+  // a max with 0 leaves the key as it is
+  return __hip_atomic_fetch_max(p.slots + (size_t)r * p.chunks + c, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The row's key: the largest of its chunk keys.
+__device__ __forceinline__ u64 row_key(const AcceptParams& p, int r) {
+  u64 k = 0;
+  for (int c = 0; c < p.chunks; ++c) {
+    const u64 x = read_slot(p, r, c);
+    k = x > k ? x : k;
+  }
+  return k;
+}
+
+// Sequence b's accept decision from its rows' keys and its drafts (both
+// indexed from the sequence's first row r0 / first draft d0 through `key_at`
+// and `draft_at`), written to the outputs; out_accept = 0, out_next = -1 for
+// a sequence whose rows or drafts break the contract.
+template <class KeyAt, class DraftAt>
+__device__ __forceinline__ void decide(const AcceptParams& p, int b, int n, int w_old, int r0, int d0, KeyAt key_at,
+                                       DraftAt draft_at) {
+  const bool ok = n >= 0 && n <= p.max_draft && r0 >= 0 && r0 + n + 1 <= p.total_rows && d0 >= 0 &&
+                  d0 + n <= p.total_rows - p.B;
+  if (!ok) {
+    p.out_accept[b] = 0;
+    p.out_next[b] = -1;
+    return;
+  }
+  // clamped, unconditional reads: all in flight together
+  u64 key[PKV_MAX_Q_LEN];
+  int draft[PKV_MAX_Q_LEN - 1];
+#pragma unroll
+  for (int i = 0; i < PKV_MAX_Q_LEN; ++i) key[i] = key_at(r0 + min(i, n));
+#pragma unroll
+  for (int i = 0; i < PKV_MAX_Q_LEN - 1; ++i) draft[i] = n <= 0 ? -1 : draft_at(d0 + min(i, n - 1));
+  // drafts compared from the left; the first mismatch keeps the base token
+  int m = n;
+#pragma unroll
+  for (int i = PKV_MAX_Q_LEN - 2; i >= 0; --i)
+    if (i < n && key_index(key[i]) != draft[i]) m = i;
+  int next = 0;
+#pragma unroll
+  for (int i = 0; i < PKV_MAX_Q_LEN; ++i)
+    if (i == m) next = key_index(key[i]);
+  p.out_accept[b] = m + 1;
+  p.out_next[b] = next;
+  if (p.window) p.window[b] = (m == n) ? w_old + 2 : max(1, w_old - 1);
+}
+
+// The accept rule, run by the workgroup that finished last, for up to
+// kArgThreads logits rows (so at most as many sequences): thread b takes
+// sequence b. Every input and every chunk key is requested at once; the
+// chunk keys are taken and cleared by atomic exchanges and reduced per row
+// in LDS; a block-wide prefix sum of n_draft + 1 gives each sequence its
+// first row.
+__device__ void accept_rule_small(const AcceptParams& p) {
+  constexpr int kWaves = kArgThreads / 64;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  __shared__ int s_wsum[kWaves];
+  __shared__ u64 s_keys[kArgThreads];
+  __shared__ int s_draft[kArgThreads];
+  const int n = t < p.B ? p.n_draft[t] : 0;
+  const int w_old = (t < p.B && p.window) ? p.window[t] : 0;
+  const int d = t < p.total_rows - p.B ? p.draft_ids[t] : 0;
+  const int ns = p.total_rows * p.chunks;
+  u64 x[4];
+  for (int e0 = 0; e0 < ns; e0 += 4 * kArgThreads) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = e0 + u * kArgThreads + t;
+      x[u] = e < ns ? __hip_atomic_exchange(p.slots + e, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
+    }
+    if (e0 == 0) {
+      s_keys[t] = 0;
+      lds_barrier();
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = e0 + u * kArgThreads + t;
+      if (e < ns) atomicMax(&s_keys[e / p.chunks], x[u]);
+    }
+  }
+  s_draft[t] = d;
+  const int inc = wave_scan(t < p.B ? n + 1 : 0);
+  if (lane == 63) s_wsum[wave] = inc;
+  lds_barrier();
+  if (t >= p.B) return;
+  int before = 0;
+  for (int w = 0; w < wave; ++w) before += s_wsum[w];
+  const int r0 = before + inc - (n + 1);  // first row of sequence t
+  decide(p, t, n, w_old, r0, r0 - t, [&](int r) { return s_keys[r]; }, [&](int i) { return s_draft[i]; });
+}
+
+// The same rule for any number of rows: thread b of each tile of
+// kArgThreads sequences; row keys are read from their chunk keys (atomic
+// maxima with 0, which leave them as they are) and cleared at the end.
+__device__ void accept_rule_tiled(const AcceptParams& p) {
+  constexpr int kWaves = kArgThreads / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ int s_wsum[kWaves];
+  __shared__ int s_carry;
+  if (threadIdx.x == 0) s_carry = 0;
+  lds_barrier();
+  for (int t0 = 0; t0 < p.B; t0 += kArgThreads) {
+    const int b = t0 + threadIdx.x;
+    const int n = b < p.B ? p.n_draft[b] : 0;
+    const int w_old = (b < p.B && p.window) ? p.window[b] : 0;
+    const int inc = wave_scan(b < p.B ? n + 1 : 0);
+    if (lane == 63) s_wsum[wave] = inc;
+    lds_barrier();
+    int before = s_carry;
+    for (int w = 0; w < wave; ++w) before += s_wsum[w];
+    const int r0 = before + inc - (n + 1);  // first row of sequence b
+    if (b < p.B)
+      decide(p, b, n, w_old, r0, r0 - b, [&](int r) { return row_key(p, r); },
+             [&](int i) { return p.draft_ids[i]; });
+    lds_barrier();
+    if (threadIdx.x == kArgThreads - 1) s_carry = before + inc;
+    lds_barrier();
+  }
+  // every chunk key has been read (before the last barrier): clear them
+  for (int e = threadIdx.x; e < p.total_rows * p.chunks; e += kArgThreads)
+    __hip_atomic_exchange(p.slots + e, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Workgroup (c, r): chunk c of logits row r. Every load of a thread is issued
-// before any is consumed; the chunk's best pair goes into the row key.
+// before any is consumed; the chunk's best pair is stored as its chunk key,
+// and the workgroup that finishes last applies the accept rule.
 template <bool VEC4>
-__global__ __launch_bounds__(kArgThreads) void argmax_kernel(
+__global__ __launch_bounds__(kArgThreads) void accept_kernel(
     // leading scalars, preloaded into SGPRs at wave launch
-    const float* __restrict__ logits, int V, int chunk_len, u64* __restrict__ keys) {
+    const float* __restrict__ logits, int V, int chunk_len, AcceptParams p) {
   const int c = blockIdx.x;
   const int r = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   __shared__ float sv[kArgThreads / 64];
   __shared__ int si[kArgThreads / 64];
+  __shared__ int s_last;
 
   const int begin = c * chunk_len;
   const int end = min(V, begin + chunk_len);
@@ -136,92 +290,38 @@ __global__ __launch_bounds__(kArgThreads) void argmax_kernel(
     sv[wave] = bv;
     si[wave] = bi;
   }
-  __syncthreads();
-  if (wave != 0) return;
-  float v = lane < kArgThreads / 64 ? sv[lane] : -__builtin_inff();
-  int i = lane < kArgThreads / 64 ? si[lane] : INT_MAX;
-  wave_best(v, i);
-  if (lane == 0 && i != INT_MAX)
-    __hip_atomic_fetch_max(keys + r, argmax_key(v, i), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Inclusive prefix sum over the 64 lanes of a wave.
-__device__ __forceinline__ int wave_scan(int x) {
-  const int lane = threadIdx.x & 63;
-  for (int d = 1; d < 64; d <<= 1) {
-    const int y = __builtin_amdgcn_ds_bpermute(((lane - d) & 63) << 2, x);
-    if (lane >= d) x += y;
-  }
-  return x;
-}
-
-// One workgroup: thread b (in tiles of kRuleThreads sequences) finds its
-// sequence's first logits row by a block-wide prefix sum of n_draft + 1,
-// reads its rows' keys and drafts (all requested together), applies the
-// accept rule and the window update. Then every row key is cleared.
-__global__ __launch_bounds__(kRuleThreads) void accept_rule_kernel(AcceptParams p) {
-  constexpr int kWaves = kRuleThreads / 64;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  __shared__ int s_wsum[kWaves];
-  __shared__ int s_carry;
-  __shared__ u64 s_keys[kRuleThreads];
-  __shared__ int s_draft[kRuleThreads];
-  // Up to kRuleThreads rows, every key and draft is fetched up front, in the
-  // same memory round trip as n_draft, and read from LDS below.
-  const bool staged = p.total_rows <= kRuleThreads;
-  if (staged) {
-    if ((int)threadIdx.x < p.total_rows) s_keys[threadIdx.x] = p.keys[threadIdx.x];
-    if ((int)threadIdx.x < p.total_rows - p.B) s_draft[threadIdx.x] = p.draft_ids[threadIdx.x];
-  }
-  if (threadIdx.x == 0) s_carry = 0;
-  __syncthreads();
-  for (int t0 = 0; t0 < p.B; t0 += kRuleThreads) {
-    const int b = t0 + threadIdx.x;
-    const int n = b < p.B ? p.n_draft[b] : 0;
-    const int w_old = (b < p.B && p.window) ? p.window[b] : 0;
-    const int inc = wave_scan(b < p.B ? n + 1 : 0);
-    if (lane == 63) s_wsum[wave] = inc;
-    __syncthreads();
-    int before = s_carry;
-    for (int w = 0; w < wave; ++w) before += s_wsum[w];
-    const int r0 = before + inc - (n + 1);  // first row of sequence b
-    const int d0 = r0 - b;                  // first draft: the sum of n_draft before b
-    if (b < p.B) {
-      const bool ok = n >= 0 && n <= p.max_draft && r0 >= 0 && r0 + n + 1 <= p.total_rows && d0 >= 0 &&
-                      d0 + n <= p.total_rows - p.B;
-      if (!ok) {
-        p.out_accept[b] = 0;
-        p.out_next[b] = -1;
-      } else {
-        // clamped, unconditional loads: all in flight together
-        u64 key[PKV_MAX_Q_LEN];
-        int draft[PKV_MAX_Q_LEN - 1];
-#pragma unroll
-        for (int i = 0; i < PKV_MAX_Q_LEN; ++i) key[i] = staged ? s_keys[r0 + min(i, n)] : p.keys[r0 + min(i, n)];
-#pragma unroll
-        for (int i = 0; i < PKV_MAX_Q_LEN - 1; ++i)
-          draft[i] = n <= 0 ? -1 : staged ? s_draft[d0 + min(i, n - 1)] : p.draft_ids[d0 + min(i, n - 1)];
-        // drafts compared from the left; the first mismatch keeps the base token
-        int m = n;
-#pragma unroll
-        for (int i = PKV_MAX_Q_LEN - 2; i >= 0; --i)
-          if (i < n && key_index(key[i]) != draft[i]) m = i;
-        int next = 0;
-#pragma unroll
-        for (int i = 0; i < PKV_MAX_Q_LEN; ++i)
-          if (i == m) next = key_index(key[i]);
-        p.out_accept[b] = m + 1;
-        p.out_next[b] = next;
-        if (p.window) p.window[b] = (m == n) ? w_old + 2 : max(1, w_old - 1);
+  lds_barrier();
+  if (wave == 0) {
+    float v = lane < kArgThreads / 64 ? sv[lane] : -__builtin_inff();
+    int i = lane < kArgThreads / 64 ? si[lane] : INT_MAX;
+    wave_best(v, i);
+    if (lane == 0) {
+      // The chunk's key has been exchanged in (the old value returned)
+      // before the chunk is counted, and counts go in two levels (the
+      // chunks of a row, then the rows) so that few atomics meet on one
+      // address.
+      const u64 was = __hip_atomic_exchange(p.slots + (size_t)r * gridDim.x + c, i != INT_MAX ? argmax_key(v, i) : 0ull,
+                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      asm volatile("s_waitcnt vmcnt(0)" ::"v"(was) : "memory");
+      uint32_t* row_count = p.row_done + (size_t)r * kCountStride;
+      bool last = __hip_atomic_fetch_add(row_count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1;
+      if (last) {
+        // every chunk of the row has counted: reset its counter for the next call
+        __hip_atomic_exchange(row_count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last = __hip_atomic_fetch_add(p.done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gridDim.y - 1;
       }
+      s_last = last;
     }
-    __syncthreads();
-    if (threadIdx.x == kRuleThreads - 1) s_carry = before + inc;
-    __syncthreads();
   }
-  // every key has been read (its value was used before the barrier): clear
-  // all rows, owned or not, for the next call
-  for (int r = threadIdx.x; r < p.total_rows; r += kRuleThreads) p.keys[r] = 0ull;
+  lds_barrier();
+  if (!s_last) return;
+  // the row counters were reset by each row's last workgroup; the chunk keys
+  // are cleared by the rule; the row count is reset here
+  if (threadIdx.x == 0) __hip_atomic_exchange(p.done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (p.total_rows <= kArgThreads)
+    accept_rule_small(p);
+  else
+    accept_rule_tiled(p);
 }
 
 }  // namespace
@@ -242,9 +342,11 @@ AcceptWorkspace accept_workspace(int B, int total_rows, int V) {
   len = (len + 3) / 4 * 4;
   ws.chunk_len = (int)len;
   ws.chunks = (int)((V + len - 1) / len);
-  ws.keys_off = 0;
-  ws.total = ((size_t)total_rows * 8 + 255) / 256 * 256;
-  if (ws.total == 0) ws.total = 256;
+  // counters, then chunk keys; all zero between calls
+  ws.done_off = 0;
+  ws.rows_off = 256;
+  ws.slots_off = ws.rows_off + (size_t)total_rows * kCountStride * 4;
+  ws.total = ws.slots_off + ((size_t)total_rows * ws.chunks * 8 + 255) / 256 * 256;
   return ws;
 }
 
@@ -254,13 +356,9 @@ hipError_t launch_accept(const AcceptParams& p, hipStream_t stream) {
   const bool vec4 = p.V % 4 == 0 && (reinterpret_cast<uintptr_t>(p.logits) & 15) == 0 &&
                     p.chunk_len <= kArgThreads * kArgUnroll * 4;
   if (vec4)
-    hipLaunchKernelGGL(argmax_kernel<true>, grid, dim3(kArgThreads), 0, stream, p.logits, p.V, p.chunk_len, p.keys);
+    hipLaunchKernelGGL(accept_kernel<true>, grid, dim3(kArgThreads), 0, stream, p.logits, p.V, p.chunk_len, p);
   else
-    hipLaunchKernelGGL(argmax_kernel<false>, grid, dim3(kArgThreads), 0, stream, p.logits, p.V, p.chunk_len,
-                       p.keys);
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(accept_rule_kernel, dim3(1), dim3(kRuleThreads), 0, stream, p);
+    hipLaunchKernelGGL(accept_kernel<false>, grid, dim3(kArgThreads), 0, stream, p.logits, p.V, p.chunk_len, p);
   return hipGetLastError();
 }
 

@@ -381,7 +381,9 @@ int pkv_accept(const float* logits, const int32_t* draft_ids, const int32_t* n_d
   p.out_accept = out_accept;
   p.out_next = out_next;
   p.window = window;
-  p.keys = reinterpret_cast<unsigned long long*>(w + ws.keys_off);
+  p.slots = reinterpret_cast<unsigned long long*>(w + ws.slots_off);
+  p.done = reinterpret_cast<uint32_t*>(w + ws.done_off);
+  p.row_done = reinterpret_cast<uint32_t*>(w + ws.rows_off);
   p.B = s->num_seqs;
   p.V = s->vocab;
   p.total_rows = s->total_rows;
