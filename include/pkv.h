@@ -53,8 +53,10 @@ typedef enum {
   PKV_ERR_WORKSPACE = -3, /* workspace NULL or smaller than the queried size    */
   PKV_ERR_HIP = -4,       /* a HIP launch or runtime call failed                */
   PKV_ERR_SPACE = -5,     /* page allocator: not enough pages (nothing changed) */
-  PKV_ERR_STATE = -6      /* page allocator: a page is not in the state the call
+  PKV_ERR_STATE = -6,     /* page allocator: a page is not in the state the call
                              needs, e.g. released more often than referenced    */
+  PKV_ERR_SCRATCH = -7    /* allocation-free call: the shape needs more than its
+                             fixed device scratch                               */
 } pkv_status;
 
 /* Error-word bits a kernel sets when a device array breaks its contract. */
@@ -295,6 +297,27 @@ int pkv_accept(const float* logits, const int32_t* draft_ids, const int32_t* n_d
                int32_t* out_accept, int32_t* out_next, int32_t* window,
                const pkv_accept_shape* shape, void* workspace, size_t workspace_bytes,
                void* stream);
+
+/*
+ * pkv_accept without a workspace argument and without any device allocation,
+ * for callers that cannot allocate: code under stream (graph) capture, tight
+ * serving loops, harnesses that forbid hipMalloc. Same arguments (less the
+ * workspace), results, contract and errors as pkv_accept.
+ *
+ * The workspace is a fixed array of PKV_ACCEPT_SCRATCH_BYTES in each GPU's
+ * device memory, held until the process ends. The first call on a device
+ * looks up that device's copy and enqueues a zero fill of it (a kernel) on
+ * `stream`; every call leaves it zero again. A shape whose workspace
+ * (pkv_accept_workspace_bytes) exceeds PKV_ACCEPT_SCRATCH_BYTES returns
+ * PKV_ERR_SCRATCH before anything is launched.
+ * All calls on one GPU share its copy: calls that may overlap in time on one
+ * GPU (other streams, other threads) race and give wrong results; order them
+ * on one stream.
+ */
+#define PKV_ACCEPT_SCRATCH_BYTES (1u << 20)
+int pkv_accept_noalloc(const float* logits, const int32_t* draft_ids, const int32_t* n_draft,
+                       int32_t* out_accept, int32_t* out_next, int32_t* window,
+                       const pkv_accept_shape* shape, void* stream);
 
 /* The draft-window rule on the host: window + 2 when accepted == n_draft + 1
  * (every draft matched, including n_draft == 0), else max(1, window - 1). */

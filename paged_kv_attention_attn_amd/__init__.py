@@ -21,4 +21,5 @@ from ._lib import (  # noqa: F401
     pkv_attn_shared_workspace_bytes, new_attn_shared_workspace, pkv_attn_fwd_shared, pkv_attn_plan,
     pkv_shared_prefix_pages, pkv_q8_encode, pkv_attn_fwd_q8, pkv_q4_encode, pkv_attn_fwd_q4,
     pkv_kv_append_q8, pkv_kv_append_q4, pkv_pool_copy_page_bytes,
+    PKV_ERR_SCRATCH, PKV_ACCEPT_SCRATCH_BYTES, pkv_accept_noalloc,
 )

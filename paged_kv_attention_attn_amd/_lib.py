@@ -20,11 +20,12 @@ PKV_PAGE_SIZE = 256
 PKV_MAX_Q_LEN = 16
 PKV_MAX_ROWS = 64
 PKV_OK, PKV_ERR_NULL, PKV_ERR_SHAPE, PKV_ERR_WORKSPACE, PKV_ERR_HIP = 0, -1, -2, -3, -4
-PKV_ERR_SPACE, PKV_ERR_STATE = -5, -6
+PKV_ERR_SPACE, PKV_ERR_STATE, PKV_ERR_SCRATCH = -5, -6, -7
+PKV_ACCEPT_SCRATCH_BYTES = 1 << 20
 PKV_EFLAG_PAGE, PKV_EFLAG_QLEN, PKV_EFLAG_ROWS, PKV_EFLAG_SPACE = 1, 2, 4, 8
 
 EXPORTS = ("pkv_attn_workspace_bytes", "pkv_attn_workspace_init", "pkv_attn_fwd",
-           "pkv_attn_check_errors", "pkv_accept_workspace_bytes", "pkv_accept",
+           "pkv_attn_check_errors", "pkv_accept_workspace_bytes", "pkv_accept", "pkv_accept_noalloc",
            "pkv_window_next", "pkv_status_string", "pkv_version", "pkv_kv_workspace_bytes",
            "pkv_kv_append", "pkv_kv_rollback", "pkv_kv_check_errors", "pkv_pool_create",
            "pkv_pool_destroy", "pkv_pool_stats", "pkv_pool_admit", "pkv_pool_alloc", "pkv_pool_retain",
@@ -98,6 +99,8 @@ def _load():
     lib.pkv_accept_workspace_bytes.restype = sz
     lib.pkv_accept.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.POINTER(pkv_accept_shape), vp, sz, vp]
     lib.pkv_accept.restype = ctypes.c_int
+    lib.pkv_accept_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.POINTER(pkv_accept_shape), vp]
+    lib.pkv_accept_noalloc.restype = ctypes.c_int
     lib.pkv_window_next.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
     lib.pkv_window_next.restype = ctypes.c_int32
     lib.pkv_status_string.argtypes = [ctypes.c_int]
@@ -357,27 +360,39 @@ def new_accept_workspace(shape, device="cuda"):
     return torch.zeros(n, dtype=torch.uint8, device=device)
 
 
-def pkv_accept(logits, draft_ids, n_draft, out_accept, out_next, window, shape, workspace, stream=None):
-    """logits fp32; draft_ids, n_draft, out_accept, out_next, window (or None): int32."""
+def _accept_args(what, logits, draft_ids, n_draft, out_accept, out_next, window, shape):
     B = shape.num_seqs
-    _extents("pkv_accept", (logits, shape.total_rows * shape.vocab, "logits"), (n_draft, B, "n_draft"),
+    _extents(what, (logits, shape.total_rows * shape.vocab, "logits"), (n_draft, B, "n_draft"),
              (out_accept, B, "out_accept"), (out_next, B, "out_next"), (window, B, "window"))
     if draft_ids is not None and draft_ids.numel() and draft_ids.numel() < shape.total_rows - B:
-        raise ValueError(f"pkv_accept: draft_ids has {draft_ids.numel()} elements, fewer than the "
+        raise ValueError(f"{what}: draft_ids has {draft_ids.numel()} elements, fewer than the "
                          f"{shape.total_rows - B} drafts the rows imply")
     for t, dt, n in ((logits, torch.float32, "logits"), (n_draft, torch.int32, "n_draft"),
-                     (out_accept, torch.int32, "out_accept"), (out_next, torch.int32, "out_next"),
-                     (workspace, torch.uint8, "workspace")):
+                     (out_accept, torch.int32, "out_accept"), (out_next, torch.int32, "out_next")):
         _need(t, dt, n)
     if draft_ids is not None and draft_ids.numel():
         _need(draft_ids, torch.int32, "draft_ids")
     if window is not None:
         _need(window, torch.int32, "window")
-    drafts = draft_ids if (draft_ids is not None and draft_ids.numel()) else None
+    return draft_ids if (draft_ids is not None and draft_ids.numel()) else None
+
+
+def pkv_accept(logits, draft_ids, n_draft, out_accept, out_next, window, shape, workspace, stream=None):
+    """logits fp32; draft_ids, n_draft, out_accept, out_next, window (or None): int32."""
+    drafts = _accept_args("pkv_accept", logits, draft_ids, n_draft, out_accept, out_next, window, shape)
+    _need(workspace, torch.uint8, "workspace")
     rc = LIB.pkv_accept(_ptr(logits), _ptr(drafts), _ptr(n_draft), _ptr(out_accept), _ptr(out_next),
                         _ptr(window), ctypes.byref(shape), _ptr(workspace), workspace.numel(),
                         _stream(stream))
     _check(rc, "pkv_accept")
+
+
+def pkv_accept_noalloc(logits, draft_ids, n_draft, out_accept, out_next, window, shape, stream=None):
+    """pkv_accept on the library's fixed per-GPU scratch (no workspace, no allocation)."""
+    drafts = _accept_args("pkv_accept_noalloc", logits, draft_ids, n_draft, out_accept, out_next, window, shape)
+    rc = LIB.pkv_accept_noalloc(_ptr(logits), _ptr(drafts), _ptr(n_draft), _ptr(out_accept), _ptr(out_next),
+                                _ptr(window), ctypes.byref(shape), _stream(stream))
+    _check(rc, "pkv_accept_noalloc")
 
 
 def pkv_window_next(window, n_draft, accepted):

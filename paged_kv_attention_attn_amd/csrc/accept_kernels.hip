@@ -32,6 +32,7 @@
 #include "internal.h"
 
 #include <climits>
+#include <mutex>
 
 #include "pkv.h"
 
@@ -324,7 +325,48 @@ __global__ __launch_bounds__(kArgThreads) void accept_kernel(
     accept_rule_tiled(p);
 }
 
+// Fills n 32-bit words with zero (a kernel, not a memset, so that a caller
+// capturing the stream into a graph records nothing but kernels).
+__global__ __launch_bounds__(256) void zero_words(u32* __restrict__ w, u32 n) {
+  for (u32 i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) w[i] = 0u;
+}
+
 }  // namespace
+
+// Workspace of the allocation-free accept entry point: one copy per GPU in
+// the code object's device memory, alive until the process ends. Host code
+// never passes this name to a kernel (on the host it is only a stand-in);
+// it uses the device address that accept_scratch looks up for the current
+// device.
+static __device__ __align__(256) unsigned char scratch[kAcceptScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];
+}  // namespace
+
+hipError_t accept_scratch(hipStream_t stream, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    // the accept protocol needs the workspace zero before a call (and
+    // leaves it zero); clear this device's copy once, on the caller's stream
+    hipLaunchKernelGGL(zero_words, dim3(64), dim3(256), 0, stream, static_cast<u32*>(ptr),
+                       (u32)(kAcceptScratchBytes / 4));
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
+  return hipSuccess;
+}
 
 AcceptWorkspace accept_workspace(int B, int total_rows, int V) {
   (void)B;

@@ -363,16 +363,26 @@ size_t pkv_accept_workspace_bytes(const pkv_accept_shape* s) {
   return pkv::accept_workspace(s->num_seqs, s->total_rows, s->vocab).total;
 }
 
-int pkv_accept(const float* logits, const int32_t* draft_ids, const int32_t* n_draft, int32_t* out_accept,
-               int32_t* out_next, int32_t* window, const pkv_accept_shape* s, void* workspace,
-               size_t workspace_bytes, void* stream) {
+// Checks shared by both accept entry points; PKV_OK when the call may go on
+// (*skip set when there is nothing to do).
+static int accept_args_ok(const float* logits, const int32_t* draft_ids, const int32_t* n_draft,
+                          const int32_t* out_accept, const int32_t* out_next, const pkv_accept_shape* s,
+                          bool* skip) {
+  *skip = false;
   if (!s) return PKV_ERR_NULL;
   if (!accept_shape_ok(s)) return PKV_ERR_SHAPE;
-  if (s->num_seqs == 0) return PKV_OK;
+  if (s->num_seqs == 0) {
+    *skip = true;
+    return PKV_OK;
+  }
   if (!logits || !n_draft || !out_accept || !out_next) return PKV_ERR_NULL;
   if (!draft_ids && s->total_rows > s->num_seqs) return PKV_ERR_NULL;
-  const pkv::AcceptWorkspace ws = pkv::accept_workspace(s->num_seqs, s->total_rows, s->vocab);
-  if (!workspace || workspace_bytes < ws.total) return PKV_ERR_WORKSPACE;
+  return PKV_OK;
+}
+
+static int accept_launch(const float* logits, const int32_t* draft_ids, const int32_t* n_draft, int32_t* out_accept,
+                         int32_t* out_next, int32_t* window, const pkv_accept_shape* s,
+                         const pkv::AcceptWorkspace& ws, void* workspace, void* stream) {
   char* w = static_cast<char*>(workspace);
   pkv::AcceptParams p;
   p.logits = logits;
@@ -392,6 +402,29 @@ int pkv_accept(const float* logits, const int32_t* draft_ids, const int32_t* n_d
   p.chunk_len = ws.chunk_len;
   if (pkv::launch_accept(p, static_cast<hipStream_t>(stream)) != hipSuccess) return PKV_ERR_HIP;
   return PKV_OK;
+}
+
+int pkv_accept(const float* logits, const int32_t* draft_ids, const int32_t* n_draft, int32_t* out_accept,
+               int32_t* out_next, int32_t* window, const pkv_accept_shape* s, void* workspace,
+               size_t workspace_bytes, void* stream) {
+  bool skip;
+  const int rc = accept_args_ok(logits, draft_ids, n_draft, out_accept, out_next, s, &skip);
+  if (rc != PKV_OK || skip) return rc;
+  const pkv::AcceptWorkspace ws = pkv::accept_workspace(s->num_seqs, s->total_rows, s->vocab);
+  if (!workspace || workspace_bytes < ws.total) return PKV_ERR_WORKSPACE;
+  return accept_launch(logits, draft_ids, n_draft, out_accept, out_next, window, s, ws, workspace, stream);
+}
+
+int pkv_accept_noalloc(const float* logits, const int32_t* draft_ids, const int32_t* n_draft, int32_t* out_accept,
+                       int32_t* out_next, int32_t* window, const pkv_accept_shape* s, void* stream) {
+  bool skip;
+  const int rc = accept_args_ok(logits, draft_ids, n_draft, out_accept, out_next, s, &skip);
+  if (rc != PKV_OK || skip) return rc;
+  const pkv::AcceptWorkspace ws = pkv::accept_workspace(s->num_seqs, s->total_rows, s->vocab);
+  if (ws.total > pkv::kAcceptScratchBytes) return PKV_ERR_SCRATCH;
+  void* scratch = nullptr;
+  if (pkv::accept_scratch(static_cast<hipStream_t>(stream), &scratch) != hipSuccess) return PKV_ERR_HIP;
+  return accept_launch(logits, draft_ids, n_draft, out_accept, out_next, window, s, ws, scratch, stream);
 }
 
 size_t pkv_kv_workspace_bytes(const pkv_kv_shape* s) {
@@ -558,6 +591,7 @@ const char* pkv_status_string(int status) {
     case PKV_ERR_HIP: return "HIP launch or runtime call failed";
     case PKV_ERR_SPACE: return "not enough pages";
     case PKV_ERR_STATE: return "a page is not in the state the call needs";
+    case PKV_ERR_SCRATCH: return "shape needs more than the fixed scratch of the allocation-free call";
     default: return "unknown status";
   }
 }

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "pkv.h"
+
 namespace pkv {
 
 constexpr int kPage = 256;
@@ -157,5 +159,11 @@ hipError_t launch_table_remap(int32_t* table, int32_t n, const int32_t* remap, i
 
 AcceptWorkspace accept_workspace(int B, int total_rows, int V);
 hipError_t launch_accept(const AcceptParams& p, hipStream_t stream);
+// Allocation-free accept: the workspace is a fixed device array of
+// kAcceptScratchBytes per GPU. accept_scratch returns its address on the
+// current device (looked up, and zero-filled on `stream`, at the first call
+// per device).
+constexpr size_t kAcceptScratchBytes = PKV_ACCEPT_SCRATCH_BYTES;
+hipError_t accept_scratch(hipStream_t stream, void** out);
 
 }  // namespace pkv

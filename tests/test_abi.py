@@ -360,3 +360,14 @@ def test_byte_page_moves_check_sizes_and_pointers(pk):
     assert f(d, d, d, d, 1, 1 << 20, 1 << 21, None, None) == pk.PKV_ERR_SHAPE   # 2^41 bytes of pool
     assert f(d, None, d, d, 1, 16, 4096, None, None) == pk.PKV_ERR_NULL
     assert f(None, None, None, None, 0, 16, 4096, None, None) == pk.PKV_OK
+
+
+def test_accept_noalloc_refuses_shapes_past_its_scratch_before_any_launch(pk):
+    # host-side check only: the pointers are never dereferenced
+    shape = pk.pkv_accept_shape(4000, 1 << 20, 4000, 0)
+    assert pk.pkv_accept_workspace_bytes(shape) > pk.PKV_ACCEPT_SCRATCH_BYTES
+    fake = ctypes.c_void_p(256)
+    rc = pk.LIB.pkv_accept_noalloc(fake, fake, fake, fake, fake, None, ctypes.byref(shape), None)
+    assert rc == pk.PKV_ERR_SCRATCH
+    assert "scratch" in pk.pkv_status_string(rc)
+    assert pk.LIB.pkv_accept_noalloc(fake, fake, fake, fake, fake, None, None, None) == pk.PKV_ERR_NULL
