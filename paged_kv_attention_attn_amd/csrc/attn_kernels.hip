@@ -765,8 +765,15 @@ __global__ __launch_bounds__(WAVES * 64) void attn_split_kernel(
     tbl = block_table[(size_t)b * W + po + page0 + threadIdx.x];
   const int seq_len = seq_lens[b] - po * kPage;
   const int q_len = q_lens[b];
-  const int q_start = __builtin_amdgcn_readfirstlane(wave_prefix(q_lens, b));
-  if (q_len <= 0) return;
+  const RowPrefix rp = row_prefix(q_lens, b, B);
+  const int q_start = rp.start;
+  // the batch's row count against total_q, once per launch (item 0 always exists)
+  if (blockIdx.x == 0 && threadIdx.x == 0 && rp.total != p.total_q) atomicOr(p.err, PKV_EFLAG_ROWS_BIT);
+  if (q_len < 0) {
+    if (s == 0 && g == 0 && threadIdx.x == 0) atomicOr(p.err, PKV_EFLAG_QLEN_BIT);
+    return;
+  }
+  if (q_len == 0 || rp.bad_before) return;
   const int n_pages = (seq_len + kPage - 1) / kPage;
   const int n_splits = (n_pages + pps - 1) / pps;
   if (q_len > p.max_q_len || q_len > seq_len || n_pages > W - po) {
@@ -1232,8 +1239,15 @@ __global__ __launch_bounds__(kLongWaves<NRB> * 64) void attn_prefill_kernel(
 
   const int seq_len = seq_lens[b];
   const int q_len = q_lens[b];
-  const int q_start = __builtin_amdgcn_readfirstlane(wave_prefix(q_lens, b));
-  if (q_len <= 0) return;
+  const RowPrefix rp = row_prefix(q_lens, b, B);
+  const int q_start = rp.start;
+  // the batch's row count against total_q, once per launch
+  if (blockIdx.x == 0 && threadIdx.x == 0 && rp.total != p.total_q) atomicOr(p.err, PKV_EFLAG_ROWS_BIT);
+  if (q_len < 0) {
+    if (qr == 0 && g == 0 && threadIdx.x == 0) atomicOr(p.err, PKV_EFLAG_QLEN_BIT);
+    return;
+  }
+  if (q_len == 0 || rp.bad_before) return;
   const int n_tiles = (q_len + qtok - 1) / qtok;
   if (qr >= n_tiles) return;
   const int n_pages = (seq_len + kPage - 1) / kPage;

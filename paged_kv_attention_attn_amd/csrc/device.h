@@ -170,13 +170,32 @@ __device__ __forceinline__ u32 lds_addr_of(const void* p) {
   return static_cast<u32>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)(p)));
 }
 
-// Sum of q_lens[0..b) by one wave.
-__device__ __forceinline__ int wave_prefix(const int32_t* q_lens, int b) {
+// Window-row bookkeeping of sequence b, by one wave over q_lens[0..B): the
+// first row of b (the sum of q_lens[0..b)), the sum over the whole batch,
+// and whether a length before b is negative (then b's first row means
+// nothing and b is skipped; that sequence's own item flags it).
+struct RowPrefix {
+  int start, total;
+  bool bad_before;
+};
+__device__ __forceinline__ RowPrefix row_prefix(const int32_t* q_lens, int b, int B) {
   const int lane = threadIdx.x & 63;
-  int s = 0;
-  for (int i = lane; i < b; i += 64) s += q_lens[i];
-  for (int m = 32; m >= 1; m >>= 1) s += __builtin_amdgcn_ds_bpermute(((lane ^ m) << 2), s);
-  return s;
+  int pre = 0, tot = 0, neg = 0;
+  for (int i = lane; i < B; i += 64) {
+    const int v = q_lens[i];
+    tot += v;
+    if (i < b) {
+      pre += v;
+      neg |= v < 0;
+    }
+  }
+  for (int m = 32; m >= 1; m >>= 1) {
+    pre += __builtin_amdgcn_ds_bpermute(((lane ^ m) << 2), pre);
+    tot += __builtin_amdgcn_ds_bpermute(((lane ^ m) << 2), tot);
+    neg |= __builtin_amdgcn_ds_bpermute(((lane ^ m) << 2), neg);
+  }
+  return {(int)__builtin_amdgcn_readfirstlane(pre), (int)__builtin_amdgcn_readfirstlane(tot),
+          __builtin_amdgcn_readfirstlane(neg) != 0};
 }
 
 constexpr int kSc1 = 16;  // cache-policy bit: coherent across XCDs (write-through / miss)

@@ -16,9 +16,12 @@
 //
 // One wave per vector: each lane holds D / 64 values (Q4: a pair of adjacent
 // values, one output byte), the largest magnitude and the all-finite test are
-// wave reductions.
+// wave reductions. The grid is capped at kEncMaxBlocks workgroups, each
+// striding over the rows, so any row count the ABI accepts fits one launch.
 
 #include "internal.h"
+
+#include <algorithm>
 
 #include "pkv.h"
 #include "quant_encode.h"
@@ -28,23 +31,22 @@ namespace {
 
 constexpr int kEncThreads = 256;
 constexpr int kEncWaves = kEncThreads / 64;
+constexpr long kEncMaxBlocks = 1L << 16;  // 64 Ki workgroups: 256 per CU, far past what fills the chip
 
 template <int D>
 __global__ __launch_bounds__(kEncThreads) void q8_encode_kernel(const uint16_t* __restrict__ src,
                                                                 int8_t* __restrict__ codes,
                                                                 float* __restrict__ scales, long rows) {
-  const long row = (long)blockIdx.x * kEncWaves + (threadIdx.x >> 6);
-  if (row >= rows) return;
-  q8_encode_wave<D>(src + row * D, codes + row * D, scales + row);
+  for (long row = (long)blockIdx.x * kEncWaves + (threadIdx.x >> 6); row < rows; row += (long)gridDim.x * kEncWaves)
+    q8_encode_wave<D>(src + row * D, codes + row * D, scales + row);
 }
 
 template <int D>
 __global__ __launch_bounds__(kEncThreads) void q4_encode_kernel(const uint16_t* __restrict__ src,
                                                                 uint8_t* __restrict__ codes,
                                                                 float* __restrict__ scales, long rows) {
-  const long row = (long)blockIdx.x * kEncWaves + (threadIdx.x >> 6);
-  if (row >= rows) return;
-  q4_encode_wave<D>(src + row * D, codes + row * (D / 2), scales + row);
+  for (long row = (long)blockIdx.x * kEncWaves + (threadIdx.x >> 6); row < rows; row += (long)gridDim.x * kEncWaves)
+    q4_encode_wave<D>(src + row * D, codes + row * (D / 2), scales + row);
 }
 
 }  // namespace
@@ -52,7 +54,7 @@ __global__ __launch_bounds__(kEncThreads) void q4_encode_kernel(const uint16_t* 
 hipError_t launch_q4_encode(const uint16_t* src, uint8_t* codes, float* scales, long rows, int D,
                             hipStream_t stream) {
   if (rows <= 0) return hipSuccess;
-  const long blocks = (rows + kEncWaves - 1) / kEncWaves;
+  const long blocks = std::min((rows + kEncWaves - 1) / kEncWaves, kEncMaxBlocks);
   if (D == 64)
     hipLaunchKernelGGL(q4_encode_kernel<64>, dim3((unsigned)blocks), dim3(kEncThreads), 0, stream, src, codes,
                        scales, rows);
@@ -65,7 +67,7 @@ hipError_t launch_q4_encode(const uint16_t* src, uint8_t* codes, float* scales, 
 hipError_t launch_q8_encode(const uint16_t* src, int8_t* codes, float* scales, long rows, int D,
                             hipStream_t stream) {
   if (rows <= 0) return hipSuccess;
-  const long blocks = (rows + kEncWaves - 1) / kEncWaves;
+  const long blocks = std::min((rows + kEncWaves - 1) / kEncWaves, kEncMaxBlocks);
   if (D == 64)
     hipLaunchKernelGGL(q8_encode_kernel<64>, dim3((unsigned)blocks), dim3(kEncThreads), 0, stream, src, codes,
                        scales, rows);

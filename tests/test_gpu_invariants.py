@@ -9,8 +9,9 @@ import pytest
 
 pytestmark = pytest.mark.gpu
 
+import oracle
 from workloads import make_tiny_case, contiguous_twin, permute_pages, duplicate_shared_pages, AttnCase
-from tests.gpu_util import say, attn_gpu, DeviceCase
+from tests.gpu_util import say, attn_gpu, DeviceCase, dev_bf16, assert_close
 
 
 @pytest.fixture(scope="module")
@@ -105,3 +106,48 @@ def test_broken_contracts_set_flags_without_faulting(pk):
     dc3.run()
     torch.cuda.synchronize()
     assert dc3.errors() & pk.PKV_EFLAG_ROWS
+
+
+def sentinel_run(pk, case, total_q, max_q_len):
+    """Attention with out pre-filled with a sentinel; returns (out, flags)."""
+    import torch
+    dc = DeviceCase(case, pk, max_q_len=max_q_len)
+    if total_q != case.q.shape[0]:   # the call's row count, independent of q_lens
+        q = np.zeros((total_q,) + case.q.shape[1:], case.q.dtype)
+        n = min(total_q, case.q.shape[0])
+        q[:n] = case.q[:n]
+        dc.q = dev_bf16(q)
+        dc.shape = pk.attn_shape(dc.q, dc.k, dc.bt, max_q_len, case.scale, 0)
+        dc.ws = pk.new_attn_workspace(dc.shape)
+        dc.out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    dc.out.fill_(1234.5)
+    dc.run()
+    torch.cuda.synchronize()
+    return dc.out.cpu().numpy(), dc.errors()
+
+
+@pytest.mark.parametrize("max_q_len", [2, 40])   # the split kernel; the long-window kernel (rows > 64)
+def test_negative_q_len_is_flagged_and_later_rows_are_left_alone(pk, max_q_len):
+    say(f"q_lens (2, -1, 2): QLEN flagged, max_q_len {max_q_len}")
+    case = make_tiny_case(304, [600, 300, 500], [2, 1, 2], Hq=8, Hkv=2, D=64)
+    ref = oracle.attention(case.q, case.k_pool, case.v_pool, case.block_table, case.seq_lens, case.q_lens,
+                           case.scale)
+    bad = AttnCase("negq", case.q, case.k_pool, case.v_pool, case.block_table, case.seq_lens,
+                   np.array([2, -1, 2], np.int32), case.scale)
+    got, flags = sentinel_run(pk, bad, case.q.shape[0], max_q_len)
+    assert flags & pk.PKV_EFLAG_QLEN
+    assert_close(got[:2], ref[:2], "sequence 0, before the negative length")
+    # sequence 2's rows would start at row 1 by the prefix sum: it is skipped, nothing else is written
+    assert np.all(got[2:] == np.float32(1234.5))
+
+
+@pytest.mark.parametrize("max_q_len", [2, 40])
+def test_row_sum_below_total_q_is_flagged(pk, max_q_len):
+    say(f"sum(q_lens) 3 < total_q 5: ROWS flagged, rows computed, the rest untouched, max_q_len {max_q_len}")
+    case = make_tiny_case(305, [600, 300], [2, 1], Hq=8, Hkv=2, D=64)
+    ref = oracle.attention(case.q, case.k_pool, case.v_pool, case.block_table, case.seq_lens, case.q_lens,
+                           case.scale)
+    got, flags = sentinel_run(pk, case, 5, max_q_len)
+    assert flags & pk.PKV_EFLAG_ROWS
+    assert_close(got[:3], ref, "the rows q_lens covers")
+    assert np.all(got[3:] == np.float32(1234.5))

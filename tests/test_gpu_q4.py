@@ -49,6 +49,21 @@ def test_q4_encoder_matches_the_oracle_bit_for_bit(pk, D):
     assert np.array_equal(np.isnan(got), np.isnan(es))
 
 
+def test_q4_encoder_strides_past_its_grid(pk):
+    # more rows than the capped grid covers in one pass (65536 workgroups of 4 rows)
+    rng = np.random.default_rng(9200)
+    n, D = 4 * 65536 + 77, 64
+    bits = f32_to_bf16_bits(rng.standard_normal((n, D)).astype(np.float32))
+    say(f"q4 encode: {n} rows, past the grid cap")
+    codes = torch.full((n, D // 2), 0x5A, dtype=torch.uint8, device="cuda")
+    scales = torch.full((n,), 7.0, dtype=torch.float32, device="cuda")
+    pk.pkv_q4_encode(dev_bf16(bits), codes, scales)
+    torch.cuda.synchronize()
+    ec, es = q4_cache.encode(bits)
+    np.testing.assert_array_equal(codes.cpu().numpy(), ec)
+    np.testing.assert_array_equal(scales.cpu().numpy().view(np.uint32), es.view(np.uint32))
+
+
 class Q4Case:
     """A case's pools encoded by the oracle, resident on the GPU."""
 
