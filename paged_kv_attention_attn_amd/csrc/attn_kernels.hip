@@ -55,6 +55,7 @@ struct ValuTile {
   static constexpr int RP = 4 * RPL;  // padded rows
   static constexpr int STEPS = TC / TG;
   static constexpr int PBUF = TC * RP * 4;  // P staging bytes per wave
+  static constexpr float kSplitWeight = 1.f / 8.f;  // the MFMA tile's two-term threshold
 
   u32 q[RPL][D / 2];
   float m[RPL], l[RPL];
@@ -137,6 +138,7 @@ struct ValuTile {
     }
     const int tok = tok0 + t;
     float alpha[RPL];
+    bool heavy = false;
 #pragma unroll
     for (int j = 0; j < RPL; ++j) {
       const float x = (tok <= lim[j] && t < nv) ? s[j] * scale_log2 : kNegInf;
@@ -147,7 +149,11 @@ struct ValuTile {
       l[j] = l[j] * alpha[j] + p;
       m[j] = mn;
       pb[t * RP + rg + 4 * j] = p;
+      // a key of this chunk weighing more than kSplitWeight of its row's sum
+      // so far (the row's 16 lanes): its bf16 P would not average out
+      heavy |= p > kSplitWeight * row16_sum(l[j]);
     }
+    const bool split = __builtin_amdgcn_ballot_w64(heavy) != 0;
     // rescale the accumulators of every row by its alpha
 #pragma unroll
     for (int j = 0; j < RPL; ++j) {
@@ -160,7 +166,9 @@ struct ValuTile {
     }
     // P.V on bf16 pairs: tokens tA = 2*sp*TG + tg and tB = tA + TG are
     // interleaved per dim, P is rounded to bf16 (as on the MFMA path), and
-    // one v_dot2 per (row, dim) takes both tokens.
+    // one v_dot2 per (row, dim) takes both tokens. On chunks with a heavy
+    // key P enters as two bf16 terms (the rounding remainder in a second
+    // v_dot2), about 16 significant bits.
     const int tg = lane / NC;
     const f32x4* pl = reinterpret_cast<const f32x4*>(pb);
     static_assert(STEPS % 2 == 0, "token pairs");
@@ -184,6 +192,17 @@ struct ValuTile {
         for (int e = 0; e < 8; ++e)
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) acc[4 * r4 + rr][e] = dot2(pp[rr], vp[e], acc[4 * r4 + rr][e]);
+        if (split) {
+          const float pf[4][2] = {{pa.x, pc.x}, {pa.y, pc.y}, {pa.z, pc.z}, {pa.w, pc.w}};
+          u32 pq[4];
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr)
+            pq[rr] = pack_bf16(pf[rr][0] - bf16lo(pp[rr]), pf[rr][1] - bf16hi(pp[rr]));
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) acc[4 * r4 + rr][e] = dot2(pq[rr], vp[e], acc[4 * r4 + rr][e]);
+        }
       }
     }
   }
