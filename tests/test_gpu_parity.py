@@ -136,6 +136,7 @@ def test_config5_queue(pk):
         np.testing.assert_array_equal(a, ea)
         np.testing.assert_array_equal(a, st.accept.planted_match + 1)
         np.testing.assert_array_equal(n, en)
+        np.testing.assert_array_equal(w, oracle.window_next(st.accept.window, st.accept.n_draft, ea))
 
 
 def test_accept_random_rows_ties_and_nan(pk):

@@ -147,6 +147,29 @@ def test_whole_prompt_prefill_full_size(pk):
     check_sampled(case, got, sample_picks(case, np.random.default_rng(6), 24), "full prefill")
 
 
+@pytest.mark.timeout(900)
+def test_whole_prompt_prefill_one_head_group_in_full(pk):
+    """8 x 8192 whole-prompt prefill: every one of the 8192 window rows of
+    one (sequence, KV head), all heads of its group, against the oracle."""
+    case = make_prefill_config("full")
+    rng = np.random.default_rng(7)
+    b, g = int(rng.integers(0, case.num_seqs)), int(rng.integers(0, case.k_pool.shape[1]))
+    Hq, Hkv = case.q.shape[1], case.k_pool.shape[1]
+    group = Hq // Hkv
+    say(f"prefill full: every row of sequence {b}, KV head {g} ({group} q heads x 8192 rows)")
+    dc = DeviceCase(case, pk)
+    got = dc.result()
+    assert dc.errors() == 0
+    L, ql = int(case.seq_lens[b]), int(case.q_lens[b])
+    r0 = int(np.sum(case.q_lens[:b]))
+    K = oracle.decode_bf16(oracle.gather_sequence(case.k_pool, case.block_table[b], L))[g:g + 1]
+    V = oracle.decode_bf16(oracle.gather_sequence(case.v_pool, case.block_table[b], L))[g:g + 1]
+    heads = slice(g * group, (g + 1) * group)
+    qrows = oracle.decode_bf16(case.q[r0:r0 + ql, heads])
+    ref = oracle.attention_rows(qrows, K, V, ql, L, case.scale)
+    assert_close(got[r0:r0 + ql, heads], ref, f"full prefill seq {b} KV head {g}")
+
+
 def test_broken_contracts_set_flags(pk):
     say("prefill: broken contracts set flags, other sequences unaffected")
     case = make_tiny_case(330, [600, 500], [200, 300], Hq=8, Hkv=2, D=64, table_width=4)
