@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libpkv.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["attn_kernels.hip", "attn_persist.hip", "accept_kernels.hip", "kv_kernels.hip", "pool_kernels.hip", "quant_kernels.hip", "host.cpp", "page_pool.cpp"]
+SOURCES = ["attn_kernels.hip", "accept_kernels.hip", "kv_kernels.hip", "pool_kernels.hip", "quant_kernels.hip", "host.cpp", "page_pool.cpp"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

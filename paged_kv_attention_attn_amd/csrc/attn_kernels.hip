@@ -1510,12 +1510,10 @@ long attn_slots(const AttnPlan& pl) {
 }
 
 constexpr int kMaxPps = 64;  // the kernel stages at most 64 table entries per split
-constexpr int kUnitsPerWg = 4;  // persistent kernel: work units per workgroup the plan aims for
 
 }  // namespace
 
-AttnPlan attn_plan(int B, int Hkv, int W, int max_q_len, int group, int D, long total_pages, int pages_per_split,
-                   bool allow_persist) {
+AttnPlan attn_plan(int B, int Hkv, int W, int max_q_len, int group, long total_pages, int pages_per_split) {
   AttnPlan pl{};
   pl.rows = max_q_len * group;
   // VALU dot products for up to 4 rows (decode with a group of 4); from 5
@@ -1531,16 +1529,10 @@ AttnPlan attn_plan(int B, int Hkv, int W, int max_q_len, int group, int D, long 
     pl.max_splits = 1;
     return pl;
   }
-  pl.persist = PKV_PERSIST && allow_persist && persist_layout(B, W, pl.rows, D, &pl.layout, &pl.nb);
   const long pages = total_pages > 0 ? total_pages : (long)B * W;
   long pps;
   if (pages_per_split > 0) {
     pps = pages_per_split;  // the caller's plan (attn_best_pps on its lengths)
-  } else if (pl.persist) {
-    // Work units of the persistent kernel: about kUnitsPerWg units per
-    // workgroup, so the ticket queue can even out the compute units' rates;
-    // each unit leaves a partial of (D + 2) floats per row to merge.
-    pps = (pages * Hkv + (long)kNumCu * kUnitsPerWg - 1) / ((long)kNumCu * kUnitsPerWg);
   } else {
     // As few splits as keep one round of workgroups on every CU. Each extra
     // split costs a partial write and read plus a merge; an idle CU costs
@@ -1559,17 +1551,8 @@ AttnPlan attn_plan(int B, int Hkv, int W, int max_q_len, int group, int D, long 
 }
 
 int attn_best_pps(int B, int Hkv, int W, int max_q_len, int group, int D, const int32_t* seq_lens) {
-  AttnPlan pl = attn_plan(B, Hkv, W, max_q_len, group, D, 0, 0);
+  AttnPlan pl = attn_plan(B, Hkv, W, max_q_len, group, 0, 0);
   if (pl.prefill) return 0;
-  if (pl.persist) {  // the persistent kernel's unit length for the pages the batch holds
-    long pages = 0;
-    for (int b = 0; b < B; ++b) {
-      long n = seq_lens[b] > 0 ? seq_lens[b] : 0;
-      if (n > (long)W * kPage) n = (long)W * kPage;
-      pages += (n + kPage - 1) / kPage;
-    }
-    return attn_plan(B, Hkv, W, max_q_len, group, D, pages > 0 ? pages : 1, 0).pps;
-  }
   const long slots = attn_slots(pl);
   // A workgroup's fixed cost (table and q loads before its first page
   // arrives, the partial stores and merge after its last), in page-stream
@@ -1604,8 +1587,8 @@ int attn_best_pps(int B, int Hkv, int W, int max_q_len, int group, int D, const 
 static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 AttnWorkspace attn_workspace(int B, int Hkv, int W, int max_q_len, int group, int D, long total_pages,
-                             int pages_per_split, bool allow_persist) {
-  const AttnPlan pl = attn_plan(B, Hkv, W, max_q_len, group, D, total_pages, pages_per_split, allow_persist);
+                             int pages_per_split) {
+  const AttnPlan pl = attn_plan(B, Hkv, W, max_q_len, group, total_pages, pages_per_split);
   AttnWorkspace ws;
   const size_t items = pl.prefill ? 0 : (size_t)B * Hkv * pl.max_splits;
   ws.err_off = 0;
@@ -1656,7 +1639,6 @@ hipError_t launch_shared_merge(const AttnParams& p, const SharedParams& sp, hipS
 
 hipError_t launch_attn(const AttnParams& p, const AttnPlan& plan, hipStream_t stream) {
   if (p.num_items == 0) return hipSuccess;
-  if (plan.persist) return launch_attn_persist(p, plan, stream);
   if (plan.prefill) {
     if (p.D == 64)
       hipLaunchKernelGGL((attn_prefill_kernel<64, PKV_PREFILL_NBUF, kLongNrb<64>>), dim3(p.num_items),

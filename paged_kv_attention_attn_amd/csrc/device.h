@@ -39,9 +39,6 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 #ifndef PKV_SHARED_WG
 #define PKV_SHARED_WG kNumCu  // workgroups the shared-prefix kernel aims for
 #endif
-#ifndef PKV_PERSIST
-#define PKV_PERSIST 0  // decode / verify shapes on the persistent kernel where its LDS layout fits
-#endif
 #ifndef PKV_FORCE_PPS
 #define PKV_FORCE_PPS 0  // pages per split; 0 = planned per shape
 #endif

@@ -146,11 +146,9 @@ SharedLayout shared_layout(const pkv_attn_shape* s, int32_t shared_pages) {
   // the tails reference the batch's pages less the shared ones of every row
   const long tail_pages = s->total_pages > 0 ? std::max(1L, s->total_pages - (long)s->num_seqs * shared_pages) : 0;
   // (a split length the caller planned for whole rows does not carry over)
-  // (the tails run the one-shot split kernel: its page offset and log-sum-exp output)
-  L.tail = pkv::attn_workspace(s->num_seqs, s->num_kv_heads, tail_w, s->max_q_len, group, s->head_dim,
-                               tail_pages, 0, false);
-  L.plan = pkv::attn_plan(s->num_seqs, s->num_kv_heads, tail_w, s->max_q_len, group, s->head_dim, tail_pages, 0,
-                          false);
+  L.tail =
+      pkv::attn_workspace(s->num_seqs, s->num_kv_heads, tail_w, s->max_q_len, group, s->head_dim, tail_pages, 0);
+  L.plan = pkv::attn_plan(s->num_seqs, s->num_kv_heads, tail_w, s->max_q_len, group, tail_pages, 0);
   L.sp = pkv::shared_plan(s->num_kv_heads, s->total_q, group, shared_pages);
   const size_t rows = (size_t)s->total_q * group;
   L.lse_off = align256(L.tail.total);
@@ -167,15 +165,9 @@ extern "C" {
 size_t pkv_attn_workspace_bytes(const pkv_attn_shape* s) {
   if (!attn_shape_ok(s)) return 0;
   const int group = s->num_q_heads / s->num_kv_heads;
-  // one workspace serves the plain call (persistent kernel where it applies)
-  // and the quantized calls (split kernel) on the same shape
-  const size_t a = pkv::attn_workspace(s->num_seqs, s->num_kv_heads, s->max_pages_per_seq, s->max_q_len, group,
-                                       s->head_dim, s->total_pages, s->pages_per_split, true)
-                       .total;
-  const size_t b = pkv::attn_workspace(s->num_seqs, s->num_kv_heads, s->max_pages_per_seq, s->max_q_len, group,
-                                       s->head_dim, s->total_pages, s->pages_per_split, false)
-                       .total;
-  return std::max(a, b);
+  return pkv::attn_workspace(s->num_seqs, s->num_kv_heads, s->max_pages_per_seq, s->max_q_len, group,
+                             s->head_dim, s->total_pages, s->pages_per_split)
+      .total;
 }
 
 int pkv_attn_plan(pkv_attn_shape* s, const int32_t* seq_lens_host) {
@@ -214,7 +206,7 @@ int pkv_attn_fwd(const void* q, const void* k_pool, const void* v_pool, const in
                                                     s->pages_per_split);
   if (!workspace || workspace_bytes < ws.total) return PKV_ERR_WORKSPACE;
   const pkv::AttnPlan plan = pkv::attn_plan(s->num_seqs, s->num_kv_heads, s->max_pages_per_seq,
-                                            s->max_q_len, group, s->head_dim, s->total_pages, s->pages_per_split);
+                                            s->max_q_len, group, s->total_pages, s->pages_per_split);
   const pkv::AttnParams p =
       attn_params(q, k_pool, v_pool, block_table, seq_lens, q_lens, out, s, workspace, ws, plan, 0);
   if (pkv::launch_attn(p, plan, static_cast<hipStream_t>(stream)) != hipSuccess) return PKV_ERR_HIP;
@@ -236,11 +228,10 @@ int attn_fwd_quant(int qbits, const void* q, const void* k_codes, const float* k
   const int group = s->num_q_heads / s->num_kv_heads;
   const pkv::AttnWorkspace ws = pkv::attn_workspace(s->num_seqs, s->num_kv_heads, s->max_pages_per_seq,
                                                     s->max_q_len, group, s->head_dim, s->total_pages,
-                                                    s->pages_per_split, false);
+                                                    s->pages_per_split);
   if (!workspace || workspace_bytes < ws.total) return PKV_ERR_WORKSPACE;
   const pkv::AttnPlan plan = pkv::attn_plan(s->num_seqs, s->num_kv_heads, s->max_pages_per_seq,
-                                            s->max_q_len, group, s->head_dim, s->total_pages, s->pages_per_split,
-                                            false);
+                                            s->max_q_len, group, s->total_pages, s->pages_per_split);
   pkv::AttnParams p =
       attn_params(q, k_codes, v_codes, block_table, seq_lens, q_lens, out, s, workspace, ws, plan, 0);
   p.k_scales = k_scales;

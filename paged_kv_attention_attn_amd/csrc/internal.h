@@ -40,15 +40,7 @@ struct AttnWorkspace {
   size_t err_off, counters_off, ml_off, acc_off, total;
 };
 
-// LDS layout of the persistent decode / verify kernel (byte offsets into its
-// dynamic LDS): K/V ring at 0, q row buffers, staged unit result, control
-// block, per-sequence arrays and the block table.
-struct PersistLayout {
-  int off_q, off_stage, off_ctrl, off_seq, bytes, qbytes;
-};
-
-// Plan: pages per split (per work unit on the persistent kernel) and the
-// kernel variant for a shape.
+// Plan: pages per split and the kernel variant for a shape.
 struct AttnPlan {
   int pps;
   int max_splits;
@@ -57,9 +49,6 @@ struct AttnPlan {
   bool prefill;  // rows > PKV_MAX_ROWS: the long-window kernel
   int qtok;      // prefill: window tokens per query tile
   int tiles;     // prefill: query tiles of the longest window
-  bool persist;  // the persistent kernel (rows <= 32, its LDS layout fits)
-  int nb;        // persistent: K/V ring depth in chunks
-  PersistLayout layout;
 };
 
 // Shared-prefix path: key splits of the shared pages and their partials.
@@ -73,10 +62,7 @@ struct SharedPlan {
   int splits, split_keys, row_tiles;
 };
 
-// allow_persist = false keeps the one-shot split kernel (the quantized caches
-// and the shared-prefix tails run only there).
-AttnPlan attn_plan(int B, int Hkv, int W, int max_q_len, int group, int D, long total_pages, int pages_per_split,
-                   bool allow_persist = true);
+AttnPlan attn_plan(int B, int Hkv, int W, int max_q_len, int group, long total_pages, int pages_per_split);
 // Pages per split for these host-side lengths: the least modelled time
 // (rounds of workgroups x (split pages + a workgroup's fixed cost)); 0 for
 // shapes on the long-window kernel.
@@ -85,9 +71,7 @@ SharedPlan shared_plan(int Hkv, int total_q, int group, int shared_pages);
 hipError_t launch_attn_shared(const AttnParams& p, const SharedParams& sp, hipStream_t stream);
 hipError_t launch_shared_merge(const AttnParams& p, const SharedParams& sp, hipStream_t stream);
 AttnWorkspace attn_workspace(int B, int Hkv, int W, int max_q_len, int group, int D, long total_pages,
-                             int pages_per_split, bool allow_persist = true);
-bool persist_layout(int B, int W, int rows, int D, PersistLayout* L, int* nb);
-hipError_t launch_attn_persist(const AttnParams& p, const AttnPlan& plan, hipStream_t stream);
+                             int pages_per_split);
 hipError_t launch_attn(const AttnParams& p, const AttnPlan& plan, hipStream_t stream);
 // Same over a quantized cache (p.k_pool / p.v_pool: codes, qbits 8 = int8 or
 // 4 = two nibbles per byte; p.k_scales / p.v_scales); decode / verify plans only.
