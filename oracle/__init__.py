@@ -22,8 +22,9 @@ What it computes is the plain definition, in float64:
   and defragmentation; ``page_pool.copy_pages`` / ``.remap_table`` for the
   data movement a defragmentation plans.
 * ``q8_cache.encode`` / ``.decode`` -- the Q8 cache: 8-bit codes with one
-  fp32 scale per token vector, and the bf16 values they decode to (attention
-  over a Q8 cache is ``attention`` over the decoded pools).
+  fp32 scale per token vector, and the values they decode to, code x scale
+  exactly (attention over a Q8 cache is ``attention_decoded`` over the
+  decoded pools).
 * ``q4_cache.encode`` / ``.decode`` -- the Q4 cache: the same scheme at 4
   bits (codes in [-7, 7], two nibbles per byte).
 * ``brute`` -- an independent pure-Python loop version of the attention, per
@@ -36,7 +37,7 @@ have no printed reference on the pages; they are pinned only through those
 checks.
 """
 
-from .paged_attention import decode_bf16, gather_sequence, attention, attention_rows
+from .paged_attention import decode_bf16, gather_sequence, attention, attention_decoded, attention_rows
 from .greedy_accept import argmax_rows, accept, window_next
 from . import kv_cache
 from . import page_pool

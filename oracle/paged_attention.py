@@ -79,8 +79,7 @@ def attention_rows(q_rows, K, V, q_len, seq_len, scale):
     return out
 
 
-def attention(q_bits, k_pool_bits, v_pool_bits, block_table, seq_lens, q_lens, scale):
-    """Paged attention over a batch: float64 [total_q, Hq, D]."""
+def _attention(q_bits, k_pool, v_pool, block_table, seq_lens, q_lens, scale, widen):
     q = decode_bf16(q_bits)
     total_q, Hq, D = q.shape
     out = np.zeros((total_q, Hq, D), dtype=np.float64)
@@ -91,10 +90,22 @@ def attention(q_bits, k_pool_bits, v_pool_bits, block_table, seq_lens, q_lens, s
         ql = int(q_lens[b])
         if ql == 0:
             continue
-        K = decode_bf16(gather_sequence(k_pool_bits, block_table[b], L))
-        V = decode_bf16(gather_sequence(v_pool_bits, block_table[b], L))
+        K = widen(gather_sequence(k_pool, block_table[b], L))
+        V = widen(gather_sequence(v_pool, block_table[b], L))
         out[r0:r0 + ql] = attention_rows(q[r0:r0 + ql], K, V, ql, L, scale)
         r0 += ql
     if r0 != total_q:
         raise ValueError(f"sum(q_lens) = {r0} but q has {total_q} rows")
     return out
+
+
+def attention(q_bits, k_pool_bits, v_pool_bits, block_table, seq_lens, q_lens, scale):
+    """Paged attention over a batch: float64 [total_q, Hq, D]."""
+    return _attention(q_bits, k_pool_bits, v_pool_bits, block_table, seq_lens, q_lens, scale, decode_bf16)
+
+
+def attention_decoded(q_bits, k_pool_vals, v_pool_vals, block_table, seq_lens, q_lens, scale):
+    """The same over pools already holding the cached values as float64
+    [P, Hkv, 256, D] (a quantized cache's decoded pools)."""
+    return _attention(q_bits, k_pool_vals, v_pool_vals, block_table, seq_lens, q_lens, scale,
+                      lambda x: np.asarray(x, dtype=np.float64))

@@ -15,16 +15,17 @@ page supports:
 * all in IEEE binary32 (the bf16 inputs are exact there);
 * storage: the nibble ``code + 8`` (1 .. 15; 8 for a zero code), two per
   byte, dim 2i in the low nibble of byte i and dim 2i + 1 in the high one;
-* decoding: ``bf16(float32(code) * scale)``, nearest even, as for Q8.
-  Attention over a Q4 cache is attention over the decoded pools.
+* decoding: ``code * scale`` exactly, as for Q8. Attention over a Q4 cache
+  is attention over the decoded pools.
 
 Layouts: packed uint8 [..., D / 2] and scales float32 [...] for bf16 bits
-uint16 [..., D] (pools: [P, Hkv, 256, D / 2] and [P, Hkv, 256]).
+uint16 [..., D] (pools: [P, Hkv, 256, D / 2] and [P, Hkv, 256]); decoded
+values float64 [..., D].
 """
 
 import numpy as np
 
-from .q8_cache import _widen, _to_bf16_bits
+from .q8_cache import _widen
 
 QMAX = np.float32(7.0)
 
@@ -66,9 +67,9 @@ def encode(bits):
 
 
 def decode(packed, scales):
-    """(packed uint8 codes, float32 scales) -> bf16 bit patterns of code * scale."""
-    c = unpack(packed).astype(np.float32)
-    s = np.asarray(scales, dtype=np.float32)[..., None]
+    """(packed uint8 codes, float32 scales) -> float64 values code * scale
+    (NaN where the scale is NaN)."""
+    c = unpack(packed).astype(np.float64)
+    s = np.asarray(scales, dtype=np.float32).astype(np.float64)[..., None]
     with np.errstate(invalid="ignore"):
-        prod = (c * s).astype(np.float32)
-    return _to_bf16_bits(prod)
+        return c * s

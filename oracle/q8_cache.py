@@ -17,12 +17,13 @@ gives no format. Readings taken (the plainest the page supports):
   0 and codes 0; a vector holding a non-finite value gets scale NaN and codes
   0 (its decoded values are NaN, like the unused slots of a bf16 pool);
 * all of it in IEEE binary32 (the inputs are bf16, exact in binary32);
-* decoding: ``bf16(float32(code) * scale)``, the binary32 product rounded to
-  bf16 (nearest, ties to even). Attention over a Q8 cache is attention over
-  the decoded pools, with every other definition unchanged.
+* decoding: ``code * scale``, the exact real product (exact in float64: 8
+  bits times 24). Attention over a Q8 cache is attention over the decoded
+  pools, with every other definition unchanged.
 
 Layouts: codes int8 [..., D] and scales float32 [...] for bf16 bits
-uint16 [..., D] (pools: [P, Hkv, 256, D] and [P, Hkv, 256]).
+uint16 [..., D] (pools: [P, Hkv, 256, D] and [P, Hkv, 256]); decoded values
+float64 [..., D].
 """
 
 import numpy as np
@@ -33,15 +34,6 @@ QMAX = np.float32(127.0)
 def _widen(bits):
     b = np.asarray(bits, dtype=np.uint16)
     return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
-
-
-def _to_bf16_bits(x32):
-    """binary32 -> bf16 bit patterns, rounding to nearest with ties to even
-    (NaN stays NaN)."""
-    u = np.ascontiguousarray(x32, dtype=np.float32).view(np.uint32)
-    rounded = ((u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)).astype(np.uint16)
-    nan = np.isnan(np.asarray(x32, dtype=np.float32))
-    return np.where(nan, np.uint16(0x7FC0), rounded)
 
 
 def encode(bits):
@@ -60,9 +52,9 @@ def encode(bits):
 
 
 def decode(codes, scales):
-    """(int8 codes, float32 scales) -> bf16 bit patterns of code * scale."""
-    c = np.asarray(codes, dtype=np.int8).astype(np.float32)
-    s = np.asarray(scales, dtype=np.float32)[..., None]
+    """(int8 codes, float32 scales) -> float64 values code * scale (NaN where
+    the scale is NaN)."""
+    c = np.asarray(codes, dtype=np.int8).astype(np.float64)
+    s = np.asarray(scales, dtype=np.float32).astype(np.float64)[..., None]
     with np.errstate(invalid="ignore"):
-        prod = (c * s).astype(np.float32)
-    return _to_bf16_bits(prod)
+        return c * s

@@ -98,7 +98,7 @@ def test_quantized_append_matches_the_oracle(pk, qbits, seed, D):
     assert pk.pkv_attn_check_errors(aws) == 0
     ekc, eks = qc.mod.encode(k2)
     evc, evs = qc.mod.encode(v2)
-    ref = oracle.attention(q, qc.mod.decode(ekc, eks), qc.mod.decode(evc, evs), t2, l2, ql, ashape.scale)
+    ref = oracle.attention_decoded(q, qc.mod.decode(ekc, eks), qc.mod.decode(evc, evs), t2, l2, ql, ashape.scale)
     assert_close(out.cpu().numpy(), ref, f"Q{qbits} attention after append")
 
 

@@ -124,7 +124,7 @@ class Q8Case:
 
     def expected(self):
         c = self.case
-        return oracle.attention(c.q, self.ref_k, self.ref_v, c.block_table, c.seq_lens, c.q_lens, c.scale)
+        return oracle.attention_decoded(c.q, self.ref_k, self.ref_v, c.block_table, c.seq_lens, c.q_lens, c.scale)
 
 
 @pytest.mark.parametrize("i", range(len(TINY)))

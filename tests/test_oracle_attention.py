@@ -240,3 +240,47 @@ def test_prefill_in_chunks_equals_whole_prompt():
         part = AttnCase("chunk", case.q[lo:hi], case.k_pool, case.v_pool, case.block_table,
                         np.array([hi], np.int32), np.array([hi - lo], np.int32), case.scale)
         np.testing.assert_array_equal(run(part), whole[lo:hi])
+
+
+# ---- attention over pools of already-decoded values (the quantized caches)
+
+def test_decoded_pools_single_visible_token_returns_its_decoded_value():
+    from oracle import q8_cache
+    case = make_tiny_case(8, [1, 1], [1, 1], Hq=4, Hkv=2, D=16)
+    kc, ks = q8_cache.encode(case.k_pool)
+    vc, vs = q8_cache.encode(case.v_pool)
+    K, V = q8_cache.decode(kc, ks), q8_cache.decode(vc, vs)
+    got = oracle.attention_decoded(case.q, K, V, case.block_table, case.seq_lens, case.q_lens, case.scale)
+    for b in range(2):
+        page = case.block_table[b, 0]
+        for h in range(4):
+            # one visible key: weight 1 on its value, code x scale exactly
+            np.testing.assert_array_equal(got[b, h], vc[page, h // 2, 0].astype(np.float64) * float(vs[page, h // 2, 0]))
+
+
+def test_decoded_pools_with_equal_keys_average_the_decoded_values():
+    from oracle import q4_cache
+    case = make_tiny_case(9, [300], [2], Hq=2, Hkv=1, D=8)
+    page0, page1 = case.block_table[0, 0], case.block_table[0, 1]
+    key = case.k_pool[page0, 0, 0].copy()
+    case.k_pool[page0, 0, :] = key
+    case.k_pool[page1, 0, :44] = key
+    kc, ks = q4_cache.encode(case.k_pool)
+    vc, vs = q4_cache.encode(case.v_pool)
+    K, V = q4_cache.decode(kc, ks), q4_cache.decode(vc, vs)
+    got = oracle.attention_decoded(case.q, K, V, case.block_table, case.seq_lens, case.q_lens, case.scale)
+    codes = np.concatenate([q4_cache.unpack(vc[page0, 0]), q4_cache.unpack(vc[page1, 0, :44])]).astype(np.float64)
+    scales = np.concatenate([vs[page0, 0], vs[page1, 0, :44]]).astype(np.float64)
+    vals = codes * scales[:, None]
+    for i in range(2):
+        visible = 300 - 2 + i + 1
+        np.testing.assert_allclose(got[i, 0], vals[:visible].mean(axis=0), rtol=1e-12, atol=1e-13)
+
+
+def test_decoded_bf16_pools_give_the_bf16_result():
+    case = make_tiny_case(10, [700, 33], [3, 1], Hq=4, Hkv=2, D=16)
+    got = oracle.attention_decoded(case.q, oracle.decode_bf16(case.k_pool), oracle.decode_bf16(case.v_pool),
+                                   case.block_table, case.seq_lens, case.q_lens, case.scale)
+    ref = np.array(attention_brute(case.q, case.k_pool, case.v_pool, case.block_table, case.seq_lens,
+                                   case.q_lens, case.scale))
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-13)

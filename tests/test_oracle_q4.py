@@ -26,9 +26,11 @@ def test_round_trip_error_is_bounded():
     x = normal_bf16(rng, (200, 128))
     p, s = q4.encode(x)
     c = q4.unpack(p)
-    d = widen(q4.decode(p, s))
-    bound = s[:, None] / 2 + np.abs(c * s[:, None].astype(np.float64)) * 2.0 ** -8
-    assert np.all(np.abs(d - widen(x)) <= bound + 1e-12)
+    d = q4.decode(p, s)
+    # half a quantization step (plus the binary32 quotient's rounding); the
+    # decoded value is the exact product
+    bound = s[:, None].astype(np.float64) * (0.5 + 2.0 ** -20)
+    assert np.all(np.abs(d - widen(x)) <= bound)
     assert np.all(np.abs(c) <= 7)
     assert p.shape == (200, 64) and p.dtype == np.uint8
 
@@ -52,7 +54,7 @@ def test_exact_multiples_and_the_nibble_order():
     assert list(p[0]) == [(1 | 2 << 4), (3 | 4 << 4), (5 | 6 << 4), (7 | 8 << 4),
                           (9 | 10 << 4), (11 | 12 << 4), (13 | 14 << 4), (15 | 15 << 4)]
     assert np.array_equal(q4.unpack(p)[0], k.astype(np.int8))
-    assert np.array_equal(q4.decode(p, s), x)
+    assert np.array_equal(q4.decode(p, s), widen(x))
 
 
 def test_ties_go_to_even():
@@ -80,21 +82,23 @@ def test_zero_and_non_finite_vectors():
     z[1, 3] = 0x8000
     p, s = q4.encode(z)
     assert np.all(p == 0x88) and np.all(s == 0)
-    assert np.all(widen(q4.decode(p, s)) == 0)
+    assert np.all(q4.decode(p, s) == 0)
     bad = np.full((3, 64), 0x3F80, np.uint16)
     bad[0, 5] = 0x7FC0
     bad[1, 9] = 0xFF80                                   # -inf
     p, s = q4.encode(bad)
     assert np.isnan(s[0]) and np.isnan(s[1]) and s[2] == np.float32(1.0 / 7)
     assert np.all(p[:2] == 0x88) and np.all(p[2] == 0xFF)
-    d = widen(q4.decode(p, s))
-    assert np.all(np.isnan(d[:2])) and np.all(d[2] == 1.0)
+    d = q4.decode(p, s)
+    assert np.all(np.isnan(d[:2]))
+    # 7 times binary32(1/7) = 0.14285714924335479736328125, exactly
+    assert np.all(d[2] == 1.00000004470348358154296875)
 
 
 def test_scalar_rederivation_on_small_vectors():
     """Element by element with numpy float32 scalars: scale, quotient, round
-    half to even by hand, the nibble pair of each byte, the product and its
-    bf16 rounding by hand."""
+    half to even by hand, the nibble pair of each byte; the decoded value is
+    the code times the scale in Python's (binary64) arithmetic."""
     rng = np.random.default_rng(14)
     x = normal_bf16(rng, (6, 16))
     p, s = q4.encode(x)
@@ -114,30 +118,22 @@ def test_scalar_rederivation_on_small_vectors():
             code = lo + 1 if frac > 0.5 or (frac == 0.5 and lo % 2 == 1) else lo
             code = int(max(-7, min(7, code)))
             codes.append(code)
-            prod = np.float32(np.float32(code) * scale)
-            u = int(np.array([prod], np.float32).view(np.uint32)[0])
-            hi, low = u >> 16, u & 0xFFFF
-            if low > 0x8000 or (low == 0x8000 and hi & 1):
-                hi += 1
-            assert hi == int(d[r, j])
+            assert d[r, j] == code * float(scale)
         for i in range(8):
             assert int(p[r, i]) == (codes[2 * i] + 8) + 16 * (codes[2 * i + 1] + 8)
 
 
 def test_every_byte_decodes_to_its_nibble_pair():
-    """All 256 bytes, at scale 1 and at an odd scale: byte b holds codes
-    (b & 15) - 8 and (b >> 4) - 8; the decoded bf16 is the float32 product
-    rounded to nearest even, done here by hand."""
+    """All 256 bytes at scale 1: byte b holds codes (b & 15) - 8 (even dim)
+    and (b >> 4) - 8 (odd dim), decoded exactly; and products worked out by
+    hand at binary32(0.3) = 0.300000011920928955078125 and at 2^-130."""
     b = np.arange(256, dtype=np.uint8).reshape(256, 1)
-    for scale in (np.float32(1.0), np.float32(0.3), np.float32(2.0 ** -130)):
-        s = np.full(256, scale, np.float32)
-        d = q4.decode(b, s)
-        for v in range(256):
-            for half, code in ((0, (v & 15) - 8), (1, (v >> 4) - 8)):
-                prod = np.float32(np.float32(code) * scale)
-                u = int(np.array([prod], np.float32).view(np.uint32)[0])
-                hi, low = u >> 16, u & 0xFFFF
-                if low > 0x8000 or (low == 0x8000 and hi & 1):
-                    hi += 1
-                assert int(d[v, half]) == (hi & 0xFFFF), (v, half, scale)
-    assert np.array_equal(q4.pack(q4.unpack(b.reshape(1, 256))), b.reshape(1, 256))
+    d = q4.decode(b, np.ones(256, np.float32))
+    for v in range(256):
+        assert d[v, 0] == (v & 15) - 8 and d[v, 1] == (v >> 4) - 8
+    d = q4.decode(np.array([[0x0F, 0xF0]], np.uint8), np.array([0.3], np.float32))
+    # bytes 0x0F, 0xF0: codes (7, -8), (-8, 7)
+    assert list(d[0]) == [2.100000083446502685546875, -2.4000000953674316406250,
+                          -2.4000000953674316406250, 2.100000083446502685546875]
+    d = q4.decode(np.array([[0x00]], np.uint8), np.array([2.0 ** -130], np.float32))
+    assert list(d[0]) == [-(2.0 ** -127), -(2.0 ** -127)]
