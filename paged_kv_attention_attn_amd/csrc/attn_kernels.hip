@@ -119,10 +119,19 @@ struct ValuTile {
   }
 
   // One chunk of TC tokens starting at absolute token tok0 (nv of them
-  // inside the sequence), from the operands fetch() copied.
-  __device__ __forceinline__ void compute(float* pb, int tok0, int nv, float scale_log2) {
+  // inside the sequence), from the operands fetch() copied. Quantized caches
+  // (QB != 0): the staged operands are codes, and qsc holds the chunk's K
+  // scales (words 0..) and V scales (words 64..): token t's score is scaled
+  // by its K scale, its weight P by its V scale (the row sum keeps plain P).
+  template <int QB = 0>
+  __device__ __forceinline__ void compute(float* pb, int tok0, int nv, float scale_log2, const float* qsc) {
     const int lane = threadIdx.x & 63;
     const int rg = lane >> 4, t = lane & 15;
+    float ksl = scale_log2, vsc = 1.f;
+    if constexpr (QB != 0) {
+      ksl = qsc[t] * (scale_log2 * kStageFactor<QB>);
+      vsc = qsc[64 + t] * kStageFactor<QB>;
+    }
     float s[RPL];
 #pragma unroll
     for (int j = 0; j < RPL; ++j) s[j] = 0.f;
@@ -141,14 +150,14 @@ struct ValuTile {
     bool heavy = false;
 #pragma unroll
     for (int j = 0; j < RPL; ++j) {
-      const float x = (tok <= lim[j] && t < nv) ? s[j] * scale_log2 : kNegInf;
+      const float x = (tok <= lim[j] && t < nv) ? s[j] * ksl : kNegInf;
       const float mn = fmaxf(m[j], row16_max(x));
       const float mu = (mn == kNegInf) ? 0.f : mn;
       alpha[j] = exp2f_fast(m[j] - mu);
       const float p = exp2f_fast(x - mu);
       l[j] = l[j] * alpha[j] + p;
       m[j] = mn;
-      pb[t * RP + rg + 4 * j] = p;
+      pb[t * RP + rg + 4 * j] = QB != 0 ? p * vsc : p;
       // a key of this chunk weighing more than kSplitWeight of its row's sum
       // so far (the row's 16 lanes): its bf16 P would not average out
       heavy |= p > kSplitWeight * row16_sum(l[j]);
@@ -352,7 +361,11 @@ struct MfmaTile {
     fetch_v(vt);
   }
 
-  __device__ __forceinline__ void compute(float*, int tok0, int nv, float scale_log2) {
+  // Quantized caches (QB != 0): as the VALU tile's compute, with the K scale
+  // on each score and the V scale on each weight of P.V (rows' sums keep
+  // plain P).
+  template <int QB = 0>
+  __device__ __forceinline__ void compute(float*, int tok0, int nv, float scale_log2, const float* qsc) {
     const int lane = threadIdx.x & 63;
     const int half = lane >> 5;
     f32x16 S[NRB];
@@ -380,7 +393,8 @@ struct MfmaTile {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int tt = 8 * (i >> 2) + 4 * half + (i & 3);
-        x[i] = (tok0 + tt <= lim[rb] && tt < nv) ? S[rb][i] * scale_log2 : kNegInf;
+        const float ksl = QB != 0 ? qsc[tt] * (scale_log2 * kStageFactor<QB>) : scale_log2;
+        x[i] = (tok0 + tt <= lim[rb] && tt < nv) ? S[rb][i] * ksl : kNegInf;
         cm = fmaxf(cm, x[i]);
       }
       cm = max_xor32(cm);
@@ -398,6 +412,10 @@ struct MfmaTile {
       // a key of this chunk weighing more than kSplitWeight of its row's sum
       // so far (both halves of the row): its bf16 P would not average out
       heavy |= cm != kNegInf && exp2f_fast(cm - mu) > kSplitWeight * sum_xor32(l[rb]);
+      if constexpr (QB != 0) {  // P.V weights carry the V scales
+#pragma unroll
+        for (int i = 0; i < 16; ++i) p[rb][i] *= qsc[64 + 8 * (i >> 2) + 4 * half + (i & 3)] * kStageFactor<QB>;
+      }
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) acc[rb][mb] *= alpha;
 #pragma unroll
@@ -642,8 +660,9 @@ struct MfmaTile {
 // ring slot holds a chunk's K and V codes (TC x D x QBITS / 8 bytes each,
 // token-major as in the pool, in whole 1 KiB load areas) and their per-token
 // scales (a 256-byte area each, filled by one 4-byte load per lane); the wave
-// decodes the slot into a bf16 K/V pair in the layout of a bf16 slot, its
-// staging area, which the row tiles read as they read a bf16 slot.
+// decodes the slot's codes into a bf16 K/V pair in the layout of a bf16
+// slot, its staging area (followed by the scales), which the row tiles read
+// as they read a bf16 slot, applying the scales to scores and weights.
 template <int D, class Tile, int NBUF, int WAVES, int QBITS = 0>
 struct KernelCfg {
   static constexpr int W = WAVES;
@@ -655,7 +674,7 @@ struct KernelCfg {
   static constexpr int NCI = QAREA / 1024;               // 1 KiB code loads per K (or V) chunk
   static constexpr int SLOT = QBITS ? 2 * QAREA + 512 : 2 * G::TILE;
   static constexpr int OPS = QBITS ? 2 * NCI + 2 : 2 * G::NI;  // load instructions per chunk
-  static constexpr int RING = NBUF * SLOT + (QBITS ? 2 * G::TILE : 0);  // per wave (+ staging)
+  static constexpr int RING = NBUF * SLOT + (QBITS ? 2 * G::TILE + 512 : 0);  // per wave (+ staging, its scales)
   static constexpr int QB = (Tile::RP * D * 2 + 1023) / 1024 * 1024;  // whole 1 KiB loads
   static constexpr int NQI = QB / 1024;                  // q load instructions per workgroup
   static constexpr int STAGE = WAVES * (RING + Tile::PBUF) + QB;
@@ -665,15 +684,18 @@ struct KernelCfg {
 };
 
 // Decode one quantized ring slot (see KernelCfg) into bf16 K and V tiles at
-// stg, in the swizzled layout of a bf16 slot: value = bf16(code * scale), the
-// fp32 product rounded to nearest even. Each lane takes 16-code pieces (one
-// token, 16 dims: 16 bytes at QB = 8, 8 bytes of nibbles at QB = 4, dim 2i in
-// the low nibble of byte i) and writes them as two 16-byte chunks. Tokens
-// past the sequence end have zero codes and scales (the chunk load
-// zero-fills them) and decode to zeros as a bf16 slot's do; a zero byte of
-// nibbles is the code pair (-8, -8) times a zero scale.
-__device__ __forceinline__ u32 pack_codes(float a, float b, float s) { return pack_bf16(a * s, b * s); }
-
+// stg, in the swizzled layout of a bf16 slot, and copy its per-token scales
+// after them (K scales at word 0, V scales at word 64). A cached value is
+// code * scale exactly; the staged tiles hold only the codes, exact in bf16,
+// and the row tiles apply a token's K scale to its score and its V scale to
+// its weight P. Q8: a code is one sign-extending byte convert. Q4: each
+// nibble n = code + 8 is moved to the top of its byte and the byte's sign bit
+// flipped, which leaves 16 * code as a signed byte (n >= 8: 16n - 128; n < 8:
+// 16n + 128 - 256), so it too is one byte convert; the row tiles fold the
+// 1/16 into the scales. Each lane takes 16-code pieces (one token, 16 dims:
+// 16 bytes at QB = 8, 8 bytes of nibbles at QB = 4, dim 2i in the low nibble
+// of byte i). Tokens past the sequence end have zero codes and zero scales
+// (the chunk load zero-fills them): their scores and weights are zero.
 template <int D, int TC, int QB, int QAREA>
 __device__ __forceinline__ void q_decode_slot(const char* slot, char* stg) {
   constexpr int NC = D / 8;          // 16-byte bf16 chunks per token
@@ -683,6 +705,9 @@ __device__ __forceinline__ void q_decode_slot(const char* slot, char* stg) {
   static_assert(TC * PPT % 64 == 0, "pieces must fill the wave");
   const int lane = threadIdx.x & 63;
   const float* sc = reinterpret_cast<const float*>(slot + 2 * QAREA);
+  float* ss = reinterpret_cast<float*>(stg + 2 * TC * D * 2);
+  ss[lane] = sc[lane];
+  ss[64 + lane] = sc[64 + lane];
 #pragma unroll
   for (int kv = 0; kv < 2; ++kv) {
     const char* src = slot + kv * QAREA;
@@ -691,45 +716,26 @@ __device__ __forceinline__ void q_decode_slot(const char* slot, char* stg) {
     for (int i = 0; i < NP; ++i) {
       const int pc = i * 64 + lane;
       const int t = pc / PPT, h = pc % PPT;
-      const float s = sc[kv * 64 + t];
       u32 o[8];
       if constexpr (QB == 8) {
         const u32x4 w = *reinterpret_cast<const u32x4*>(src + pc * PB);
         const u32 ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          o[2 * j] = pack_codes((float)(int8_t)(ws[j] & 0xFFu), (float)(int8_t)((ws[j] >> 8) & 0xFFu), s);
-          o[2 * j + 1] = pack_codes((float)(int8_t)((ws[j] >> 16) & 0xFFu), (float)(int8_t)(ws[j] >> 24), s);
+          o[2 * j] = pack_bf16((float)(int8_t)(ws[j] & 0xFFu), (float)(int8_t)((ws[j] >> 8) & 0xFFu));
+          o[2 * j + 1] = pack_bf16((float)(int8_t)((ws[j] >> 16) & 0xFFu), (float)(int8_t)(ws[j] >> 24));
         }
       } else {
         const u32x2 w = *reinterpret_cast<const u32x2*>(src + pc * PB);
         const u32 ws[2] = {w.x, w.y};
-        // nibble n = code + 8: n * s - 8 s is code * s exactly, so one fma
-        // rounds it as the product would be. -8 s is exact while finite; a
-        // wave holding a scale above 2^124 (a vector near the bf16 maximum)
-        // takes the subtract-then-multiply form instead.
-        const float s8 = -8.f * s;
-        if (__builtin_amdgcn_ballot_w64(!__builtin_isfinite(s8)) == 0) {
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            // even / odd dims, one nibble per byte; the masks go through asm so the
-            // byte converts below read them whole (v_cvt_f32_ubyte0..3) instead of
-            // the compiler extracting every nibble on its own
-            u32 lo, hi;
-            asm("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(lo) : "v"(ws[j]));
-            asm("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(hi) : "v"(ws[j] >> 4));
+        for (int j = 0; j < 2; ++j) {
+          // even dims (low nibbles) and odd dims (high nibbles), 16 * code per byte
+          const u32 lo = ((ws[j] << 4) & 0xF0F0F0F0u) ^ 0x80808080u;
+          const u32 hi = (ws[j] & 0xF0F0F0F0u) ^ 0x80808080u;
 #pragma unroll
-            for (int b = 0; b < 4; ++b)
-              o[4 * j + b] = pack_bf16(__builtin_fmaf((float)((lo >> (8 * b)) & 0xFFu), s, s8),
-                                       __builtin_fmaf((float)((hi >> (8 * b)) & 0xFFu), s, s8));
-          }
-        } else {
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int n = 0; n < 8; n += 2)
-              o[4 * j + n / 2] = pack_codes((float)((int)((ws[j] >> (4 * n)) & 15u) - 8),
-                                            (float)((int)((ws[j] >> (4 * n + 4)) & 15u) - 8), s);
+          for (int b = 0; b < 4; ++b)
+            o[4 * j + b] = pack_bf16((float)(int8_t)((lo >> (8 * b)) & 0xFFu), (float)(int8_t)((hi >> (8 * b)) & 0xFFu));
         }
       }
       dst[t * NC + ((2 * h) ^ (t & (NC - 1)))] = u32x4{o[0], o[1], o[2], o[3]};
@@ -915,16 +921,18 @@ __global__ __launch_bounds__(WAVES * 64) void attn_split_kernel(
     const int t0 = tok_begin + c * TC;
     const int nv = min(TC, tok_end - t0);
     const char* kt = ring + (k % NBUF) * C::SLOT;
+    const float* qsc = nullptr;  // quantized: the chunk's staged K and V scales
     if constexpr (QB != 0) {
       char* stg = ring + NBUF * C::SLOT;
       q_decode_slot<D, TC, QB, C::QAREA>(kt, stg);
       kt = stg;
+      qsc = reinterpret_cast<const float*>(stg + 2 * G::TILE);
     }
     tile.fetch(kt, kt + G::TILE, nv);
     // the slot is free once its operands sit in registers: refill it now so
     // NBUF chunks stay in flight while this one is computed
     if (k + NBUF < my_chunks) issue(k + NBUF);
-    tile.compute(pbuf, t0, nv, p.scale_log2);
+    tile.template compute<QB>(pbuf, t0, nv, p.scale_log2, qsc);
   }
 
   // ---- merge the waves in LDS

@@ -45,9 +45,17 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr u32 PKV_EFLAG_PAGE_BIT = 1u, PKV_EFLAG_QLEN_BIT = 2u, PKV_EFLAG_ROWS_BIT = 4u;
 constexpr int kNumCu = 256;           // MI355X compute units
-constexpr int kValuMaxRows = 4;       // q rows per (sequence, KV head) on the VALU tile
+#ifndef PKV_VALU_MAX_ROWS
+#define PKV_VALU_MAX_ROWS 4
+#endif
+constexpr int kValuMaxRows = PKV_VALU_MAX_ROWS;  // q rows per (sequence, KV head) on the VALU tile
 constexpr int kLdsPerCu = 160 * 1024;  // gfx950 LDS per CU
 constexpr float kNegInf = -__builtin_inff();
+// Quantized caches: what a token's staged K/V values must be multiplied by,
+// besides its scale, to give the cached values (Q4 stages 16 x code; the
+// factor is exact while the scale is at least 2^-122).
+template <int QB>
+constexpr float kStageFactor = QB == 4 ? 0.0625f : 1.f;
 
 __device__ __forceinline__ u32 uniform(u32 x) { return __builtin_amdgcn_readfirstlane(x); }
 
