@@ -60,9 +60,10 @@ def parse():
 
 # Sources of the attention kernel: a stored HBM-traffic measurement is used only
 # while their hash matches the one recorded with it.
-KERNEL_SOURCES = ("paged_kv_attention_attn_amd/csrc/attn_kernels.hip",
+KERNEL_SOURCES = ("paged_kv_attention_attn_amd/csrc/attn_kernels.hip", "paged_kv_attention_attn_amd/csrc/device.h",
                   "paged_kv_attention_attn_amd/csrc/internal.h")
 TRAFFIC_PROFILE = "profiles/attn_split_kernel_mfma.verify_8x8192_w6.md"
+DEDUP_PROFILE = "profiles/attn_split_kernel_valu.dedup_100x4096_shared.md"   # configuration 4, plain call
 COPY_CAL_BYTES = 256 << 20
 
 
@@ -75,12 +76,12 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
-def stored_traffic():
-    """HBM bytes per launch of the verify-workload attention kernel from the
-    committed rocprofv3 counter summary (FETCH_SIZE and WRITE_SIZE, each
-    scaled by its reading on a plain copy of known size), or None when the
-    summary is missing or was taken on different kernel sources."""
-    path = os.path.join(ROOT, TRAFFIC_PROFILE)
+def stored_traffic(profile=TRAFFIC_PROFILE):
+    """HBM bytes per launch of an attention kernel from its committed
+    rocprofv3 counter summary (FETCH_SIZE and WRITE_SIZE, each scaled by its
+    reading on a plain copy of known size), or None when the summary is
+    missing or was taken on different kernel sources."""
+    path = os.path.join(ROOT, profile)
     try:
         text = open(path).read()
         block = text.split("```json", 1)[1].split("```", 1)[0]
@@ -563,6 +564,8 @@ def main():
                                "over fp32 logits [48, 128256] with the +2/-1 window rule",
                    "global_batch": int(case.num_seqs), "seq_len": int(case.seq_lens[0]),
                    "q_len": int(case.q_lens[0]), "parallelism": "single GPU"},
+        "value_note": "value = K/V bytes per step / (attention + accept) time per step; "
+                      "attn_kv_gbps and roofline are the attention kernel alone",
         "hbm_fraction": round(value / HBM_PEAK_GBPS, 4),
         "attn_kv_gbps": round(attn_gbps, 2),
         "attn_hbm_fraction": round(attn_gbps / HBM_PEAK_GBPS, 4),
@@ -591,10 +594,22 @@ def main():
             a = Attn(c, pk, torch, R)
             ms = time_ms(torch, a, args.steps, args.warmup)
             kb = kv_logical_bytes(c.seq_lens, c.num_kv_heads, c.head_dim)
-            sweep[f"config{cfg}"] = {"attn_us": round(ms * 1e3, 3), "kv_bytes": kb,
-                                     "kv_gbps": round(kb / (ms * 1e-3) / 1e9, 2),
-                                     "hbm_fraction": round(kb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-                                     "decode_tokens_per_s": round(c.num_seqs / (ms * 1e-3), 1)}
+            ent = {"attn_us": round(ms * 1e3, 3), "kv_bytes": kb,
+                   "kv_gbps": round(kb / (ms * 1e-3) / 1e9, 2),
+                   "hbm_fraction": round(kb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                   "decode_tokens_per_s": round(c.num_seqs / (ms * 1e-3), 1)}
+            if cfg == 4:
+                # shared prefix pages are read through one L2 per XCD, so the
+                # logical K/V bytes (the prefix counted once per sequence) far
+                # exceed what DRAM delivers: a logical rate, not an HBM fraction
+                ent["kv_bytes_logical"] = ent.pop("kv_bytes")
+                ent["kv_gbps_logical"] = ent.pop("kv_gbps")
+                ent["logical_rate_over_hbm_peak"] = ent.pop("hbm_fraction")
+                rec = stored_traffic(DEDUP_PROFILE)
+                ent["dram_bytes_per_launch"] = None if rec is None else int(rec["hbm_bytes_per_launch"])
+                ent["dram_gbps"] = None if rec is None else round(rec["hbm_bytes_per_launch"] / (ms * 1e-3) / 1e9, 2)
+                ent["dram_profile"] = DEDUP_PROFILE if rec is not None else None
+            sweep[f"config{cfg}"] = ent
             if ca is not None:   # a verify step: attention + accept
                 ac = Accept(ca, pk, torch, R)
                 ms_acc = time_ms(torch, ac, args.steps, args.warmup)
