@@ -55,6 +55,7 @@ struct ValuTile {
   static constexpr int RP = 4 * RPL;  // padded rows
   static constexpr int STEPS = TC / TG;
   static constexpr int PBUF = TC * RP * 4;  // P staging bytes per wave
+  static constexpr bool kVDirect = true;    // quantized caches: V converted straight from its codes
   static constexpr float kSplitWeight = 1.f / 8.f;  // the MFMA tile's two-term threshold
 
   u32 q[RPL][D / 2];
@@ -115,6 +116,42 @@ struct ValuTile {
       const int tt = st * TG + tg;
       vv[st] = vl[tt * NC + (dc ^ (tt & (NC - 1)))];
       if (tt >= nv) vv[st] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  // Quantized caches: this lane's K row from the slot's staged bf16 K tile
+  // (as fetch), and its V pieces converted straight from the slot's codes
+  // (vc: token-major, D * QB / 8 bytes per token; each V code is read and
+  // converted once, by the lane whose P.V piece it is): Q8, one
+  // sign-extending byte convert per code; Q4, 16 * code per byte as in
+  // q_decode_slot.
+  template <int QB>
+  __device__ __forceinline__ void fetch_q(const char* kt, const char* vc, int nv) {
+    const int lane = threadIdx.x & 63;
+    const int t = lane & 15;
+    const u32x4* kl = reinterpret_cast<const u32x4*>(kt);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) kv[c] = kl[t * NC + (c ^ (t & (NC - 1)))];
+    const int tg = lane / NC, dc = lane % NC;
+    constexpr int TB = D * QB / 8;  // code bytes per token
+#pragma unroll
+    for (int st = 0; st < STEPS; ++st) {
+      const int tt = st * TG + tg;
+      u32 o[4];
+      if constexpr (QB == 8) {
+        const u32x2 w = *reinterpret_cast<const u32x2*>(vc + tt * TB + dc * 8);
+        o[0] = pack_bf16((float)(int8_t)(w.x & 0xFFu), (float)(int8_t)((w.x >> 8) & 0xFFu));
+        o[1] = pack_bf16((float)(int8_t)((w.x >> 16) & 0xFFu), (float)(int8_t)(w.x >> 24));
+        o[2] = pack_bf16((float)(int8_t)(w.y & 0xFFu), (float)(int8_t)((w.y >> 8) & 0xFFu));
+        o[3] = pack_bf16((float)(int8_t)((w.y >> 16) & 0xFFu), (float)(int8_t)(w.y >> 24));
+      } else {
+        const u32 w = *reinterpret_cast<const u32*>(vc + tt * TB + dc * 4);
+        const u32 lo = ((w << 4) & 0xF0F0F0F0u) ^ 0x80808080u, hi = (w & 0xF0F0F0F0u) ^ 0x80808080u;
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          o[b] = pack_bf16((float)(int8_t)((lo >> (8 * b)) & 0xFFu), (float)(int8_t)((hi >> (8 * b)) & 0xFFu));
+      }
+      vv[st] = tt < nv ? u32x4{o[0], o[1], o[2], o[3]} : u32x4{0u, 0u, 0u, 0u};
     }
   }
 
@@ -254,6 +291,7 @@ struct MfmaTile {
   static constexpr int MB = D / 32;  // 32-dim blocks of the output
   static constexpr int RP = 32 * NRB;
   static constexpr int PBUF = 0;
+  static constexpr bool kVDirect = false;  // quantized caches: V staged as bf16 like K
 
   u32x4 qb[NRB][KK];
   float m[NRB], l[NRB];
@@ -674,7 +712,11 @@ struct KernelCfg {
   static constexpr int NCI = QAREA / 1024;               // 1 KiB code loads per K (or V) chunk
   static constexpr int SLOT = QBITS ? 2 * QAREA + 512 : 2 * G::TILE;
   static constexpr int OPS = QBITS ? 2 * NCI + 2 : 2 * G::NI;  // load instructions per chunk
-  static constexpr int RING = NBUF * SLOT + (QBITS ? 2 * G::TILE + 512 : 0);  // per wave (+ staging, its scales)
+  // staging: the bf16 K tile (and V tile unless the row tile converts V
+  // straight from its codes), then the chunk's scales
+  static constexpr bool VDIRECT = QBITS != 0 && Tile::kVDirect;
+  static constexpr int STG_TILES = VDIRECT ? 1 : 2;
+  static constexpr int RING = NBUF * SLOT + (QBITS ? STG_TILES * G::TILE + 512 : 0);  // per wave (+ staging)
   static constexpr int QB = (Tile::RP * D * 2 + 1023) / 1024 * 1024;  // whole 1 KiB loads
   static constexpr int NQI = QB / 1024;                  // q load instructions per workgroup
   static constexpr int STAGE = WAVES * (RING + Tile::PBUF) + QB;
@@ -696,7 +738,7 @@ struct KernelCfg {
 // 16 bytes at QB = 8, 8 bytes of nibbles at QB = 4, dim 2i in the low nibble
 // of byte i). Tokens past the sequence end have zero codes and zero scales
 // (the chunk load zero-fills them): their scores and weights are zero.
-template <int D, int TC, int QB, int QAREA>
+template <int D, int TC, int QB, int QAREA, int TILES = 2>
 __device__ __forceinline__ void q_decode_slot(const char* slot, char* stg) {
   constexpr int NC = D / 8;          // 16-byte bf16 chunks per token
   constexpr int PPT = D / 16;        // 16-code pieces per token
@@ -705,11 +747,11 @@ __device__ __forceinline__ void q_decode_slot(const char* slot, char* stg) {
   static_assert(TC * PPT % 64 == 0, "pieces must fill the wave");
   const int lane = threadIdx.x & 63;
   const float* sc = reinterpret_cast<const float*>(slot + 2 * QAREA);
-  float* ss = reinterpret_cast<float*>(stg + 2 * TC * D * 2);
+  float* ss = reinterpret_cast<float*>(stg + TILES * TC * D * 2);
   ss[lane] = sc[lane];
   ss[64 + lane] = sc[64 + lane];
 #pragma unroll
-  for (int kv = 0; kv < 2; ++kv) {
+  for (int kv = 0; kv < TILES; ++kv) {
     const char* src = slot + kv * QAREA;
     u32x4* dst = reinterpret_cast<u32x4*>(stg + kv * TC * D * 2);
 #pragma unroll
@@ -758,7 +800,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_split_kernel(
   constexpr int NI = G::NI;
   constexpr int NC = G::NC;
   constexpr int RP = Tile::RP;
-  static_assert(NBUF >= 2 && NBUF <= 4, "ring depth");
+  static_assert(NBUF >= 2 && NBUF <= 6, "ring depth");
   __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
   __shared__ int s_pages[C::MAX_PPS];
   __shared__ int s_last;
@@ -924,11 +966,15 @@ __global__ __launch_bounds__(WAVES * 64) void attn_split_kernel(
     const float* qsc = nullptr;  // quantized: the chunk's staged K and V scales
     if constexpr (QB != 0) {
       char* stg = ring + NBUF * C::SLOT;
-      q_decode_slot<D, TC, QB, C::QAREA>(kt, stg);
-      kt = stg;
-      qsc = reinterpret_cast<const float*>(stg + 2 * G::TILE);
+      q_decode_slot<D, TC, QB, C::QAREA, C::STG_TILES>(kt, stg);
+      qsc = reinterpret_cast<const float*>(stg + C::STG_TILES * G::TILE);
+      if constexpr (C::VDIRECT)
+        tile.template fetch_q<QB>(stg, kt + C::QAREA, nv);
+      else
+        tile.fetch(stg, stg + G::TILE, nv);
+    } else {
+      tile.fetch(kt, kt + G::TILE, nv);
     }
-    tile.fetch(kt, kt + G::TILE, nv);
     // the slot is free once its operands sit in registers: refill it now so
     // NBUF chunks stay in flight while this one is computed
     if (k + NBUF < my_chunks) issue(k + NBUF);
@@ -1495,7 +1541,12 @@ hipError_t launch_one(const AttnParams& p, hipStream_t stream) {
 
 template <int D, int QB>
 hipError_t launch_d(const AttnParams& p, const AttnPlan& plan, hipStream_t stream) {
-  if (!plan.mfma) return launch_one<D, ValuTile<D, 1>, PKV_VALU_NBUF, PKV_VALU_WAVES, QB>(p, stream);
+  // the Q4 VALU ring goes deeper: a chunk of codes is a quarter of a bf16
+  // chunk, and with the V codes converted straight from the slot (no V
+  // staging) four slots still leave two workgroups per CU (Q8 measured no
+  // better at three slots than at two)
+  constexpr int kValuNbuf = QB == 8 ? PKV_VALU_Q8_NBUF : QB == 4 ? PKV_VALU_Q4_NBUF : PKV_VALU_NBUF;
+  if (!plan.mfma) return launch_one<D, ValuTile<D, 1>, kValuNbuf, PKV_VALU_WAVES, QB>(p, stream);
   if (plan.rows <= 32) return launch_one<D, MfmaTile<D, 1>, PKV_MFMA_NBUF, PKV_MFMA_WAVES, QB>(p, stream);
   return launch_one<D, MfmaTile<D, 2>, PKV_MFMA_NBUF, PKV_MFMA_WAVES, QB>(p, stream);
 }

@@ -24,6 +24,12 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 #ifndef PKV_VALU_NBUF
 #define PKV_VALU_NBUF 2  // LDS ring depth (chunks) per wave, VALU row tile
 #endif
+#ifndef PKV_VALU_Q8_NBUF
+#define PKV_VALU_Q8_NBUF 2  // LDS ring depth (chunks) per wave, VALU row tile over a Q8 cache
+#endif
+#ifndef PKV_VALU_Q4_NBUF
+#define PKV_VALU_Q4_NBUF 4  // LDS ring depth (chunks) per wave, VALU row tile over a Q4 cache
+#endif
 #ifndef PKV_MFMA_NBUF
 #define PKV_MFMA_NBUF 2  // LDS ring depth (chunks) per wave, MFMA row tile
 #endif
@@ -212,6 +218,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, u32
 // Wait until at most `ahead` (0..MAXA) chunks of N load ops each are pending.
 template <int N, int MAXA>
 __device__ __forceinline__ void wait_ahead(int ahead) {
+  static_assert(MAXA <= 5 && MAXA * N < 64, "vmcnt range");
+  if constexpr (MAXA >= 5) {
+    if (ahead >= 5) { wait_vmcnt<5 * N>(); return; }
+  }
   if constexpr (MAXA >= 4) {
     if (ahead >= 4) { wait_vmcnt<4 * N>(); return; }
   }
