@@ -140,16 +140,15 @@ struct ValuTile {
       u32 o[4];
       if constexpr (QB == 8) {
         const u32x2 w = *reinterpret_cast<const u32x2*>(vc + tt * TB + dc * 8);
-        o[0] = pack_bf16((float)(int8_t)(w.x & 0xFFu), (float)(int8_t)((w.x >> 8) & 0xFFu));
-        o[1] = pack_bf16((float)(int8_t)((w.x >> 16) & 0xFFu), (float)(int8_t)(w.x >> 24));
-        o[2] = pack_bf16((float)(int8_t)(w.y & 0xFFu), (float)(int8_t)((w.y >> 8) & 0xFFu));
-        o[3] = pack_bf16((float)(int8_t)((w.y >> 16) & 0xFFu), (float)(int8_t)(w.y >> 24));
+        sbytes_bf16(w.x, o[0], o[1]);
+        sbytes_bf16(w.y, o[2], o[3]);
       } else {
         const u32 w = *reinterpret_cast<const u32*>(vc + tt * TB + dc * 4);
         const u32 lo = ((w << 4) & 0xF0F0F0F0u) ^ 0x80808080u, hi = (w & 0xF0F0F0F0u) ^ 0x80808080u;
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-          o[b] = pack_bf16((float)(int8_t)((lo >> (8 * b)) & 0xFFu), (float)(int8_t)((hi >> (8 * b)) & 0xFFu));
+        o[0] = pack_bf16(sbyte_f32<0>(lo), sbyte_f32<0>(hi));
+        o[1] = pack_bf16(sbyte_f32<1>(lo), sbyte_f32<1>(hi));
+        o[2] = pack_bf16(sbyte_f32<2>(lo), sbyte_f32<2>(hi));
+        o[3] = pack_bf16(sbyte_f32<3>(lo), sbyte_f32<3>(hi));
       }
       vv[st] = tt < nv ? u32x4{o[0], o[1], o[2], o[3]} : u32x4{0u, 0u, 0u, 0u};
     }
@@ -763,10 +762,7 @@ __device__ __forceinline__ void q_decode_slot(const char* slot, char* stg) {
         const u32x4 w = *reinterpret_cast<const u32x4*>(src + pc * PB);
         const u32 ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          o[2 * j] = pack_bf16((float)(int8_t)(ws[j] & 0xFFu), (float)(int8_t)((ws[j] >> 8) & 0xFFu));
-          o[2 * j + 1] = pack_bf16((float)(int8_t)((ws[j] >> 16) & 0xFFu), (float)(int8_t)(ws[j] >> 24));
-        }
+        for (int j = 0; j < 4; ++j) sbytes_bf16(ws[j], o[2 * j], o[2 * j + 1]);
       } else {
         const u32x2 w = *reinterpret_cast<const u32x2*>(src + pc * PB);
         const u32 ws[2] = {w.x, w.y};
@@ -775,9 +771,10 @@ __device__ __forceinline__ void q_decode_slot(const char* slot, char* stg) {
           // even dims (low nibbles) and odd dims (high nibbles), 16 * code per byte
           const u32 lo = ((ws[j] << 4) & 0xF0F0F0F0u) ^ 0x80808080u;
           const u32 hi = (ws[j] & 0xF0F0F0F0u) ^ 0x80808080u;
-#pragma unroll
-          for (int b = 0; b < 4; ++b)
-            o[4 * j + b] = pack_bf16((float)(int8_t)((lo >> (8 * b)) & 0xFFu), (float)(int8_t)((hi >> (8 * b)) & 0xFFu));
+          o[4 * j + 0] = pack_bf16(sbyte_f32<0>(lo), sbyte_f32<0>(hi));
+          o[4 * j + 1] = pack_bf16(sbyte_f32<1>(lo), sbyte_f32<1>(hi));
+          o[4 * j + 2] = pack_bf16(sbyte_f32<2>(lo), sbyte_f32<2>(hi));
+          o[4 * j + 3] = pack_bf16(sbyte_f32<3>(lo), sbyte_f32<3>(hi));
         }
       }
       dst[t * NC + ((2 * h) ^ (t & (NC - 1)))] = u32x4{o[0], o[1], o[2], o[3]};

@@ -177,6 +177,30 @@ __device__ __forceinline__ u32 pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(u32, v);
 }
 
+// Signed byte B of w as a float: one sign-extending SDWA convert (left to
+// itself the compiler sometimes shifts and bit-extracts every byte first).
+template <int B>
+__device__ __forceinline__ float sbyte_f32(u32 w) {
+  static_assert(B >= 0 && B < 4, "byte index");
+  float r;
+  if constexpr (B == 0)
+    asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_0" : "=v"(r) : "v"(w));
+  else if constexpr (B == 1)
+    asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1" : "=v"(r) : "v"(w));
+  else if constexpr (B == 2)
+    asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2" : "=v"(r) : "v"(w));
+  else
+    asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3" : "=v"(r) : "v"(w));
+  return r;
+}
+
+// The four signed bytes of w as two bf16 pairs (bytes 0, 1 and 2, 3); exact
+// for bytes in [-128, 127].
+__device__ __forceinline__ void sbytes_bf16(u32 w, u32& lo, u32& hi) {
+  lo = pack_bf16(sbyte_f32<0>(w), sbyte_f32<1>(w));
+  hi = pack_bf16(sbyte_f32<2>(w), sbyte_f32<3>(w));
+}
+
 __device__ __forceinline__ u32 lds_addr_of(const void* p) {
   return static_cast<u32>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)(p)));
 }
