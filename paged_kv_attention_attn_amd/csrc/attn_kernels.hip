@@ -57,6 +57,7 @@ struct ValuTile {
   static constexpr int PBUF = TC * RP * 4;  // P staging bytes per wave
   static constexpr bool kVDirect = true;    // quantized caches: V converted straight from its codes
   static constexpr float kSplitWeight = 1.f / 8.f;  // the MFMA tile's two-term threshold
+  static constexpr float kLazyLog2 = 8.f;           // reference-max slack, as on the long-window tile
 
   u32 q[RPL][D / 2];
   float m[RPL], l[RPL];
@@ -182,33 +183,50 @@ struct ValuTile {
       }
     }
     const int tok = tok0 + t;
-    float alpha[RPL];
+    // Lazy rescale: a row keeps its reference max m while the chunk's scores
+    // stay below m + kLazyLog2, so P = 2^(x - m) may reach 2^kLazyLog2 and the
+    // weights' ratios are unchanged; only a row that outgrows it moves m and
+    // rescales its sum and accumulators (rare after the first chunks, and
+    // then the whole wave skips the accumulator pass).
+    float x[RPL], cm[RPL];
+    bool grow = false;
+#pragma unroll
+    for (int j = 0; j < RPL; ++j) {
+      x[j] = (tok <= lim[j] && t < nv) ? s[j] * ksl : kNegInf;
+      cm[j] = row16_max(x[j]);
+      grow |= cm[j] > m[j] + kLazyLog2;
+    }
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      float alpha[RPL];
+#pragma unroll
+      for (int j = 0; j < RPL; ++j) {
+        const bool g = cm[j] > m[j] + kLazyLog2;
+        alpha[j] = g ? exp2f_fast(m[j] - cm[j]) : 1.f;  // 0 while m is -inf
+        m[j] = g ? cm[j] : m[j];
+        l[j] *= alpha[j];
+      }
+#pragma unroll
+      for (int j = 0; j < RPL; ++j) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha[j]), g4 * 16));
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[g4 + 4 * j][e] *= a;
+        }
+      }
+    }
     bool heavy = false;
 #pragma unroll
     for (int j = 0; j < RPL; ++j) {
-      const float x = (tok <= lim[j] && t < nv) ? s[j] * ksl : kNegInf;
-      const float mn = fmaxf(m[j], row16_max(x));
-      const float mu = (mn == kNegInf) ? 0.f : mn;
-      alpha[j] = exp2f_fast(m[j] - mu);
-      const float p = exp2f_fast(x - mu);
-      l[j] = l[j] * alpha[j] + p;
-      m[j] = mn;
+      const float mu = (m[j] == kNegInf) ? 0.f : m[j];
+      const float p = exp2f_fast(x[j] - mu);
+      l[j] += p;
       pb[t * RP + rg + 4 * j] = QB != 0 ? p * vsc : p;
       // a key of this chunk weighing more than kSplitWeight of its row's sum
       // so far (the row's 16 lanes): its bf16 P would not average out
       heavy |= p > kSplitWeight * row16_sum(l[j]);
     }
     const bool split = __builtin_amdgcn_ballot_w64(heavy) != 0;
-    // rescale the accumulators of every row by its alpha
-#pragma unroll
-    for (int j = 0; j < RPL; ++j) {
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha[j]), g4 * 16));
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[g4 + 4 * j][e] *= a;
-      }
-    }
     // P.V on bf16 pairs: tokens tA = 2*sp*TG + tg and tB = tA + TG are
     // interleaved per dim, P is rounded to bf16 (as on the MFMA path), and
     // one v_dot2 per (row, dim) takes both tokens. On chunks with a heavy
