@@ -61,6 +61,7 @@ struct ValuTile {
 
   u32 q[RPL][D / 2];
   float m[RPL], l[RPL];
+  float mu[RPL];  // m, or 0 while m is -inf (the exponent's offset)
   int lim[RPL];
   float acc[RP][8];
   u32x4 kv[NC];      // this lane's token row of the current K chunk
@@ -72,6 +73,7 @@ struct ValuTile {
     for (int j = 0; j < RPL; ++j) {
       const int r = rg + 4 * j;
       m[j] = kNegInf;
+      mu[j] = 0.f;
       l[j] = 0.f;
       lim[j] = r < rows ? seq_len - q_len + r / group : -1;
     }
@@ -125,9 +127,14 @@ struct ValuTile {
   // (vc: token-major, D * QB / 8 bytes per token; each V code is read and
   // converted once, by the lane whose P.V piece it is): Q8, one
   // sign-extending byte convert per code; Q4, 16 * code per byte as in
-  // q_decode_slot.
+  // q_decode_slot. The converts pair the two tokens of each P.V step per dim
+  // (vv[2 sp] holds dims 0..3 as (tA, tB) bf16 pairs, vv[2 sp + 1] dims
+  // 4..7), the layout compute() would otherwise build with shifts and masks.
+  // Tokens past the sequence end need no mask: their codes and scales were
+  // loaded as zeros, so their weights P * V scale are zero and their V
+  // values finite (a zero Q4 byte stages as 16 * -8).
   template <int QB>
-  __device__ __forceinline__ void fetch_q(const char* kt, const char* vc, int nv) {
+  __device__ __forceinline__ void fetch_q(const char* kt, const char* vc) {
     const int lane = threadIdx.x & 63;
     const int t = lane & 15;
     const u32x4* kl = reinterpret_cast<const u32x4*>(kt);
@@ -135,23 +142,32 @@ struct ValuTile {
     for (int c = 0; c < NC; ++c) kv[c] = kl[t * NC + (c ^ (t & (NC - 1)))];
     const int tg = lane / NC, dc = lane % NC;
     constexpr int TB = D * QB / 8;  // code bytes per token
+    static_assert(STEPS % 2 == 0, "token pairs");
 #pragma unroll
-    for (int st = 0; st < STEPS; ++st) {
-      const int tt = st * TG + tg;
-      u32 o[4];
+    for (int sp = 0; sp < STEPS / 2; ++sp) {
+      const int tA = 2 * sp * TG + tg, tB = tA + TG;
+      float a[8], b[8];
       if constexpr (QB == 8) {
-        const u32x2 w = *reinterpret_cast<const u32x2*>(vc + tt * TB + dc * 8);
-        sbytes_bf16(w.x, o[0], o[1]);
-        sbytes_bf16(w.y, o[2], o[3]);
+        const u32x2 wa = *reinterpret_cast<const u32x2*>(vc + tA * TB + dc * 8);
+        const u32x2 wb = *reinterpret_cast<const u32x2*>(vc + tB * TB + dc * 8);
+        a[0] = sbyte_f32<0>(wa.x), a[1] = sbyte_f32<1>(wa.x), a[2] = sbyte_f32<2>(wa.x), a[3] = sbyte_f32<3>(wa.x);
+        a[4] = sbyte_f32<0>(wa.y), a[5] = sbyte_f32<1>(wa.y), a[6] = sbyte_f32<2>(wa.y), a[7] = sbyte_f32<3>(wa.y);
+        b[0] = sbyte_f32<0>(wb.x), b[1] = sbyte_f32<1>(wb.x), b[2] = sbyte_f32<2>(wb.x), b[3] = sbyte_f32<3>(wb.x);
+        b[4] = sbyte_f32<0>(wb.y), b[5] = sbyte_f32<1>(wb.y), b[6] = sbyte_f32<2>(wb.y), b[7] = sbyte_f32<3>(wb.y);
       } else {
-        const u32 w = *reinterpret_cast<const u32*>(vc + tt * TB + dc * 4);
-        const u32 lo = ((w << 4) & 0xF0F0F0F0u) ^ 0x80808080u, hi = (w & 0xF0F0F0F0u) ^ 0x80808080u;
-        o[0] = pack_bf16(sbyte_f32<0>(lo), sbyte_f32<0>(hi));
-        o[1] = pack_bf16(sbyte_f32<1>(lo), sbyte_f32<1>(hi));
-        o[2] = pack_bf16(sbyte_f32<2>(lo), sbyte_f32<2>(hi));
-        o[3] = pack_bf16(sbyte_f32<3>(lo), sbyte_f32<3>(hi));
+        const u32 wa = *reinterpret_cast<const u32*>(vc + tA * TB + dc * 4);
+        const u32 wb = *reinterpret_cast<const u32*>(vc + tB * TB + dc * 4);
+        // dim 2i in the low nibble of byte i
+        const u32 la = ((wa << 4) & 0xF0F0F0F0u) ^ 0x80808080u, ha = (wa & 0xF0F0F0F0u) ^ 0x80808080u;
+        const u32 lb = ((wb << 4) & 0xF0F0F0F0u) ^ 0x80808080u, hb = (wb & 0xF0F0F0F0u) ^ 0x80808080u;
+        a[0] = sbyte_f32<0>(la), a[1] = sbyte_f32<0>(ha), a[2] = sbyte_f32<1>(la), a[3] = sbyte_f32<1>(ha);
+        a[4] = sbyte_f32<2>(la), a[5] = sbyte_f32<2>(ha), a[6] = sbyte_f32<3>(la), a[7] = sbyte_f32<3>(ha);
+        b[0] = sbyte_f32<0>(lb), b[1] = sbyte_f32<0>(hb), b[2] = sbyte_f32<1>(lb), b[3] = sbyte_f32<1>(hb);
+        b[4] = sbyte_f32<2>(lb), b[5] = sbyte_f32<2>(hb), b[6] = sbyte_f32<3>(lb), b[7] = sbyte_f32<3>(hb);
       }
-      vv[st] = tt < nv ? u32x4{o[0], o[1], o[2], o[3]} : u32x4{0u, 0u, 0u, 0u};
+      vv[2 * sp] = u32x4{pack_bf16(a[0], b[0]), pack_bf16(a[1], b[1]), pack_bf16(a[2], b[2]), pack_bf16(a[3], b[3])};
+      vv[2 * sp + 1] =
+          u32x4{pack_bf16(a[4], b[4]), pack_bf16(a[5], b[5]), pack_bf16(a[6], b[6]), pack_bf16(a[7], b[7])};
     }
   }
 
@@ -187,22 +203,25 @@ struct ValuTile {
     // stay below m + kLazyLog2, so P = 2^(x - m) may reach 2^kLazyLog2 and the
     // weights' ratios are unchanged; only a row that outgrows it moves m and
     // rescales its sum and accumulators (rare after the first chunks, and
-    // then the whole wave skips the accumulator pass).
-    float x[RPL], cm[RPL];
+    // then the whole wave skips the accumulator pass). m is uniform over a
+    // row's 16 lanes, so a lane's own score decides whether its row grows;
+    // the row maximum is taken only then.
+    float x[RPL];
     bool grow = false;
 #pragma unroll
     for (int j = 0; j < RPL; ++j) {
       x[j] = (tok <= lim[j] && t < nv) ? s[j] * ksl : kNegInf;
-      cm[j] = row16_max(x[j]);
-      grow |= cm[j] > m[j] + kLazyLog2;
+      grow |= x[j] > m[j] + kLazyLog2;
     }
     if (__builtin_amdgcn_ballot_w64(grow)) {
       float alpha[RPL];
 #pragma unroll
       for (int j = 0; j < RPL; ++j) {
-        const bool g = cm[j] > m[j] + kLazyLog2;
-        alpha[j] = g ? exp2f_fast(m[j] - cm[j]) : 1.f;  // 0 while m is -inf
-        m[j] = g ? cm[j] : m[j];
+        const float cm = row16_max(x[j]);
+        const bool g = cm > m[j] + kLazyLog2;
+        alpha[j] = g ? exp2f_fast(m[j] - cm) : 1.f;  // 0 while m is -inf
+        m[j] = g ? cm : m[j];
+        mu[j] = (m[j] == kNegInf) ? 0.f : m[j];
         l[j] *= alpha[j];
       }
 #pragma unroll
@@ -218,8 +237,7 @@ struct ValuTile {
     bool heavy = false;
 #pragma unroll
     for (int j = 0; j < RPL; ++j) {
-      const float mu = (m[j] == kNegInf) ? 0.f : m[j];
-      const float p = exp2f_fast(x[j] - mu);
+      const float p = exp2f_fast(x[j] - mu[j]);
       l[j] += p;
       pb[t * RP + rg + 4 * j] = QB != 0 ? p * vsc : p;
       // a key of this chunk weighing more than kSplitWeight of its row's sum
@@ -239,12 +257,17 @@ struct ValuTile {
     for (int sp = 0; sp < STEPS / 2; ++sp) {
       const int tA = 2 * sp * TG + tg, tB = tA + TG;
       const u32x4 wa = vv[2 * sp], wb = vv[2 * sp + 1];
-      const u32 va4[4] = {wa.x, wa.y, wa.z, wa.w}, vb4[4] = {wb.x, wb.y, wb.z, wb.w};
       u32 vp[8];  // (V[tA][d], V[tB][d]) for the lane's 8 dims
+      if constexpr (QB != 0) {  // fetch_q converted them in this order
+        vp[0] = wa.x, vp[1] = wa.y, vp[2] = wa.z, vp[3] = wa.w;
+        vp[4] = wb.x, vp[5] = wb.y, vp[6] = wb.z, vp[7] = wb.w;
+      } else {
+        const u32 va4[4] = {wa.x, wa.y, wa.z, wa.w}, vb4[4] = {wb.x, wb.y, wb.z, wb.w};
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        vp[2 * k] = (va4[k] & 0xFFFFu) | (vb4[k] << 16);
-        vp[2 * k + 1] = (va4[k] >> 16) | (vb4[k] & 0xFFFF0000u);
+        for (int k = 0; k < 4; ++k) {
+          vp[2 * k] = (va4[k] & 0xFFFFu) | (vb4[k] << 16);
+          vp[2 * k + 1] = (va4[k] >> 16) | (vb4[k] & 0xFFFF0000u);
+        }
       }
 #pragma unroll
       for (int r4 = 0; r4 < RP / 4; ++r4) {
@@ -984,7 +1007,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_split_kernel(
       q_decode_slot<D, TC, QB, C::QAREA, C::STG_TILES>(kt, stg);
       qsc = reinterpret_cast<const float*>(stg + C::STG_TILES * G::TILE);
       if constexpr (C::VDIRECT)
-        tile.template fetch_q<QB>(stg, kt + C::QAREA, nv);
+        tile.template fetch_q<QB>(stg, kt + C::QAREA);
       else
         tile.fetch(stg, stg + G::TILE, nv);
     } else {
