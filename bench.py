@@ -349,6 +349,30 @@ def prefill_leg(torch, pk, seed, steps, warmup):
                       "tflops": round(tflops, 1), "mfma_fraction": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                       "tokens_per_s": round(float(c.q_lens.sum()) / (ms * 1e-3), 1),
                       "window_tokens": int(c.q_lens.sum()), "cached_tokens": int(c.seq_lens.sum())}
+        if which == "dedup":
+            # the same tails through the shared-prefix call: every tail row of
+            # the batch stacked against the 16 shared pages once per KV head,
+            # then each tail over its own keys, merged by log-sum-exp
+            log("prefill dedup through the shared-prefix call")
+            shared = 16
+            ws = pk.new_attn_shared_workspace(a.shape, shared)
+            f = lambda i: pk.pkv_attn_fwd_shared(a.q, a.k[0], a.v[0], a.bt, a.sl, a.ql, a.out, a.shape, shared, ws)
+            a(0)
+            torch.cuda.synchronize()
+            plain = a.out.cpu().numpy()
+            ms_s = time_ms(torch, f, steps, warmup)
+            torch.cuda.synchronize()
+            assert pk.pkv_attn_check_errors(ws) == 0, "shared-prefix call flagged its inputs"
+            got = a.out.cpu().numpy()
+            # both calls meet the oracle's tolerance, so they agree within twice it
+            assert np.all(np.abs(got - plain) <= 2 * (2e-3 + 1e-2 * np.abs(plain))), "shared call != plain call"
+            tf_s = fl / (ms_s * 1e-3) / 1e12
+            out[which]["shared_call"] = {
+                "us": round(ms_s * 1e3, 1), "tflops": round(tf_s, 1),
+                "mfma_fraction": round(tf_s / MFMA_BF16_PEAK_TFLOPS, 4), "shared_pages": shared,
+                "note": "pkv_attn_fwd_shared on the same batch (same algorithmic flops); output checked "
+                        "against the plain call"}
+            del ws
         del a
         torch.cuda.empty_cache()
     out["note"] = ("algorithmic flops = 4 * head_dim * q_heads * sum over window rows of visible keys; "

@@ -157,13 +157,15 @@ int pkv_attn_fwd(const void* q, const void* k_pool, const void* v_pool,
                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Decode / verify (max_q_len * Hq/Hkv <= PKV_MAX_ROWS) over a batch whose
- * sequences all begin with the same shared_pages pages: a deduplicated prompt
- * prefix (Dynamic Generator page, "Deduplication": every job references the
- * same cached pages). Same arguments, layouts and result as pkv_attn_fwd; the
- * shared keys are attended to once per KV head for all window rows of the
- * batch (matrix cores, rows of every sequence stacked), the rest of every
- * sequence as in pkv_attn_fwd, and the two are merged by log-sum-exp.
+ * Attention over a batch whose sequences all begin with the same shared_pages
+ * pages: a deduplicated prompt prefix (Dynamic Generator page,
+ * "Deduplication": every job references the same cached pages). Windows of
+ * any length: decode, verify, or the prefill of each job's private tail. Same
+ * arguments, layouts and result as pkv_attn_fwd; the shared keys are attended
+ * to once per KV head for all window rows of the batch (matrix cores, rows of
+ * every sequence stacked, so a short window pads nothing on its own), the rest
+ * of every sequence as in pkv_attn_fwd, and the two are merged by
+ * log-sum-exp.
  * shared_pages = 0 is pkv_attn_fwd. Workspace: pkv_attn_shared_workspace_bytes
  * (zero-filled before its first use, like pkv_attn_fwd's; every call leaves
  * it ready for the next).

@@ -1348,7 +1348,10 @@ __global__ __launch_bounds__(kLongWaves<NRB> * 64) void attn_prefill_kernel(
   const int b = bg / Hkv, g = bg % Hkv;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
 
-  const int seq_len = seq_lens[b];
+  // p.page_offset leading table entries (and their tokens) are skipped: a
+  // shared prefix attended to elsewhere; 0 otherwise
+  const int po = p.page_offset;
+  const int seq_len = seq_lens[b] - po * kPage;
   const int q_len = q_lens[b];
   const RowPrefix rp = row_prefix(q_lens, b, B);
   const int q_start = rp.start;
@@ -1362,7 +1365,7 @@ __global__ __launch_bounds__(kLongWaves<NRB> * 64) void attn_prefill_kernel(
   const int n_tiles = (q_len + qtok - 1) / qtok;
   if (qr >= n_tiles) return;
   const int n_pages = (seq_len + kPage - 1) / kPage;
-  if (q_len > p.max_q_len || q_len > seq_len || n_pages > W || n_pages > kPrefillMaxPages) {
+  if (q_len > p.max_q_len || q_len > seq_len || n_pages > W - po || n_pages > kPrefillMaxPages) {
     if (qr == 0 && g == 0 && threadIdx.x == 0) atomicOr(p.err, PKV_EFLAG_QLEN_BIT);
     return;
   }
@@ -1376,7 +1379,7 @@ __global__ __launch_bounds__(kLongWaves<NRB> * 64) void attn_prefill_kernel(
   const int n_chunks = (key_end + TC - 1) / TC;
   const int need_pages = (key_end + kPage - 1) / kPage;
   for (int j = threadIdx.x; j < need_pages; j += THREADS) {
-    int e = block_table[(size_t)b * W + j];
+    int e = block_table[(size_t)b * W + po + j];
     if (e < 0 || e >= p.P) {
       atomicOr(p.err, PKV_EFLAG_PAGE_BIT);
       e = -1;
@@ -1413,7 +1416,10 @@ __global__ __launch_bounds__(kLongWaves<NRB> * 64) void attn_prefill_kernel(
       const int r = wave * WROWS + rb * 32 + (lane & 31);
       const float ls = tile.lacc[rb][0];
       if (r < r_lo || r >= r_hi) continue;
-      float* dst = p.out + ((size_t)(q_start + tq0 + r / p.group) * p.Hq + g * p.group + r % p.group) * D;
+      const size_t th = (size_t)(q_start + tq0 + r / p.group) * p.Hq + g * p.group + r % p.group;
+      float* dst = p.out + th * D;
+      // the row's base-2 log-sum-exp, for a merge with keys attended elsewhere
+      if (p.out_lse && half == 0) p.out_lse[th] = tile.m[rb] + __log2f(ls);
 #pragma unroll
       for (int mb = 0; mb < Tile::MB; ++mb)
 #pragma unroll

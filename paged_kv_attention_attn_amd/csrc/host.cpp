@@ -115,13 +115,12 @@ pkv::AttnParams attn_params(const void* q, const void* k_pool, const void* v_poo
   return p;
 }
 
-// The shared-prefix call: decode / verify windows only (the tails run the
-// split kernel), and at least one page of every table past the shared ones.
+// The shared-prefix call: at least one page of every table past the shared
+// ones (the tails run the split kernel, or the long-window kernel for windows
+// of more than PKV_MAX_ROWS rows).
 bool shared_shape_ok(const pkv_attn_shape* s, int32_t shared_pages) {
   if (!attn_shape_ok(s) || shared_pages < 0) return false;
   if (shared_pages == 0) return true;
-  const long rows = (long)s->max_q_len * (s->num_q_heads / s->num_kv_heads);
-  if (rows > PKV_MAX_ROWS) return false;
   if (shared_pages >= s->max_pages_per_seq) return false;
   if ((long)s->total_q * (s->num_q_heads / s->num_kv_heads) > (1L << 24)) return false;
   return true;
@@ -319,8 +318,8 @@ int pkv_attn_fwd_shared(const void* q, const void* k_pool, const void* v_pool, c
   if (!workspace || workspace_bytes < L.total) return PKV_ERR_WORKSPACE;
   char* w = static_cast<char*>(workspace);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  // the tails: the split kernel with the shared pages skipped, leaving each
-  // row's log-sum-exp too
+  // the tails: the split kernel (or, for long windows, the long-window
+  // kernel) with the shared pages skipped, leaving each row's log-sum-exp too
   pkv::AttnParams p =
       attn_params(q, k_pool, v_pool, block_table, seq_lens, q_lens, out, s, workspace, L.tail, L.plan, shared_pages);
   p.out_lse = reinterpret_cast<float*>(w + L.lse_off);

@@ -2,8 +2,8 @@
 tables all begin with the same pages attends to them once for every window
 row, then to each sequence's own tail, merged by log-sum-exp. Compared with
 the oracle (which knows nothing of the sharing), on the prefix-dedup
-configuration and on small decode / verify shapes; plus its contract flags
-and repeated calls on one workspace."""
+configuration and on small decode, verify and tail-prefill shapes; plus its
+contract flags and repeated calls on one workspace."""
 
 import numpy as np
 import pytest
@@ -86,6 +86,11 @@ SHAPES = [
     (3, [6, 40, 300], [6, 3, 6], 32, 8, 128),                    # verify windows (24 rows), 8 KV heads
     (2, [16, 500, 77, 1000], [16, 2, 9, 1], 8, 2, 64),           # 64 rows, head_dim 64
     (5, [10] * 70, [1] * 70, 8, 8, 128),                         # one KV head per q head, 70 sequences
+    # windows past the decode / verify kernel: the tails go through the
+    # long-window kernel with the shared pages skipped
+    (2, [300, 40, 600], [300, 20, 150], 8, 2, 128),              # tail prefills (q_len <= tail)
+    (1, [256, 5, 700, 33], [256, 5, 700, 33], 8, 2, 64),         # every tail token a window row
+    (3, [100, 1, 500], [100, 1, 3], 32, 8, 128),                 # long, decode and verify windows mixed
 ]
 
 
@@ -108,6 +113,20 @@ def test_dedup_configuration(pk):
     assert flags == 0
     assert_close(got, oracle_attn(case), "dedup shared")
     assert np.array_equal(got, again)
+
+
+def test_dedup_tail_prefill_through_the_shared_call(pk):
+    """The dedup prefill workload (100 tails of 1..256 tokens, every tail token
+    a window row, over the 16 shared pages) through the shared call: sampled
+    rows against the oracle, repeated calls bit-identical."""
+    from workloads import make_prefill_config
+    from tests.test_gpu_prefill import sample_picks, check_sampled
+    say("shared prefix: dedup tail prefill, 100 tails over 16 shared pages")
+    case = make_prefill_config("dedup")
+    got, again, flags = run_shared(pk, case, 16)
+    assert flags == 0
+    check_sampled(case, got, sample_picks(case, np.random.default_rng(8), 40), "shared dedup prefill")
+    assert np.array_equal(got, again), "repeated call differs"
 
 
 def test_zero_shared_pages_is_the_plain_call(pk):
