@@ -617,7 +617,18 @@ struct MfmaTile {
       const bool g = cmax[rb] > m[rb] + kLazyLog2;
       const float alpha = g ? exp2f_fast(m[rb] - cmax[rb]) : 1.f;
       m[rb] = g ? cmax[rb] : m[rb];
-      lacc[rb] *= alpha;
+      {
+        // every element of lacc[rb] holds the row sum and only element 0 is
+        // read, so only it is rescaled (the others are never used)
+        float x = lacc[rb][0], t;
+        asm volatile(
+            "v_accvgpr_read_b32 %1, %0\n\t"
+            "v_mul_f32 %1, %1, %2\n\t"
+            "v_accvgpr_write_b32 %0, %1"
+            : "+a"(x), "=&v"(t)
+            : "v"(alpha));
+        lacc[rb][0] = x;
+      }
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -645,7 +656,9 @@ struct MfmaTile {
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
       const float mu = (m[rb] == kNegInf) ? 0.f : m[rb];
-      any |= exp2f_fast(cmax[rb] - mu) > kSplitWeight * lacc[rb][0];
+      float ls;  // the row sum, read straight out of its accumulation register
+      asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(ls) : "a"(lacc[rb][0]));
+      any |= exp2f_fast(cmax[rb] - mu) > kSplitWeight * ls;
     }
     return __builtin_amdgcn_ballot_w64(any) != 0;
   }
