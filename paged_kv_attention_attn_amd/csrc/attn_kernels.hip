@@ -1447,14 +1447,16 @@ __global__ __launch_bounds__(kLongWaves<NRB> * 64) void attn_prefill_kernel(
 
 // ------------------------------------------------------ shared-prefix path
 
-// Decode / verify over a batch whose sequences all begin with the same
+// Attention over a batch whose sequences all begin with the same
 // shared_pages pages (a deduplicated prompt prefix, ExLlamaV2 "Dynamic
-// Generator" page, "Deduplication"). The shared keys are attended to once per
-// KV head for every window row of the batch stacked into 256-row MFMA tiles
-// (rows = total_q x group), cut into key splits; each split leaves a partial
-// (reference max, row sum, unnormalised accumulator) per row. The tails run
-// through the split kernel with the shared pages skipped, which also leaves
-// each row's log-sum-exp, and shared_merge_kernel folds the partials in.
+// Generator" page, "Deduplication"). The tails run first, through the split
+// kernel (or the long-window kernel) with the shared pages skipped, and leave
+// each row normalised with its log-sum-exp. The shared keys are then attended
+// to once per KV head for every window row of the batch stacked into 256-row
+// MFMA tiles (rows = total_q x group). With one key split a workgroup merges
+// its rows into the tails' at once; with several, each split leaves a partial
+// (reference max, row sum, unnormalised accumulator) per row and
+// shared_merge_kernel folds them in.
 //
 // Work item = (KV head g, row tile, key split), KV head fastest so that every
 // item of one head lands on one XCD when Hkv is a multiple of 8.
@@ -1514,6 +1516,35 @@ __global__ __launch_bounds__(kLongWaves<NRB> * 64) void attn_shared_kernel(Share
   const int n_chunks = (key_end - key_begin) / 32;
   stream_keys<D, NBUF, NRB>(tile, ring, s_pages, p, Hkv, g, key_begin, key_end, 0, n_chunks, qs.scale_log2);
 
+  // One key split: merge with the tail's row straight away. The tails ran
+  // first and left each row normalised in out with its base-2 log-sum-exp in
+  // out_lse: a partial with row sum 1 at that reference max.
+  if (sp.splits == 1) {
+    const int half = lane >> 5;
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      const int r = wave * WROWS + rb * 32 + (lane & 31);
+      if (r >= r_hi) continue;
+      const int R = rt * kPrefillRows + r;
+      const size_t th = (size_t)(R / p.group) * p.Hq + g * p.group + R % p.group;
+      const float mt = p.out_lse[th], ms = tile.m[rb];
+      const float mx = fmaxf(mt, ms);
+      const float wt = exp2f_fast(mt - mx);
+      const float ws = ms == kNegInf ? 0.f : exp2f_fast(ms - mx);
+      const float inv = 1.f / (wt + ws * tile.lacc[rb][0]);
+      float* o = p.out + th * D;
+#pragma unroll
+      for (int mb = 0; mb < Tile::MB; ++mb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          f32x4* dst = reinterpret_cast<f32x4*>(o + mb * 32 + 8 * j + 4 * half);
+          const f32x4 a = {tile.acc[rb][mb][4 * j], tile.acc[rb][mb][4 * j + 1], tile.acc[rb][mb][4 * j + 2],
+                           tile.acc[rb][mb][4 * j + 3]};
+          *dst = (wt * *dst + ws * a) * inv;
+        }
+    }
+    return;
+  }
   // partials: (m, l) and the unnormalised accumulator of each valid row
   {
     const int half = lane >> 5;

@@ -128,7 +128,7 @@ bool shared_shape_ok(const pkv_attn_shape* s, int32_t shared_pages) {
 
 // Workspace of the shared-prefix call: the tails' attention workspace (planned
 // for the table width past the shared pages), each row's log-sum-exp, and the
-// shared partials.
+// shared partials (none with a single key split).
 struct SharedLayout {
   pkv::AttnWorkspace tail;
   pkv::AttnPlan plan;
@@ -150,10 +150,12 @@ SharedLayout shared_layout(const pkv_attn_shape* s, int32_t shared_pages) {
   L.plan = pkv::attn_plan(s->num_seqs, s->num_kv_heads, tail_w, s->max_q_len, group, tail_pages, 0);
   L.sp = pkv::shared_plan(s->num_kv_heads, s->total_q, group, shared_pages);
   const size_t rows = (size_t)s->total_q * group;
+  // partials only with several key splits (one split merges in place)
+  const size_t parts = L.sp.splits > 1 ? (size_t)s->num_kv_heads * L.sp.splits * rows : 0;
   L.lse_off = align256(L.tail.total);
   L.ml_off = align256(L.lse_off + (size_t)s->total_q * s->num_q_heads * 4);
-  L.acc_off = align256(L.ml_off + (size_t)s->num_kv_heads * L.sp.splits * rows * 2 * 4);
-  L.total = align256(L.acc_off + (size_t)s->num_kv_heads * L.sp.splits * rows * s->head_dim * 4);
+  L.acc_off = align256(L.ml_off + parts * 2 * 4);
+  L.total = align256(L.acc_off + parts * s->head_dim * 4);
   return L;
 }
 
@@ -330,9 +332,10 @@ int pkv_attn_fwd_shared(const void* q, const void* k_pool, const void* v_pool, c
   sp.splits = L.sp.splits;
   sp.split_keys = L.sp.split_keys;
   sp.row_tiles = L.sp.row_tiles;
-  if (pkv::launch_attn_shared(p, sp, st) != hipSuccess) return PKV_ERR_HIP;
+  // tails first: with one key split the shared kernel merges into them
   if (pkv::launch_attn(p, L.plan, st) != hipSuccess) return PKV_ERR_HIP;
-  if (pkv::launch_shared_merge(p, sp, st) != hipSuccess) return PKV_ERR_HIP;
+  if (pkv::launch_attn_shared(p, sp, st) != hipSuccess) return PKV_ERR_HIP;
+  if (sp.splits > 1 && pkv::launch_shared_merge(p, sp, st) != hipSuccess) return PKV_ERR_HIP;
   return PKV_OK;
 }
 

@@ -91,6 +91,9 @@ SHAPES = [
     (2, [300, 40, 600], [300, 20, 150], 8, 2, 128),              # tail prefills (q_len <= tail)
     (1, [256, 5, 700, 33], [256, 5, 700, 33], 8, 2, 64),         # every tail token a window row
     (3, [100, 1, 500], [100, 1, 3], 32, 8, 128),                 # long, decode and verify windows mixed
+    # 8192 stacked rows per KV head: 256 row tiles, so a single key split,
+    # merged into the tails' rows inside the shared kernel
+    (2, [256] * 8, [256] * 8, 32, 8, 128),
 ]
 
 
