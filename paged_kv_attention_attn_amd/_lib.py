@@ -140,13 +140,22 @@ LIB = _load()
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    # a plain int: ctypes converts it for a c_void_p argument
+    return None if t is None else t.data_ptr()
+
+
+# the current device's current stream as a raw handle, without building a
+# torch Stream object on every call (these run once per launch)
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+_get_device = getattr(torch._C, "_cuda_getDevice", None)
 
 
 def _stream(stream):
-    if stream is None:
-        stream = torch.cuda.current_stream()
-    return ctypes.c_void_p(stream.cuda_stream)
+    if stream is not None:
+        return stream.cuda_stream
+    if _raw_stream is not None and _get_device is not None:
+        return _raw_stream(_get_device())
+    return torch.cuda.current_stream().cuda_stream
 
 
 def _check(rc, what):
