@@ -1702,27 +1702,32 @@ int attn_best_pps(int B, int Hkv, int W, int max_q_len, int group, int D, const 
   if (pl.prefill) return 0;
   const long slots = attn_slots(pl);
   // A workgroup's fixed cost (table and q loads before its first page
-  // arrives, the partial stores and merge after its last), in page-stream
+  // arrives, the output or partial stores after its last), in page-stream
   // times: about 11 us against 5 us per 128 KiB page of K and V (head_dim
-  // 128) at a CU's share of the HBM rate.
+  // 128) at a CU's share of the HBM rate. A batch with any sequence cut into
+  // several splits also waits for their merge (the partial stores'
+  // acknowledgement, the count, the last split's loads): about half that.
   const long overhead = D >= 128 ? 2 : 4;
+  const long merge = overhead / 2;
   const int top = W < kMaxPps ? W : kMaxPps;
   long best_cost = -1;
   int best = 1;
   for (int pps = 1; pps <= top; ++pps) {
     long busy = 0;
+    bool split = false;
     for (int b = 0; b < B; ++b) {
       long n = seq_lens[b] > 0 ? seq_lens[b] : 0;
       if (n > (long)W * kPage) n = (long)W * kPage;
       const long pages = (n + kPage - 1) / kPage;
       busy += (pages + pps - 1) / pps;
+      split |= pages > pps;
     }
     busy *= Hkv;
     long rounds = (busy + slots - 1) / slots;
     if (rounds < 1) rounds = 1;
-    // a split's time ~ its pages plus the fixed cost; ties go to longer
-    // splits (fewer partials to merge)
-    const long cost = rounds * (pps + overhead);
+    // a split's time ~ its pages plus the fixed cost (and the merge); ties
+    // go to longer splits (fewer partials to merge)
+    const long cost = rounds * (pps + overhead + (split ? merge : 0));
     if (best_cost < 0 || cost <= best_cost) {
       best_cost = cost;
       best = pps;
