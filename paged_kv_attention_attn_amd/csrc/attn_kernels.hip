@@ -851,7 +851,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_split_kernel(
   constexpr int NI = G::NI;
   constexpr int NC = G::NC;
   constexpr int RP = Tile::RP;
-  static_assert(NBUF >= 2 && NBUF <= 6, "ring depth");
+  static_assert(NBUF >= 1 && NBUF <= 6, "ring depth");
   __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
   __shared__ int s_pages[C::MAX_PPS];
   __shared__ int s_last;
@@ -1634,7 +1634,18 @@ hipError_t launch_d(const AttnParams& p, const AttnPlan& plan, hipStream_t strea
   // staging) four slots still leave two workgroups per CU (Q8 measured no
   // better at three slots than at two)
   constexpr int kValuNbuf = QB == 8 ? PKV_VALU_Q8_NBUF : QB == 4 ? PKV_VALU_Q4_NBUF : PKV_VALU_NBUF;
-  if (!plan.mfma) return launch_one<D, ValuTile<D, 1>, kValuNbuf, PKV_VALU_WAVES, QB>(p, stream);
+  if (!plan.mfma) {
+    // bf16 decode with more items than one round of two-slot rings holds
+    // (the dedup batch, the tails of the shared-prefix call): one-slot rings
+    // fit four workgroups per CU, so the items start in one round, with the
+    // same bytes in flight per CU
+    using Two = KernelCfg<D, ValuTile<D, 1>, kValuNbuf, PKV_VALU_WAVES, QB>;
+    if constexpr (QB == 0 && kValuNbuf == 2) {
+      if ((long)p.num_items > (long)kNumCu * (kLdsPerCu / Two::SMEM))
+        return launch_one<D, ValuTile<D, 1>, 1, PKV_VALU_WAVES, QB>(p, stream);
+    }
+    return launch_one<D, ValuTile<D, 1>, kValuNbuf, PKV_VALU_WAVES, QB>(p, stream);
+  }
   if (plan.rows <= 32) return launch_one<D, MfmaTile<D, 1>, PKV_MFMA_NBUF, PKV_MFMA_WAVES, QB>(p, stream);
   return launch_one<D, MfmaTile<D, 2>, PKV_MFMA_NBUF, PKV_MFMA_WAVES, QB>(p, stream);
 }
