@@ -1064,6 +1064,37 @@ __global__ __launch_bounds__(WAVES * 64) void attn_split_kernel(
     }
     if (n_splits == 1) {
       const int h = g * p.group + r % p.group;
+      if (p.shared_ml) {
+        // the shared prefix's key splits, in order, after this row's own
+        // keys (batches of 8 with every load issued first)
+        constexpr int SB = 8;
+        const size_t rows_all = (size_t)p.total_q * p.group;
+        const size_t R = (size_t)(q_start + r / p.group) * p.group + r % p.group;
+        for (int s0 = 0; s0 < p.shared_splits; s0 += SB) {
+          f32x2 ml[SB];
+          f32x4 pa[SB];
+#pragma unroll
+          for (int j = 0; j < SB; ++j) {
+            const size_t i = ((size_t)g * p.shared_splits + min(s0 + j, p.shared_splits - 1)) * rows_all + R;
+            ml[j] = *reinterpret_cast<const f32x2*>(p.shared_ml + i * 2);
+            pa[j] = *reinterpret_cast<const f32x4*>(p.shared_acc + i * D + 4 * dq);
+          }
+          float Mn = M;
+#pragma unroll
+          for (int j = 0; j < SB; ++j)
+            if (s0 + j < p.shared_splits) Mn = fmaxf(Mn, ml[j].x);
+          const float f = M == kNegInf ? 0.f : exp2f_fast(M - Mn);
+          L *= f;
+          A *= f;
+#pragma unroll
+          for (int j = 0; j < SB; ++j) {
+            const float w = (s0 + j >= p.shared_splits || ml[j].x == kNegInf) ? 0.f : exp2f_fast(ml[j].x - Mn);
+            L += w * ml[j].y;
+            A += w * pa[j];
+          }
+          M = Mn;
+        }
+      }
       *reinterpret_cast<f32x4*>(p.out + ((size_t)(q_start + r / p.group) * p.Hq + h) * D + 4 * dq) = A / L;
       if (p.out_lse && dq == 0) p.out_lse[(size_t)(q_start + r / p.group) * p.Hq + h] = M + __log2f(L);
     } else {

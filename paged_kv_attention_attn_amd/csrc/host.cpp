@@ -332,10 +332,26 @@ int pkv_attn_fwd_shared(const void* q, const void* k_pool, const void* v_pool, c
   sp.splits = L.sp.splits;
   sp.split_keys = L.sp.split_keys;
   sp.row_tiles = L.sp.row_tiles;
-  // tails first: with one key split the shared kernel merges into them
+  if (sp.splits == 1) {
+    // tails first; the shared kernel merges its single split into them
+    if (pkv::launch_attn(p, L.plan, st) != hipSuccess) return PKV_ERR_HIP;
+    return pkv::launch_attn_shared(p, sp, st) != hipSuccess ? PKV_ERR_HIP : PKV_OK;
+  }
+  if (!L.plan.prefill && L.plan.max_splits == 1) {
+    // decode / verify tails of one split each: the shared splits first, then
+    // the tails, which merge them into their rows before writing them
+    if (pkv::launch_attn_shared(p, sp, st) != hipSuccess) return PKV_ERR_HIP;
+    pkv::AttnParams pt = p;
+    pt.out_lse = nullptr;
+    pt.shared_ml = sp.part_ml;
+    pt.shared_acc = sp.part_acc;
+    pt.shared_splits = sp.splits;
+    return pkv::launch_attn(pt, L.plan, st) != hipSuccess ? PKV_ERR_HIP : PKV_OK;
+  }
+  // otherwise: tails, shared splits, then the merge
   if (pkv::launch_attn(p, L.plan, st) != hipSuccess) return PKV_ERR_HIP;
   if (pkv::launch_attn_shared(p, sp, st) != hipSuccess) return PKV_ERR_HIP;
-  if (sp.splits > 1 && pkv::launch_shared_merge(p, sp, st) != hipSuccess) return PKV_ERR_HIP;
+  if (pkv::launch_shared_merge(p, sp, st) != hipSuccess) return PKV_ERR_HIP;
   return PKV_OK;
 }
 

@@ -33,6 +33,12 @@ struct AttnParams {
   float* out_lse;       // nullable: [total_q, Hq] base-2 log-sum-exp of each row's scaled scores
   const float* k_scales;  // quantized caches only: [P, Hkv, 256] per-token scales (k_pool / v_pool hold codes)
   const float* v_scales;
+  // nullable: shared-prefix partials [Hkv][shared_splits][total_q * group] of
+  // (m, l) and [D], merged in split order into each single-split row before
+  // it is written (the shared-prefix call's tails)
+  const float* shared_ml;
+  const float* shared_acc;
+  int32_t shared_splits;
 };
 
 // Workspace layout for a shape (byte offsets from the workspace base).
