@@ -1480,14 +1480,17 @@ __global__ __launch_bounds__(kLongWaves<NRB> * 64) void attn_prefill_kernel(
 
 // Attention over a batch whose sequences all begin with the same
 // shared_pages pages (a deduplicated prompt prefix, ExLlamaV2 "Dynamic
-// Generator" page, "Deduplication"). The tails run first, through the split
-// kernel (or the long-window kernel) with the shared pages skipped, and leave
-// each row normalised with its log-sum-exp. The shared keys are then attended
-// to once per KV head for every window row of the batch stacked into 256-row
-// MFMA tiles (rows = total_q x group). With one key split a workgroup merges
-// its rows into the tails' at once; with several, each split leaves a partial
-// (reference max, row sum, unnormalised accumulator) per row and
-// shared_merge_kernel folds them in.
+// Generator" page, "Deduplication"). The shared keys are attended to once per
+// KV head for every window row of the batch stacked into 256-row MFMA tiles
+// (rows = total_q x group); the tails (each sequence's keys past the shared
+// pages) run through the split kernel or the long-window kernel with the
+// shared pages skipped. The two meet by log-sum-exp in one of three ways
+// (the host picks by the plans): with one key split the tails run first,
+// leaving each row normalised with its log-sum-exp, and a workgroup of this
+// kernel merges its rows into theirs at once; with several key splits each
+// split leaves a partial (reference max, row sum, unnormalised accumulator)
+// per row, folded in by the tails' own epilogue when they run after it with
+// one split each, else by shared_merge_kernel after both.
 //
 // Work item = (KV head g, row tile, key split), KV head fastest so that every
 // item of one head lands on one XCD when Hkv is a multiple of 8.
