@@ -228,6 +228,17 @@ def test_host_plan_counts_pages_and_picks_a_split_length(pk):
     prefill = good_shape(pk, num_seqs=1, max_pages_per_seq=8, total_q=300, max_q_len=300)
     pk.pkv_attn_plan(prefill, [600])
     assert (prefill.total_pages, prefill.pages_per_split) == (3, 0)
+    # a batch far too small to fill the chip keeps whole sequences (a split
+    # would add a merge and shorten nothing): configuration 1's shape
+    tiny = good_shape(pk, num_seqs=1, num_q_heads=8, num_kv_heads=2, head_dim=64, num_pages=16,
+                      max_pages_per_seq=2, total_q=1)
+    pk.pkv_attn_plan(tiny, [300])
+    assert (tiny.total_pages, tiny.pages_per_split) == (2, 2)
+    # and the batched-decode mix (64 sequences of 2-4 pages, 8 KV heads) one
+    # split per sequence: 512 workgroups, two per CU
+    mix = good_shape(pk, num_seqs=64, max_pages_per_seq=4, num_pages=256, total_q=64)
+    pk.pkv_attn_plan(mix, [512 + (37 * i) % 513 for i in range(64)])
+    assert mix.pages_per_split == 4
 
 
 def test_host_plan_rejects_bad_input(pk):
