@@ -911,6 +911,12 @@ __global__ __launch_bounds__(WAVES * 64) void attn_split_kernel(
     }
     s_pages[threadIdx.x] = tbl;
   }
+  // Every load the compiler issued itself has landed by now (the table
+  // entries were just used). A wait it can see says so: otherwise, before it
+  // reuses the registers those loads targeted, it inserts vmcnt(0), which also
+  // counts the direct q and K/V loads below and would hold the first K/V
+  // chunk back until the q rows landed.
+  __builtin_amdgcn_s_waitcnt(kVmcnt0);
   const int rows = q_len * p.group;  // <= RP by the plan
   __syncthreads();
 

@@ -235,6 +235,10 @@ __device__ __forceinline__ RowPrefix row_prefix(const int32_t* q_lens, int b, in
 
 constexpr int kSc1 = 16;  // cache-policy bit: coherent across XCDs (write-through / miss)
 
+// s_waitcnt immediate for vmcnt(0) alone (gfx9 encoding: vmcnt in bits 3:0
+// and 15:14, expcnt 6:4 and lgkmcnt 11:8 at their maxima)
+constexpr int kVmcnt0 = 0x0F70;
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, u32 bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
 }
