@@ -269,9 +269,9 @@ typedef struct {
 } pkv_accept_shape;
 
 /* Bytes of device workspace pkv_accept needs (0 on a bad shape). It holds one
- * 64-bit argmax key and a finish counter per logits row; it must be
- * zero-filled before its first use, and every call leaves it zero again (so
- * it can serve any later shape with no more rows). */
+ * 64-bit argmax key per chunk of each logits row; it must be zero-filled
+ * before its first use, and every call leaves it zero again (so it can serve
+ * any later shape whose workspace is no larger). */
 size_t pkv_accept_workspace_bytes(const pkv_accept_shape* shape);
 
 /*

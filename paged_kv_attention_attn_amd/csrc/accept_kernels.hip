@@ -10,20 +10,21 @@
 //
 // One kernel. Its workgroups scan row chunks (an HBM-bound fp32 stream; one
 // row alone is far too small to fill the chip) and store each chunk's best
-// (value, index) as a 64-bit key. Each then counts itself finished; the
-// workgroup that counts last takes the largest chunk key of every row,
-// applies the accept rule and the window update, and clears the keys and
-// counters for the next call.
+// (value, index) as a 64-bit key, which is never zero, into the chunk's slot.
+// The last workgroup of the grid, which the dispatcher starts after every
+// other one, polls the slots until every key has arrived, takes the largest
+// chunk key of every row, applies the accept rule and the window update, and
+// clears the slots for the next call. No workgroup waits for its own store
+// and nothing is counted, so the chain after the stream is one memory round
+// trip: the last key's store, seen by the next poll.
 //
-// Ordering. Chunk keys and counters are only touched by agent-scope atomic
-// read-modify-writes (exchanges, adds, and maxima with 0 to read a key that
-// is read twice), and the hardware performs the atomics on one address at one place for
-// every XCD, one after another. A workgroup counts only once its key
-// exchange has returned (so has been performed), and the last workgroup
-// reads the keys only once its own count has returned; so every key read
-// comes after every key write. This is the release / acquire order of the
-// language's model without its L2-wide write-back and invalidate, which only
-// non-atomic data would need.
+// Ordering. The slots are only touched by agent-scope atomics (stores,
+// loads, exchanges, and maxima with 0 to read a key that is read twice), and
+// the hardware performs the atomics on one address at one place for every
+// XCD, one after another; a key is read only once it has been seen, so every
+// key read comes after its write, and the slots are zero again before the
+// call ends. Only these slots carry data between workgroups, so none of the
+// language model's L2-wide write-back and invalidate is needed.
 //
 // argmax order: larger value first; NaN above every number; lower index on
 // equal values (and between NaNs); -0 equals +0. The key encodes exactly this
@@ -51,7 +52,6 @@ constexpr int kArgUnroll = 8;                 // float4 loads in flight per thre
 #define PKV_ARG_TARGET_WGS 768
 #endif
 constexpr int kArgTargetWgs = PKV_ARG_TARGET_WGS;  // about three workgroups per CU
-constexpr int kCountStride = 32;  // u32 words between row counters: one 128-byte line each
 
 // (a, ia) ranks before (b, ib): the larger value, a NaN above every number,
 // the lower index on equal values (and between NaNs). Branch-free.
@@ -119,6 +119,48 @@ __device__ __forceinline__ int wave_scan(int x) {
   return x;
 }
 
+// Key of a chunk with no element: below every pair, and not zero, which
+// marks a slot whose key has not arrived.
+constexpr u64 kEmptyKey = 1;
+// Polls of one slot before the last workgroup gives up on it: each is a
+// memory round trip, so this is far beyond any real call.
+constexpr int kMaxPolls = 1 << 20;
+constexpr int kPollBatch = 4;  // slots polled at once per thread
+
+// Run by the last workgroup: polls every chunk key of the call until it has
+// arrived (slots are zero between calls and keys never are), calling
+// take(e, key) once per slot e as it is first seen, each thread for its own
+// slots, several at a time. Returns false if some key did not arrive within
+// kMaxPolls polls.
+template <class Take>
+__device__ __forceinline__ bool take_keys(const AcceptParams& p, Take take) {
+  const int ns = p.total_rows * p.chunks;
+  bool ok = true;
+  for (int e0 = 0; e0 < ns; e0 += kPollBatch * kArgThreads) {
+    u32 pending = 0;
+#pragma unroll
+    for (int u = 0; u < kPollBatch; ++u)
+      if (e0 + u * kArgThreads + (int)threadIdx.x < ns) pending |= 1u << u;
+    for (int it = 0; pending != 0 && it < kMaxPolls; ++it) {
+      u64 x[kPollBatch];
+#pragma unroll
+      for (int u = 0; u < kPollBatch; ++u)
+        x[u] = (pending >> u) & 1u ? __hip_atomic_load(p.slots + e0 + u * kArgThreads + threadIdx.x,
+                                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                   : 0ull;
+#pragma unroll
+      for (int u = 0; u < kPollBatch; ++u)
+        if (((pending >> u) & 1u) && x[u] != 0ull) {
+          pending &= ~(1u << u);
+          take(e0 + u * kArgThreads + (int)threadIdx.x, x[u]);
+        }
+      if (pending != 0) __builtin_amdgcn_s_sleep(1);
+    }
+    ok = ok && pending == 0;
+  }
+  return ok;
+}
+
 // Chunk key of (row, chunk), read by the last workgroup.
 __device__ __forceinline__ u64 read_slot(const AcceptParams& p, int r, int c) {
   // a max with 0 leaves the key as it is
@@ -129,7 +171,8 @@ __device__ __forceinline__ u64 read_slot(const AcceptParams& p, int r, int c) {
 __device__ __forceinline__ u64 row_key(const AcceptParams& p, int r) {
   u64 k = 0;
   for (int c = 0; c < p.chunks; ++c) {
-    const u64 x = read_slot(p, r, c);
+    u64 x = read_slot(p, r, c);
+    x = x == kEmptyKey ? 0ull : x;
     k = x > k ? x : k;
   }
   return k;
@@ -182,27 +225,20 @@ __device__ void accept_rule_small(const AcceptParams& p) {
   __shared__ int s_wsum[kWaves];
   __shared__ u64 s_keys[kArgThreads];
   __shared__ int s_draft[kArgThreads];
+  __shared__ int s_ok;
   const int n = t < p.B ? p.n_draft[t] : 0;
   const int w_old = (t < p.B && p.window) ? p.window[t] : 0;
   const int d = t < p.total_rows - p.B ? p.draft_ids[t] : 0;
-  const int ns = p.total_rows * p.chunks;
-  u64 x[4];
-  for (int e0 = 0; e0 < ns; e0 += 4 * kArgThreads) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int e = e0 + u * kArgThreads + t;
-      x[u] = e < ns ? __hip_atomic_exchange(p.slots + e, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
-    }
-    if (e0 == 0) {
-      s_keys[t] = 0;
-      lds_barrier();
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int e = e0 + u * kArgThreads + t;
-      if (e < ns) atomicMax(&s_keys[e / p.chunks], x[u]);
-    }
-  }
+  s_keys[t] = 0;
+  if (t == 0) s_ok = 1;
+  lds_barrier();
+  // each key is taken into its row's maximum as soon as it is seen, and its
+  // slot cleared for the next call
+  const bool ok = take_keys(p, [&](int e, u64 x) {
+    atomicMax(&s_keys[e / p.chunks], x == kEmptyKey ? 0ull : x);
+    __hip_atomic_store(p.slots + e, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  });
+  if (!ok) s_ok = 0;
   s_draft[t] = d;
   const int inc = wave_scan(t < p.B ? n + 1 : 0);
   if (lane == 63) s_wsum[wave] = inc;
@@ -211,6 +247,11 @@ __device__ void accept_rule_small(const AcceptParams& p) {
   int before = 0;
   for (int w = 0; w < wave; ++w) before += s_wsum[w];
   const int r0 = before + inc - (n + 1);  // first row of sequence t
+  if (!s_ok) {  // a chunk key that never came: the contract-break outputs
+    p.out_accept[t] = 0;
+    p.out_next[t] = -1;
+    return;
+  }
   decide(p, t, n, w_old, r0, r0 - t, [&](int r) { return s_keys[r]; }, [&](int i) { return s_draft[i]; });
 }
 
@@ -222,7 +263,13 @@ __device__ void accept_rule_tiled(const AcceptParams& p) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   __shared__ int s_wsum[kWaves];
   __shared__ int s_carry;
-  if (threadIdx.x == 0) s_carry = 0;
+  __shared__ int s_ok;
+  if (threadIdx.x == 0) {
+    s_carry = 0;
+    s_ok = 1;
+  }
+  lds_barrier();
+  if (!take_keys(p, [](int, u64) {})) s_ok = 0;
   lds_barrier();
   for (int t0 = 0; t0 < p.B; t0 += kArgThreads) {
     const int b = t0 + threadIdx.x;
@@ -234,9 +281,13 @@ __device__ void accept_rule_tiled(const AcceptParams& p) {
     int before = s_carry;
     for (int w = 0; w < wave; ++w) before += s_wsum[w];
     const int r0 = before + inc - (n + 1);  // first row of sequence b
-    if (b < p.B)
+    if (b < p.B && !s_ok) {
+      p.out_accept[b] = 0;
+      p.out_next[b] = -1;
+    } else if (b < p.B) {
       decide(p, b, n, w_old, r0, r0 - b, [&](int r) { return row_key(p, r); },
              [&](int i) { return p.draft_ids[i]; });
+    }
     lds_barrier();
     if (threadIdx.x == kArgThreads - 1) s_carry = before + inc;
     lds_barrier();
@@ -258,7 +309,6 @@ __global__ __launch_bounds__(kArgThreads) void accept_kernel(
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   __shared__ float sv[kArgThreads / 64];
   __shared__ int si[kArgThreads / 64];
-  __shared__ int s_last;
 
   const int begin = c * chunk_len;
   const int end = min(V, begin + chunk_len);
@@ -296,29 +346,14 @@ __global__ __launch_bounds__(kArgThreads) void accept_kernel(
     float v = lane < kArgThreads / 64 ? sv[lane] : -__builtin_inff();
     int i = lane < kArgThreads / 64 ? si[lane] : INT_MAX;
     wave_best(v, i);
-    if (lane == 0) {
-      // The chunk's key has been exchanged in (the old value returned)
-      // before the chunk is counted, and counts go in two levels (the
-      // chunks of a row, then the rows) so that few atomics meet on one
-      // address.
-      const u64 was = __hip_atomic_exchange(p.slots + (size_t)r * gridDim.x + c, i != INT_MAX ? argmax_key(v, i) : 0ull,
-                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      asm volatile("s_waitcnt vmcnt(0)" ::"v"(was) : "memory");
-      uint32_t* row_count = p.row_done + (size_t)r * kCountStride;
-      bool last = __hip_atomic_fetch_add(row_count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1;
-      if (last) {
-        // every chunk of the row has counted: reset its counter for the next call
-        __hip_atomic_exchange(row_count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        last = __hip_atomic_fetch_add(p.done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gridDim.y - 1;
-      }
-      s_last = last;
-    }
+    // the chunk's key, nonzero; nothing waits for it here
+    if (lane == 0)
+      __hip_atomic_store(p.slots + (size_t)r * gridDim.x + c, i != INT_MAX ? argmax_key(v, i) : kEmptyKey,
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  lds_barrier();
-  if (!s_last) return;
-  // the row counters were reset by each row's last workgroup; the chunk keys
-  // are cleared by the rule; the row count is reset here
-  if (threadIdx.x == 0) __hip_atomic_exchange(p.done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // The last workgroup of the grid, dispatched after every other one, waits
+  // for every chunk key and applies the rule (it clears the keys).
+  if (c != (int)gridDim.x - 1 || r != (int)gridDim.y - 1) return;
   if (p.total_rows <= kArgThreads)
     accept_rule_small(p);
   else
@@ -384,11 +419,9 @@ AcceptWorkspace accept_workspace(int B, int total_rows, int V) {
   len = (len + 3) / 4 * 4;
   ws.chunk_len = (int)len;
   ws.chunks = (int)((V + len - 1) / len);
-  // counters, then chunk keys; all zero between calls
-  ws.done_off = 0;
-  ws.rows_off = 256;
-  ws.slots_off = ws.rows_off + (size_t)total_rows * kCountStride * 4;
-  ws.total = ws.slots_off + ((size_t)total_rows * ws.chunks * 8 + 255) / 256 * 256;
+  // the chunk keys, zero between calls
+  ws.slots_off = 0;
+  ws.total = ((size_t)total_rows * ws.chunks * 8 + 255) / 256 * 256;
   return ws;
 }
 

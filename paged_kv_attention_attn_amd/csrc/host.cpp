@@ -401,8 +401,6 @@ static int accept_launch(const float* logits, const int32_t* draft_ids, const in
   p.out_next = out_next;
   p.window = window;
   p.slots = reinterpret_cast<unsigned long long*>(w + ws.slots_off);
-  p.done = reinterpret_cast<uint32_t*>(w + ws.done_off);
-  p.row_done = reinterpret_cast<uint32_t*>(w + ws.rows_off);
   p.B = s->num_seqs;
   p.V = s->vocab;
   p.total_rows = s->total_rows;

@@ -94,14 +94,12 @@ struct AcceptParams {
   int32_t* out_accept;
   int32_t* out_next;
   int32_t* window;              // nullable
-  unsigned long long* slots;    // [total_rows][chunks] argmax key of each row chunk
-  uint32_t* done;               // rows finished; zero between calls
-  uint32_t* row_done;           // [total_rows] chunks finished per row, one 128-byte line each; zero between calls
+  unsigned long long* slots;    // [total_rows][chunks] argmax key of each row chunk; zero between calls
   int32_t B, V, total_rows, max_draft, chunks, chunk_len;
 };
 
 struct AcceptWorkspace {
-  size_t done_off, rows_off, slots_off, total;
+  size_t slots_off, total;
   int chunks, chunk_len;
 };
 
