@@ -124,7 +124,8 @@ def test_bad_accept_shapes_are_rejected(pk, bad):
 def test_accept_workspace_and_nulls(pk):
     s = pk.pkv_accept_shape(8, 128256, 48, 5)
     need = pk.pkv_accept_workspace_bytes(s)
-    assert need >= 48 * 8
+    # one 8-byte key per (row, chunk): 16 chunks of 8016 logits per row here
+    assert need == 48 * 16 * 8
     dummy = ctypes.c_void_p(0x1000)
     rc = pk.LIB.pkv_accept(dummy, dummy, dummy, dummy, dummy, None, ctypes.byref(s), dummy, need - 1,
                            None)
