@@ -292,7 +292,11 @@ size_t pkv_accept_workspace_bytes(const pkv_accept_shape* shape);
  * argmax: lowest index among equal maxima; a NaN counts as the maximum and the
  * first NaN wins. Results are bit-exact.
  * A sequence whose rows or drafts break the contract gets out_accept = 0 and
- * out_next = -1. One call at a time per workspace.
+ * out_next = -1. One call at a time per workspace. The call's last workgroup
+ * waits for the others' chunk results; if they have not all arrived after
+ * about 10 seconds (other work holding the GPU's compute units all that
+ * time), every sequence gets out_accept = 0, out_next = -1 and the workspace
+ * must be zero-filled again before its next use.
  * Contract: sum(n_draft + 1) == total_rows; n_draft[b] <= max_draft.
  */
 int pkv_accept(const float* logits, const int32_t* draft_ids, const int32_t* n_draft,

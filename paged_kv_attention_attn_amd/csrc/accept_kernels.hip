@@ -122,26 +122,29 @@ __device__ __forceinline__ int wave_scan(int x) {
 // Key of a chunk with no element: below every pair, and not zero, which
 // marks a slot whose key has not arrived.
 constexpr u64 kEmptyKey = 1;
-// Polls of one slot before the last workgroup gives up on it: each is a
-// memory round trip, so this is far beyond any real call.
-constexpr int kMaxPolls = 1 << 20;
+// How long the last workgroup polls for a key before it gives up: 2^30 ticks
+// of the constant-rate wall clock (about 11 s at its 100 MHz), far beyond any
+// call, also while other streams' kernels hold CUs that the call's other
+// workgroups still wait for.
+constexpr long long kPollTicks = 1ll << 30;
 constexpr int kPollBatch = 4;  // slots polled at once per thread
 
 // Run by the last workgroup: polls every chunk key of the call until it has
 // arrived (slots are zero between calls and keys never are), calling
 // take(e, key) once per slot e as it is first seen, each thread for its own
 // slots, several at a time. Returns false if some key did not arrive within
-// kMaxPolls polls.
+// kPollTicks.
 template <class Take>
 __device__ __forceinline__ bool take_keys(const AcceptParams& p, Take take) {
   const int ns = p.total_rows * p.chunks;
+  const long long t0 = wall_clock64();
   bool ok = true;
   for (int e0 = 0; e0 < ns; e0 += kPollBatch * kArgThreads) {
     u32 pending = 0;
 #pragma unroll
     for (int u = 0; u < kPollBatch; ++u)
       if (e0 + u * kArgThreads + (int)threadIdx.x < ns) pending |= 1u << u;
-    for (int it = 0; pending != 0 && it < kMaxPolls; ++it) {
+    while (pending != 0 && wall_clock64() - t0 < kPollTicks) {
       u64 x[kPollBatch];
 #pragma unroll
       for (int u = 0; u < kPollBatch; ++u)
