@@ -11,10 +11,11 @@
 // One kernel. Its workgroups scan row chunks (an HBM-bound fp32 stream; one
 // row alone is far too small to fill the chip) and store each chunk's best
 // (value, index) as a 64-bit key, which is never zero, into the chunk's slot.
-// The last workgroup of the grid, which the dispatcher starts after every
-// other one, polls the slots until every key has arrived, takes the largest
-// chunk key of every row, applies the accept rule and the window update, and
-// clears the slots for the next call. No workgroup waits for its own store
+// The last workgroup of the grid (so started after every other one) polls
+// the slots until every key has arrived, takes the largest chunk key of every
+// row, applies the accept rule and the window update, and clears the slots
+// for the next call; on large grids it is a workgroup of its own, which
+// scans nothing. No workgroup waits for its own store
 // and nothing is counted, so the chain after the stream is one memory round
 // trip: the last key's store, seen by the next poll.
 //
@@ -52,6 +53,7 @@ constexpr int kArgUnroll = 8;                 // float4 loads in flight per thre
 #define PKV_ARG_TARGET_WGS 768
 #endif
 constexpr int kArgTargetWgs = PKV_ARG_TARGET_WGS;  // about three workgroups per CU
+constexpr long kChipCus = 256;                     // MI355X compute units
 
 // (a, ia) ranks before (b, ib): the larger value, a NaN above every number,
 // the lower index on equal values (and between NaNs). Branch-free.
@@ -300,15 +302,32 @@ __device__ void accept_rule_tiled(const AcceptParams& p) {
     __hip_atomic_exchange(p.slots + e, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Workgroup (c, r): chunk c of logits row r. Every load of a thread is issued
-// before any is consumed; the chunk's best pair is stored as its chunk key,
-// and the workgroup that finishes last applies the accept rule.
+// The rule, in one workgroup: it waits for every chunk key first.
+__device__ __forceinline__ void accept_rule(const AcceptParams& p) {
+  if (p.total_rows <= kArgThreads)
+    accept_rule_small(p);
+  else
+    accept_rule_tiled(p);
+}
+
+// Workgroup (c, r), r < rows: chunk c of logits row r. Every load of a
+// thread is issued before any is consumed; the chunk's best pair is stored as
+// its chunk key. The rule runs in a workgroup that the dispatcher starts after
+// every chunk workgroup. With own_rule the grid has one row more, whose first
+// workgroup scans nothing and polls from its start (the others end at once):
+// on grids larger than one round of the chip the chunk workgroups start over
+// microseconds, and the last of them starts last. Otherwise the last chunk
+// workgroup scans its chunk and then applies the rule.
 template <bool VEC4>
 __global__ __launch_bounds__(kArgThreads) void accept_kernel(
     // leading scalars, preloaded into SGPRs at wave launch
-    const float* __restrict__ logits, int V, int chunk_len, AcceptParams p) {
+    const float* __restrict__ logits, int V, int chunk_len, int own_rule, AcceptParams p) {
   const int c = blockIdx.x;
   const int r = blockIdx.y;
+  if (own_rule && r == (int)gridDim.y - 1) {
+    if (c == 0) accept_rule(p);
+    return;
+  }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   __shared__ float sv[kArgThreads / 64];
   __shared__ int si[kArgThreads / 64];
@@ -354,13 +373,7 @@ __global__ __launch_bounds__(kArgThreads) void accept_kernel(
       __hip_atomic_store(p.slots + (size_t)r * gridDim.x + c, i != INT_MAX ? argmax_key(v, i) : kEmptyKey,
                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  // The last workgroup of the grid, dispatched after every other one, waits
-  // for every chunk key and applies the rule (it clears the keys).
-  if (c != (int)gridDim.x - 1 || r != (int)gridDim.y - 1) return;
-  if (p.total_rows <= kArgThreads)
-    accept_rule_small(p);
-  else
-    accept_rule_tiled(p);
+  if (!own_rule && c == (int)gridDim.x - 1 && r == (int)gridDim.y - 1) accept_rule(p);
 }
 
 // Fills n 32-bit words with zero (a kernel, not a memset, so that a caller
@@ -430,13 +443,18 @@ AcceptWorkspace accept_workspace(int B, int total_rows, int V) {
 
 hipError_t launch_accept(const AcceptParams& p, hipStream_t stream) {
   if (p.B == 0 || p.total_rows == 0) return hipSuccess;
-  dim3 grid(p.chunks, p.total_rows);
+  // one workgroup per (row, chunk); past one round of the chip, a row more
+  // for the rule
+  const int own_rule = (long)p.chunks * p.total_rows > kChipCus && p.total_rows < 65535 ? 1 : 0;
+  const dim3 grid(p.chunks, p.total_rows + own_rule);
   const bool vec4 = p.V % 4 == 0 && (reinterpret_cast<uintptr_t>(p.logits) & 15) == 0 &&
                     p.chunk_len <= kArgThreads * kArgUnroll * 4;
   if (vec4)
-    hipLaunchKernelGGL(accept_kernel<true>, grid, dim3(kArgThreads), 0, stream, p.logits, p.V, p.chunk_len, p);
+    hipLaunchKernelGGL(accept_kernel<true>, grid, dim3(kArgThreads), 0, stream, p.logits, p.V, p.chunk_len,
+                       own_rule, p);
   else
-    hipLaunchKernelGGL(accept_kernel<false>, grid, dim3(kArgThreads), 0, stream, p.logits, p.V, p.chunk_len, p);
+    hipLaunchKernelGGL(accept_kernel<false>, grid, dim3(kArgThreads), 0, stream, p.logits, p.V, p.chunk_len,
+                       own_rule, p);
   return hipGetLastError();
 }
 
