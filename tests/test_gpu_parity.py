@@ -198,6 +198,32 @@ def test_accept_workspace_is_clean_after_each_call(pk):
         np.testing.assert_array_equal(on.cpu().numpy(), en)
 
 
+@pytest.mark.parametrize("q_lens", [[6, 6, 4], [6, 6, 5], [1]])
+def test_accept_on_either_side_of_the_rule_workgroup(pk, q_lens):
+    """16 rows x 16 chunks of a 32768-wide vocabulary make 256 chunk
+    workgroups, whose last one applies the rule after its own chunk; 17 rows
+    (272) add a workgroup that only applies the rule; one row is the small
+    case. Each matches the oracle bit for bit, twice in a row on one
+    workspace."""
+    say(f"accept: rows {sum(q_lens)} over a 32768-wide vocabulary")
+    import torch
+    acc = make_accept_case(31 + len(q_lens), q_lens, 32768)
+    logits = torch.from_numpy(np.ascontiguousarray(acc.logits)).cuda()
+    drafts = dev_i32(acc.draft_ids) if acc.draft_ids.size else torch.empty(0, dtype=torch.int32, device="cuda")
+    nd = dev_i32(acc.n_draft)
+    shape = pk.accept_shape(logits, nd, acc.max_draft)
+    ws = pk.new_accept_workspace(shape)
+    ea, en, _ = oracle.accept(acc.logits, acc.draft_ids, acc.n_draft)
+    for _ in range(2):
+        oa = torch.full((acc.num_seqs,), -7, dtype=torch.int32, device="cuda")
+        on = torch.full_like(oa, -7)
+        pk.pkv_accept(logits, drafts, nd, oa, on, None, shape, ws)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(oa.cpu().numpy(), ea)
+        np.testing.assert_array_equal(on.cpu().numpy(), en)
+        np.testing.assert_array_equal(oa.cpu().numpy(), acc.planted_match + 1)
+
+
 @pytest.mark.skip(reason="its one run against the two-level accept kernel ended in a GPU memory fault whose "
                          "cause reading the kernel and a CPU emulation of its indexing have not shown (every "
                          "global access of the rule is bounded by B or the row count, not by n_draft); it "
