@@ -1676,9 +1676,11 @@ hipError_t launch_d(const AttnParams& p, const AttnPlan& plan, hipStream_t strea
   constexpr int kValuNbuf = QB == 8 ? PKV_VALU_Q8_NBUF : QB == 4 ? PKV_VALU_Q4_NBUF : PKV_VALU_NBUF;
   if (!plan.mfma) {
     // bf16 decode with more items than one round of two-slot rings holds
-    // (the dedup batch, the tails of the shared-prefix call): one-slot rings
-    // fit four workgroups per CU, so the items start in one round, with the
-    // same bytes in flight per CU
+    // (the dedup batch, the tails of the shared-prefix call): one-slot rings.
+    // The tile's registers keep two workgroups per CU at head_dim 128 either
+    // way (three at 64), so such batches still take more than one round; with
+    // half the chunks in flight per wave they measured faster on both (the
+    // dedup batch reads its shared pages through one L2 per XCD)
     using Two = KernelCfg<D, ValuTile<D, 1>, kValuNbuf, PKV_VALU_WAVES, QB>;
     if constexpr (QB == 0 && kValuNbuf == 2) {
       if ((long)p.num_items > (long)kNumCu * (kLdsPerCu / Two::SMEM))
