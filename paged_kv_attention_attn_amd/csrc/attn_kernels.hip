@@ -55,6 +55,7 @@ struct ValuTile {
   static constexpr int RP = 4 * RPL;  // padded rows
   static constexpr int STEPS = TC / TG;
   static constexpr int PBUF = TC * RP * 4;  // P staging bytes per wave
+  static constexpr int MS = D;              // row stride (floats) of the waves' merge area
   static constexpr bool kVDirect = true;    // quantized caches: V converted straight from its codes
   static constexpr float kSplitWeight = 1.f / 8.f;  // the MFMA tile's two-term threshold
   static constexpr float kLazyLog2 = 8.f;           // reference-max slack, as on the long-window tile
@@ -331,6 +332,10 @@ struct MfmaTile {
   static constexpr int MB = D / 32;  // 32-dim blocks of the output
   static constexpr int RP = 32 * NRB;
   static constexpr int PBUF = 0;
+  // row stride (floats) of the waves' merge area: one row per lane, so a
+  // stride of D would put every lane of a store on the same bank; 4 more
+  // floats move each row by four banks
+  static constexpr int MS = D + 4;
   static constexpr bool kVDirect = false;  // quantized caches: V staged as bf16 like K
 
   u32x4 qb[NRB][KK];
@@ -463,39 +468,72 @@ struct MfmaTile {
     // this lane holds tokens 8*(i/4) + 4*half + i%4 of q row `row`
     u32x4 pb[NRB][2];
     float p[NRB][16];
-    bool heavy = false;
+    float x[NRB][16], cm[NRB];
+    bool grow = false;
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
-      float x[16];
-      float cm = kNegInf;
+      cm[rb] = kNegInf;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int tt = 8 * (i >> 2) + 4 * half + (i & 3);
         const float ksl = QB != 0 ? qsc[tt] * (scale_log2 * kStageFactor<QB>) : scale_log2;
-        x[i] = (tok0 + tt <= lim[rb] && tt < nv) ? S[rb][i] * ksl : kNegInf;
-        cm = fmaxf(cm, x[i]);
+        x[rb][i] = (tok0 + tt <= lim[rb] && tt < nv) ? S[rb][i] * ksl : kNegInf;
+        cm[rb] = fmaxf(cm[rb], x[rb][i]);
       }
-      cm = max_xor32(cm);
-      const float mn = fmaxf(m[rb], cm);
-      const float mu = (mn == kNegInf) ? 0.f : mn;
-      const float alpha = exp2f_fast(m[rb] - mu);
+      cm[rb] = max_xor32(cm[rb]);
+      grow |= cm[rb] > m[rb] + kLazyLog2;
+    }
+    // Lazy rescale: a row keeps its reference max m while the chunk stays
+    // below m + kLazyLog2, so P = 2^(x - m) may reach 2^kLazyLog2 and the
+    // softmax ratio is unchanged; only a row that outgrows it moves m and
+    // rescales its sum and O^T (rare after the first chunk).
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      // O^T stays in the accumulation registers: read, multiply and write
+      // back each element in place (a plain multiply would make the compiler
+      // keep a VALU-side copy of O^T across the chunk loop). The s_nop runs
+      // cover the matrix-core result latency before the first read and the
+      // write-to-operand latency after the last write.
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::: "memory");
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) {
+        const bool gr = cm[rb] > m[rb] + kLazyLog2;
+        const float alpha = gr ? exp2f_fast(m[rb] - cm[rb]) : 1.f;
+        m[rb] = gr ? cm[rb] : m[rb];
+        l[rb] *= alpha;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            float v = acc[rb][mb][i], t;
+            asm volatile(
+                "v_accvgpr_read_b32 %1, %0\n\t"
+                "v_mul_f32 %1, %1, %2\n\t"
+                "v_accvgpr_write_b32 %0, %1"
+                : "+a"(v), "=&v"(t)
+                : "v"(alpha));
+            acc[rb][mb][i] = v;
+          }
+      }
+      asm volatile("s_nop 3" ::: "memory");
+    }
+    bool heavy = false;
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      const float mu = (m[rb] == kNegInf) ? 0.f : m[rb];
       float ps = 0.f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        p[rb][i] = exp2f_fast(x[i] - mu);
+        p[rb][i] = exp2f_fast(x[rb][i] - mu);
         ps += p[rb][i];
       }
-      l[rb] = l[rb] * alpha + ps;
-      m[rb] = mn;
+      l[rb] += ps;
       // a key of this chunk weighing more than kSplitWeight of its row's sum
       // so far (both halves of the row): its bf16 P would not average out
-      heavy |= cm != kNegInf && exp2f_fast(cm - mu) > kSplitWeight * sum_xor32(l[rb]);
+      heavy |= cm[rb] != kNegInf && exp2f_fast(cm[rb] - mu) > kSplitWeight * sum_xor32(l[rb]);
       if constexpr (QB != 0) {  // P.V weights carry the V scales
 #pragma unroll
         for (int i = 0; i < 16; ++i) p[rb][i] *= qsc[64 + 8 * (i >> 2) + 4 * half + (i & 3)] * kStageFactor<QB>;
       }
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) acc[rb][mb] *= alpha;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         pb[rb][ks].x = pack_bf16(p[rb][8 * ks + 0], p[rb][8 * ks + 1]);
@@ -737,9 +775,10 @@ struct MfmaTile {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int d = mb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-          racc[r * D + d] = acc[rb][mb][i];
+        for (int j = 0; j < 4; ++j) {
+          const int d = mb * 32 + 8 * j + 4 * half;
+          *reinterpret_cast<f32x4*>(racc + r * MS + d) =
+              f32x4{acc[rb][mb][4 * j], acc[rb][mb][4 * j + 1], acc[rb][mb][4 * j + 2], acc[rb][mb][4 * j + 3]};
         }
     }
   }
@@ -773,7 +812,7 @@ struct KernelCfg {
   static constexpr int QB = (Tile::RP * D * 2 + 1023) / 1024 * 1024;  // whole 1 KiB loads
   static constexpr int NQI = QB / 1024;                  // q load instructions per workgroup
   static constexpr int STAGE = WAVES * (RING + Tile::PBUF) + QB;
-  static constexpr int MERGE = WAVES * Tile::RP * (D + 2) * 4;
+  static constexpr int MERGE = WAVES * Tile::RP * (Tile::MS + 2) * 4;
   static constexpr int SMEM = STAGE > MERGE ? STAGE : MERGE;
   static constexpr int MAX_PPS = 64;
 };
@@ -837,7 +876,18 @@ __device__ __forceinline__ void q_decode_slot(const char* slot, char* stg) {
   }
 }
 
-template <int D, class Tile, int NBUF, int WAVES, int QB = 0>
+// SHR: the shared-prefix call's shared keys on few rows (decode and verify
+// batches). Work item = (KV head g, tile of RP stacked batch rows, split s of
+// the shared pages), KV head fastest so that every item of one head lands on
+// one XCD when Hkv is a multiple of 8. Rows are the batch's window rows times
+// the head group, stacked (row R: window row R / group, q head g * group +
+// R % group); every row sees every shared key, so nothing is masked. The
+// split's table entries are sequence 0's; the grid checks that every table
+// starts with them and that every window lies past them. Each item leaves
+// its rows' partial (m, l, acc) in part_ml / part_acc, laid out
+// [Hkv][splits][total_q * group], for the tails to merge. pps = shared pages
+// per split, max_splits = the splits, page_offset = the shared pages.
+template <int D, class Tile, int NBUF, int WAVES, int QB = 0, bool SHR = false>
 __global__ __launch_bounds__(WAVES * 64) void attn_split_kernel(
     // leading scalars: what the first loads need, preloaded into SGPRs at
     // wave launch instead of read from the argument buffer
@@ -863,62 +913,99 @@ __global__ __launch_bounds__(WAVES * 64) void attn_split_kernel(
   // gets the same mix of early splits (work for every sequence) and late ones
   // (only long sequences have them); and a ragged batch's empty items come
   // last in each XCD's queue.
-  const int pairs = num_items / B;
-  const int xcd = blockIdx.x % kNumXcd, k = blockIdx.x / kNumXcd;
-  const int b = k % B;
-  const int j = xcd + kNumXcd * (k / B);
-  if (j >= pairs) return;
-  const int g = j % Hkv;
-  const int s = j / Hkv;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-
-  // independent loads first, so their latencies overlap: the sequence's
-  // lengths, the split's table entries and the window-row prefix sum
-  // p.page_offset leading table entries (and their tokens) are skipped: a
-  // shared prefix attended to elsewhere; 0 otherwise
-  const int po = p.page_offset;
-  const int page0 = s * pps;
-  int tbl = -1;
-  if ((int)threadIdx.x < pps && page0 + (int)threadIdx.x < W - po)
-    tbl = block_table[(size_t)b * W + po + page0 + threadIdx.x];
-  const int seq_len = seq_lens[b] - po * kPage;
-  const int q_len = q_lens[b];
-  const RowPrefix rp = row_prefix(q_lens, b, B);
-  const int q_start = rp.start;
-  // the batch's row count against total_q, once per launch (item 0 always exists)
-  if (blockIdx.x == 0 && threadIdx.x == 0 && rp.total != p.total_q) atomicOr(p.err, PKV_EFLAG_ROWS_BIT);
-  if (q_len < 0) {
-    if (s == 0 && g == 0 && threadIdx.x == 0) atomicOr(p.err, PKV_EFLAG_QLEN_BIT);
-    return;
-  }
-  if (q_len == 0 || rp.bad_before) return;
-  const int n_pages = (seq_len + kPage - 1) / kPage;
-  const int n_splits = (n_pages + pps - 1) / pps;
-  if (q_len > p.max_q_len || q_len > seq_len || n_pages > W - po) {
-    if (s == 0 && g == 0 && threadIdx.x == 0) atomicOr(p.err, PKV_EFLAG_QLEN_BIT);
-    return;
-  }
-  if (s >= n_splits) return;
-  if (q_start + q_len > p.total_q) {
-    if (s == 0 && g == 0 && threadIdx.x == 0) atomicOr(p.err, PKV_EFLAG_ROWS_BIT);
-    return;
-  }
-  const int npg = min(pps, n_pages - page0);
-  if ((int)threadIdx.x < npg) {
-    if (tbl < 0 || tbl >= p.P) {
-      atomicOr(p.err, PKV_EFLAG_PAGE_BIT);
-      tbl = -1;
+  int b, g, s, seq_len, q_len, q_start, n_splits, page0, npg, rows;
+  int rt = 0;  // SHR: row tile
+  if constexpr (SHR) {
+    const int rows_all = p.total_q * p.group;
+    const int row_tiles = (rows_all + RP - 1) / RP;
+    g = blockIdx.x % Hkv;
+    rt = (blockIdx.x / Hkv) % row_tiles;
+    s = blockIdx.x / Hkv / row_tiles;
+    b = 0;
+    const int shared_pages = p.page_offset;
+    seq_len = shared_pages * kPage;
+    // the contract, one (sequence, shared entry) pair per thread of the grid
+    for (long e = (long)blockIdx.x * kThreads + threadIdx.x; e < (long)B * shared_pages;
+         e += (long)gridDim.x * kThreads) {
+      const int bb = (int)(e / shared_pages), jj = (int)(e % shared_pages);
+      if (block_table[(size_t)bb * W + jj] != block_table[jj]) atomicOr(p.err, PKV_EFLAG_PAGE_BIT);
+      if (jj == 0 && q_lens[bb] > 0 && seq_lens[bb] - q_lens[bb] < seq_len) atomicOr(p.err, PKV_EFLAG_QLEN_BIT);
     }
-    s_pages[threadIdx.x] = tbl;
+    q_len = 0;
+    q_start = 0;
+    n_splits = p.max_splits;
+    page0 = s * pps;
+    if (s >= n_splits || page0 >= shared_pages) return;
+    npg = min(pps, shared_pages - page0);
+    if ((int)threadIdx.x < npg) {
+      int tbl = block_table[page0 + threadIdx.x];
+      if (tbl < 0 || tbl >= p.P) {
+        atomicOr(p.err, PKV_EFLAG_PAGE_BIT);
+        tbl = -1;
+      }
+      s_pages[threadIdx.x] = tbl;
+    }
+    rows = min(RP, rows_all - rt * RP);
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
+    __syncthreads();
+  } else {
+    const int pairs = num_items / B;
+    const int xcd = blockIdx.x % kNumXcd, k = blockIdx.x / kNumXcd;
+    b = k % B;
+    const int j = xcd + kNumXcd * (k / B);
+    if (j >= pairs) return;
+    g = j % Hkv;
+    s = j / Hkv;
+
+    // independent loads first, so their latencies overlap: the sequence's
+    // lengths, the split's table entries and the window-row prefix sum
+    // p.page_offset leading table entries (and their tokens) are skipped: a
+    // shared prefix attended to elsewhere; 0 otherwise
+    const int po = p.page_offset;
+    page0 = s * pps;
+    int tbl = -1;
+    if ((int)threadIdx.x < pps && page0 + (int)threadIdx.x < W - po)
+      tbl = block_table[(size_t)b * W + po + page0 + threadIdx.x];
+    seq_len = seq_lens[b] - po * kPage;
+    q_len = q_lens[b];
+    const RowPrefix rp = row_prefix(q_lens, b, B);
+    q_start = rp.start;
+    // the batch's row count against total_q, once per launch (item 0 always exists)
+    if (blockIdx.x == 0 && threadIdx.x == 0 && rp.total != p.total_q) atomicOr(p.err, PKV_EFLAG_ROWS_BIT);
+    if (q_len < 0) {
+      if (s == 0 && g == 0 && threadIdx.x == 0) atomicOr(p.err, PKV_EFLAG_QLEN_BIT);
+      return;
+    }
+    if (q_len == 0 || rp.bad_before) return;
+    const int n_pages = (seq_len + kPage - 1) / kPage;
+    n_splits = (n_pages + pps - 1) / pps;
+    if (q_len > p.max_q_len || q_len > seq_len || n_pages > W - po) {
+      if (s == 0 && g == 0 && threadIdx.x == 0) atomicOr(p.err, PKV_EFLAG_QLEN_BIT);
+      return;
+    }
+    if (s >= n_splits) return;
+    if (q_start + q_len > p.total_q) {
+      if (s == 0 && g == 0 && threadIdx.x == 0) atomicOr(p.err, PKV_EFLAG_ROWS_BIT);
+      return;
+    }
+    npg = min(pps, n_pages - page0);
+    if ((int)threadIdx.x < npg) {
+      if (tbl < 0 || tbl >= p.P) {
+        atomicOr(p.err, PKV_EFLAG_PAGE_BIT);
+        tbl = -1;
+      }
+      s_pages[threadIdx.x] = tbl;
+    }
+    // Every load the compiler issued itself has landed by now (the table
+    // entries were just used). A wait it can see says so: otherwise, before it
+    // reuses the registers those loads targeted, it inserts vmcnt(0), which also
+    // counts the direct q and K/V loads below and would hold the first K/V
+    // chunk back until the q rows landed.
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
+    rows = q_len * p.group;  // <= RP by the plan
+    __syncthreads();
   }
-  // Every load the compiler issued itself has landed by now (the table
-  // entries were just used). A wait it can see says so: otherwise, before it
-  // reuses the registers those loads targeted, it inserts vmcnt(0), which also
-  // counts the direct q and K/V loads below and would hold the first K/V
-  // chunk back until the q rows landed.
-  __builtin_amdgcn_s_waitcnt(kVmcnt0);
-  const int rows = q_len * p.group;  // <= RP by the plan
-  __syncthreads();
 
   const int tok_begin = page0 * kPage;
   const int tok_end = min(seq_len, (page0 + npg) * kPage);
@@ -942,7 +1029,8 @@ __global__ __launch_bounds__(WAVES * 64) void attn_split_kernel(
       u32 off = q_bytes;  // out of range: zero
       if (r < rows) {
         const int c = pos ^ (r & (NC - 1));
-        off = (u32)(((q_start + r / p.group) * p.Hq + g * p.group + r % p.group) * D) * 2u + c * 16;
+        const int R = SHR ? rt * RP + r : r;  // SHR: the stacked batch row
+        off = (u32)(((q_start + R / p.group) * p.Hq + g * p.group + R % p.group) * D) * 2u + c * 16;
       }
       dma16(rq, off, uniform(qbase + i * 1024));
     }
@@ -1000,7 +1088,10 @@ __global__ __launch_bounds__(WAVES * 64) void attn_split_kernel(
   };
 
   Tile tile;
-  tile.init(p.group, rows, seq_len, q_len);
+  if constexpr (SHR)
+    tile.init(1, rows, 1 << 30, 0);  // every shared key visible to every row
+  else
+    tile.init(p.group, rows, seq_len, q_len);
   // fill the whole ring
   const int pro = min(NBUF, my_chunks);
 #pragma unroll
@@ -1043,7 +1134,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_split_kernel(
   float* red_m = reinterpret_cast<float*>(smem);
   float* red_l = red_m + kWaves * RP;
   float* red_acc = red_l + kWaves * RP;
-  tile.spill(red_m + wave * RP, red_l + wave * RP, red_acc + (size_t)wave * RP * D);
+  tile.spill(red_m + wave * RP, red_l + wave * RP, red_acc + (size_t)wave * RP * Tile::MS);
   __syncthreads();
 
   constexpr int D4 = D / 4;
@@ -1065,10 +1156,15 @@ __global__ __launch_bounds__(WAVES * 64) void attn_split_kernel(
         const float mw = red_m[w * RP + r];
         const float wt = (mw == kNegInf) ? 0.f : exp2f_fast(mw - M);
         L += wt * red_l[w * RP + r];
-        A += wt * *reinterpret_cast<const f32x4*>(red_acc + ((size_t)w * RP + r) * D + 4 * dq);
+        A += wt * *reinterpret_cast<const f32x4*>(red_acc + ((size_t)w * RP + r) * Tile::MS + 4 * dq);
       }
     }
-    if (n_splits == 1) {
+    if constexpr (SHR) {
+      // the shared split's partial of stacked row R, read by the next kernel
+      const size_t i = ((size_t)g * n_splits + s) * ((size_t)p.total_q * p.group) + rt * RP + r;
+      *reinterpret_cast<f32x4*>(p.part_acc + i * D + 4 * dq) = A;
+      if (dq == 0) *reinterpret_cast<f32x2*>(p.part_ml + i * 2) = f32x2{M, L};
+    } else if (n_splits == 1) {
       const int h = g * p.group + r % p.group;
       if (p.shared_ml) {
         // the shared prefix's key splits, in order, after this row's own
@@ -1112,7 +1208,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_split_kernel(
       }
     }
   }
-  if (n_splits == 1) return;
+  if (SHR || n_splits == 1) return;
 
   // ---- the last workgroup of (b, g) merges every split in split order.
   // Every thread's partial stores are acknowledged (vmcnt 0) before the
@@ -1807,6 +1903,29 @@ AttnWorkspace attn_workspace(int B, int Hkv, int W, int max_q_len, int group, in
 SharedPlan shared_plan(int Hkv, int total_q, int group, int shared_pages) {
   SharedPlan sp;
   const int rows = total_q * group;
+  // Few rows per KV head (decode and verify batches): the decode / verify
+  // kernel's matrix-core row tile over key splits of whole pages, each of its
+  // waves streaming a private ring, one round of workgroups. There a 256-row
+  // tile would be mostly padding and its split too short to fill its ring.
+  {
+    const int tr = rows <= 32 ? 32 : 64;
+    const long tiles = (long)Hkv * ((rows + tr - 1) / tr);
+    const int smem = tr == 32 ? KernelCfg<128, MfmaTile<128, 1>, PKV_MFMA_NBUF, PKV_MFMA_WAVES>::SMEM
+                              : KernelCfg<128, MfmaTile<128, 2>, PKV_MFMA_NBUF, PKV_MFMA_WAVES>::SMEM;
+    const long slots = (long)kNumCu * (kLdsPerCu / smem < 1 ? 1 : kLdsPerCu / smem);
+    long splits = slots / tiles;
+    if (splits > shared_pages) splits = shared_pages;
+    if (PKV_SHARED_ROW_TILE && splits >= 2) {
+      int pps = (int)((shared_pages + splits - 1) / splits);
+      if (pps > kMaxPps) pps = kMaxPps;  // the kernel stages at most kMaxPps table entries per split
+      sp.tile_rows = tr;
+      sp.row_tiles = (rows + tr - 1) / tr;
+      sp.split_keys = pps * kPage;
+      sp.splits = (shared_pages + pps - 1) / pps;
+      return sp;
+    }
+  }
+  sp.tile_rows = 0;
   sp.row_tiles = (rows + kPrefillRows - 1) / kPrefillRows;
   const int chunks = shared_pages * kPage / 32;
   // about one workgroup per CU (one fits: the ring takes most of the LDS),
@@ -1821,7 +1940,26 @@ SharedPlan shared_plan(int Hkv, int total_q, int group, int shared_pages) {
   return sp;
 }
 
+template <int D, int NRB>
+hipError_t launch_shared_rows(const AttnParams& p, const SharedParams& sp, hipStream_t stream) {
+  AttnParams q = p;
+  q.part_ml = sp.part_ml;
+  q.part_acc = sp.part_acc;
+  q.pps = sp.split_keys / kPage;
+  q.max_splits = sp.splits;
+  q.page_offset = sp.shared_pages;
+  q.num_items = p.Hkv * sp.row_tiles * sp.splits;
+  hipLaunchKernelGGL((attn_split_kernel<D, MfmaTile<D, NRB>, PKV_MFMA_NBUF, PKV_MFMA_WAVES, 0, true>),
+                     dim3(q.num_items), dim3(PKV_MFMA_WAVES * 64), 0, stream, q.block_table, q.seq_lens, q.q_lens,
+                     q.num_items, q.B, q.Hkv, q.pps, q.W, q);
+  return hipGetLastError();
+}
+
 hipError_t launch_attn_shared(const AttnParams& p, const SharedParams& sp, hipStream_t stream) {
+  if (sp.tile_rows == 32)
+    return p.D == 64 ? launch_shared_rows<64, 1>(p, sp, stream) : launch_shared_rows<128, 1>(p, sp, stream);
+  if (sp.tile_rows == 64)
+    return p.D == 64 ? launch_shared_rows<64, 2>(p, sp, stream) : launch_shared_rows<128, 2>(p, sp, stream);
   const unsigned grid = (unsigned)((long)p.Hkv * sp.row_tiles * sp.splits);
   if (p.D == 64)
     hipLaunchKernelGGL((attn_shared_kernel<64, PKV_PREFILL_NBUF, kLongNrb<64>>), dim3(grid),

@@ -45,6 +45,9 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 #ifndef PKV_SHARED_WG
 #define PKV_SHARED_WG kNumCu  // workgroups the shared-prefix kernel aims for
 #endif
+#ifndef PKV_SHARED_ROW_TILE
+#define PKV_SHARED_ROW_TILE 1  // shared-prefix keys of few-row batches on the decode / verify row tile
+#endif
 #ifndef PKV_FORCE_PPS
 #define PKV_FORCE_PPS 0  // pages per split; 0 = planned per shape
 #endif

@@ -332,6 +332,7 @@ int pkv_attn_fwd_shared(const void* q, const void* k_pool, const void* v_pool, c
   sp.splits = L.sp.splits;
   sp.split_keys = L.sp.split_keys;
   sp.row_tiles = L.sp.row_tiles;
+  sp.tile_rows = L.sp.tile_rows;
   if (sp.splits == 1) {
     // tails first; the shared kernel merges its single split into them
     if (pkv::launch_attn(p, L.plan, st) != hipSuccess) return PKV_ERR_HIP;

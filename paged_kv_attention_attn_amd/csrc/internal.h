@@ -61,11 +61,14 @@ struct AttnPlan {
 struct SharedParams {
   float* part_ml;       // [Hkv][splits][total_q * group][2] = (reference max (log2 units), row sum)
   float* part_acc;      // [Hkv][splits][total_q * group][D] unnormalised
-  int32_t shared_pages, splits, split_keys, row_tiles;
+  int32_t shared_pages, splits, split_keys, row_tiles, tile_rows;
 };
 
 struct SharedPlan {
   int splits, split_keys, row_tiles;
+  // 0: the long-window kernel's 256-row tiles; 32 or 64: the decode / verify
+  // kernel's matrix-core row tile (few rows per KV head), row_tiles of that size
+  int tile_rows;
 };
 
 AttnPlan attn_plan(int B, int Hkv, int W, int max_q_len, int group, long total_pages, int pages_per_split);

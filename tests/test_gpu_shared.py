@@ -91,6 +91,9 @@ SHAPES = [
     (2, [300, 40, 600], [300, 20, 150], 8, 2, 128),              # tail prefills (q_len <= tail)
     (1, [256, 5, 700, 33], [256, 5, 700, 33], 8, 2, 64),         # every tail token a window row
     (3, [100, 1, 500], [100, 1, 3], 32, 8, 128),                 # long, decode and verify windows mixed
+    # 2200 stacked rows per KV head: too many for the decode / verify row
+    # tile, so the 256-row shared tiles over 3 key splits, then the merge kernel
+    (2, [200, 150, 100, 100], [200, 150, 100, 100], 32, 8, 128),
     # 8192 stacked rows per KV head: 256 row tiles, so a single key split,
     # merged into the tails' rows inside the shared kernel
     (2, [256] * 8, [256] * 8, 32, 8, 128),
