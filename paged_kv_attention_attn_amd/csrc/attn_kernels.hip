@@ -469,17 +469,40 @@ struct MfmaTile {
     u32x4 pb[NRB][2];
     float p[NRB][16];
     float x[NRB][16], cm[NRB];
+    // a row sees the chunk's tokens 0 .. thr[rb]; the mask is skipped when
+    // every row of the wave sees the whole chunk (padding rows, lim < 0,
+    // hold scores of a zero q row and are never read)
+    int thr[NRB];
+    bool partial = false;
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      thr[rb] = min(lim[rb] - tok0, nv - 1);
+      partial |= lim[rb] >= 0 && thr[rb] < TC - 1;
+    }
+    const bool masked = __builtin_amdgcn_ballot_w64(partial) != 0;
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int tt = 8 * (i >> 2) + 4 * half + (i & 3);
+        const float ksl = QB != 0 ? qsc[tt] * (scale_log2 * kStageFactor<QB>) : scale_log2;
+        x[rb][i] = S[rb][i] * ksl;
+      }
+    if (masked) {
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int tt = 8 * (i >> 2) + 4 * half + (i & 3);
+          if (tt > thr[rb]) x[rb][i] = kNegInf;
+        }
+    }
     bool grow = false;
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
       cm[rb] = kNegInf;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int tt = 8 * (i >> 2) + 4 * half + (i & 3);
-        const float ksl = QB != 0 ? qsc[tt] * (scale_log2 * kStageFactor<QB>) : scale_log2;
-        x[rb][i] = (tok0 + tt <= lim[rb] && tt < nv) ? S[rb][i] * ksl : kNegInf;
-        cm[rb] = fmaxf(cm[rb], x[rb][i]);
-      }
+      for (int i = 0; i < 16; ++i) cm[rb] = fmaxf(cm[rb], x[rb][i]);
       cm[rb] = max_xor32(cm[rb]);
       grow |= cm[rb] > m[rb] + kLazyLog2;
     }
