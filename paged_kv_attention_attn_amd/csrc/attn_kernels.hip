@@ -1794,16 +1794,20 @@ hipError_t launch_d(const AttnParams& p, const AttnPlan& plan, hipStream_t strea
   // better at three slots than at two)
   constexpr int kValuNbuf = QB == 8 ? PKV_VALU_Q8_NBUF : QB == 4 ? PKV_VALU_Q4_NBUF : PKV_VALU_NBUF;
   if (!plan.mfma) {
-    // bf16 decode with more items than one round of two-slot rings holds
-    // (the dedup batch, the tails of the shared-prefix call): one-slot rings.
-    // The tile's registers keep two workgroups per CU at head_dim 128 either
-    // way (three at 64), so such batches still take more than one round; with
-    // half the chunks in flight per wave they measured faster on both (the
-    // dedup batch reads its shared pages through one L2 per XCD)
-    using Two = KernelCfg<D, ValuTile<D, 1>, kValuNbuf, PKV_VALU_WAVES, QB>;
-    if constexpr (QB == 0 && kValuNbuf == 2) {
-      if ((long)p.num_items > (long)kNumCu * (kLdsPerCu / Two::SMEM))
+    // bf16 decode with more items than one round of four-wave workgroups
+    // holds. Items of at most two pages (the tails of the shared-prefix
+    // call): two-wave workgroups. The tile's registers allow two waves per
+    // SIMD at head_dim 128, so a CU holds two four-wave workgroups but four
+    // two-wave ones, and 800 one-page tails run in one round instead of two
+    // (shared call 44.9 -> 42.4 us). Longer items (the dedup batch, 17 pages
+    // each) keep four waves on one-slot rings: their chunks in flight per
+    // item set their pace (two-wave workgroups: 165.6 -> 175.8 us).
+    using Four = KernelCfg<D, ValuTile<D, 1>, kValuNbuf, PKV_VALU_WAVES, QB>;
+    if constexpr (QB == 0 && kValuNbuf == 2 && PKV_VALU_WAVES == 4) {
+      if ((long)p.num_items > (long)kNumCu * (kLdsPerCu / Four::SMEM)) {
+        if (min(p.pps, p.W - p.page_offset) <= 2) return launch_one<D, ValuTile<D, 1>, 2, 2, QB>(p, stream);
         return launch_one<D, ValuTile<D, 1>, 1, PKV_VALU_WAVES, QB>(p, stream);
+      }
     }
     return launch_one<D, ValuTile<D, 1>, kValuNbuf, PKV_VALU_WAVES, QB>(p, stream);
   }
