@@ -456,15 +456,16 @@ struct MfmaTile {
     for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) S[rb][i] = 0.f;
-    // S^T[token][q row] = sum_d K[token][d] * Q[q row][d]
+    // S^T[token][q row] = sum_d K[token][d] * Q[q row][d], row block by row
+    // block, so the first block's softmax can run beside the next block's
+    // products
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
+    for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
-      for (int rb = 0; rb < NRB; ++rb)
+      for (int kk = 0; kk < KK; ++kk)
         S[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ka[kk]),
                                                         __builtin_bit_cast(bf16x8, qb[rb][kk]), S[rb], 0, 0,
                                                         0);
-    }
     // this lane holds tokens 8*(i/4) + 4*half + i%4 of q row `row`
     u32x4 pb[NRB][2];
     float p[NRB][16];
@@ -552,7 +553,8 @@ struct MfmaTile {
       l[rb] += ps;
       // a key of this chunk weighing more than kSplitWeight of its row's sum
       // so far (both halves of the row): its bf16 P would not average out
-      heavy |= cm[rb] != kNegInf && exp2f_fast(cm[rb] - mu) > kSplitWeight * sum_xor32(l[rb]);
+      // (evaluated without a branch: exp2 of -inf is 0)
+      heavy |= (cm[rb] != kNegInf) & (exp2f_fast(cm[rb] - mu) > kSplitWeight * sum_xor32(l[rb]));
       if constexpr (QB != 0) {  // P.V weights carry the V scales
 #pragma unroll
         for (int i = 0; i < 16; ++i) p[rb][i] *= qsc[64 + 8 * (i >> 2) + 4 * half + (i & 3)] * kStageFactor<QB>;
@@ -567,11 +569,11 @@ struct MfmaTile {
     }
     // O^T[d][q row] += sum_token V[token][d] * P[q row][token]
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+    for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
+      for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int rb = 0; rb < NRB; ++rb)
+        for (int ks = 0; ks < 2; ++ks)
           acc[rb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va[mb][ks]),
                                                                 __builtin_bit_cast(bf16x8, pb[rb][ks]),
                                                                 acc[rb][mb], 0, 0, 0);
