@@ -177,7 +177,8 @@ struct ValuTile {
   // (QB != 0): the staged operands are codes, and qsc holds the chunk's K
   // scales (words 0..) and V scales (words 64..): token t's score is scaled
   // by its K scale, its weight P by its V scale (the row sum keeps plain P).
-  template <int QB = 0>
+  // (MAYMASK is accepted for the kernel's sake; this tile always masks)
+  template <int QB = 0, bool MAYMASK = true>
   __device__ __forceinline__ void compute(float* pb, int tok0, int nv, float scale_log2, const float* qsc) {
     const int lane = threadIdx.x & 63;
     const int rg = lane >> 4, t = lane & 15;
@@ -447,7 +448,9 @@ struct MfmaTile {
   // Quantized caches (QB != 0): as the VALU tile's compute, with the K scale
   // on each score and the V scale on each weight of P.V (rows' sums keep
   // plain P).
-  template <int QB = 0>
+  // MAYMASK false: every chunk is whole and seen in full by every row (the
+  // shared-prefix rows), so no mask code at all
+  template <int QB = 0, bool MAYMASK = true>
   __device__ __forceinline__ void compute(float*, int tok0, int nv, float scale_log2, const float* qsc) {
     const int lane = threadIdx.x & 63;
     const int half = lane >> 5;
@@ -480,7 +483,7 @@ struct MfmaTile {
       thr[rb] = min(lim[rb] - tok0, nv - 1);
       partial |= lim[rb] >= 0 && thr[rb] < TC - 1;
     }
-    const bool masked = __builtin_amdgcn_ballot_w64(partial) != 0;
+    const bool masked = MAYMASK && __builtin_amdgcn_ballot_w64(partial) != 0;
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
@@ -1151,7 +1154,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_split_kernel(
     // the slot is free once its operands sit in registers: refill it now so
     // NBUF chunks stay in flight while this one is computed
     if (k + NBUF < my_chunks) issue(k + NBUF);
-    tile.template compute<QB>(pbuf, t0, nv, p.scale_log2, qsc);
+    tile.template compute<QB, !SHR>(pbuf, t0, nv, p.scale_log2, qsc);
   }
 
   // ---- merge the waves in LDS
