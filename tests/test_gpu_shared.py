@@ -194,12 +194,19 @@ def test_planned_shape_on_the_shared_call(pk):
 
 
 @pytest.mark.parametrize("scale", [-0.2, 0.0, 0.6])
-def test_shared_prefix_any_finite_scale(pk, scale):
-    """The prefix kernel runs a negative scale on -q and a zero scale on q = 0;
-    the tails and the merge take the scale as given."""
-    case = shared_case(440, 2, [30, 300, 600], [1, 3, 2])
+@pytest.mark.parametrize("rows", ["few", "many"])
+def test_shared_prefix_any_finite_scale(pk, scale, rows):
+    """Any finite scale on both shared-prefix engines: the decode / verify
+    row tile (few stacked rows, 24 here) takes the scale as given; the
+    256-row tiles (many rows, 2200 per KV head here) run a negative scale on
+    -q and a zero scale on q = 0; the tails and the merge take it as given."""
+    if rows == "few":
+        case, sp = shared_case(440, 2, [30, 300, 600], [1, 3, 2]), 2
+    else:
+        case, sp = shared_case(441, 2, [200, 150, 100, 100], [200, 150, 100, 100], 32, 8, 128), 2
+    say(f"shared prefix, scale {scale}, {rows} rows")
     case = AttnCase("shared-scale", case.q, case.k_pool, case.v_pool, case.block_table, case.seq_lens,
                     case.q_lens, float(np.float32(scale)))
-    got, again, flags = run_shared(pk, case, 2)
+    got, again, flags = run_shared(pk, case, sp)
     assert flags == 0
-    assert_close(got, oracle_attn(case), f"shared scale {scale}")
+    assert_close(got, oracle_attn(case), f"shared scale {scale} ({rows} rows)")
